@@ -1,0 +1,231 @@
+"""Oracle for the MC2 per-rank operators -- TEST INFRASTRUCTURE ONLY.
+
+A ctypes wrapper over ``mc2_oracle.c``, the plain CPU implementation of what
+the operators compute.  Only the tests, ``__graft_entry__.smoke()`` and the
+benchmark's CPU-baseline leg may import this package; the product path
+(``comm_matmul_tensor_amd``) never does, and it shares no code with it.
+
+All arrays are numpy arrays in the storage conventions of ``mc2_inputs``
+(bf16 as uint16 bit patterns, fp8 and E8M0 as uint8 codes).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from typing import Dict, Optional, Sequence
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "mc2_oracle.c")
+_LIB = os.path.join(_HERE, "libmc2_oracle.so")
+
+DT = {"f32": 0, "f16": 1, "bf16": 2, "i8": 3, "i32": 4, "e4m3fn": 5, "e5m2": 6, "e8m0": 7}
+_STORAGE = {"f32": np.float32, "f16": np.float16, "bf16": np.uint16, "i8": np.int8,
+            "i32": np.int32, "e4m3fn": np.uint8, "e5m2": np.uint8, "e8m0": np.uint8}
+
+P = ctypes.c_void_p
+I64 = ctypes.c_int64
+INT = ctypes.c_int
+
+
+def build(force: bool = True) -> str:
+    """Compile the oracle with gcc: -O2, OpenMP, no contraction, no fast-math."""
+    if force or not os.path.exists(_LIB):
+        tmp = _LIB + ".tmp"
+        subprocess.check_call(["gcc", "-O2", "-std=c11", "-fopenmp", "-ffp-contract=off",
+                               "-fno-fast-math", "-fPIC", "-shared", _SRC, "-o", tmp, "-lm"])
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+_lib = None
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB):
+            build(force=True)
+        lib = ctypes.CDLL(_LIB)
+        sig = {
+            "orc_allgather": (None, [P, INT, I64, I64, P]),
+            "orc_matmul": (None, [P, INT, P, INT, I64, I64, I64, INT, P]),
+            "orc_allgather_matmul": (None, [P, INT, I64, I64, P, I64, INT, INT, P, P]),
+            "orc_permute": (None, [P, INT, I64, I64, P]),
+            "orc_smooth_quant": (None, [P, I64, I64, P, INT, P, P]),
+            "orc_int8_matmul": (I64, [P, P, I64, I64, I64, P]),
+            "orc_dequant": (None, [P, P, P, P, I64, I64, INT, P]),
+            "orc_alltoall_quant_matmul": (I64, [P, INT, I64, I64, INT, P, I64, P, P, P, P, P, P, P, P]),
+            "orc_quant_all_reduce": (INT, [P, P, INT, I64, I64, INT, INT, P, INT]),
+            "orc_decode_array": (INT, [INT, I64, P, P]),
+            "orc_encode_array": (INT, [INT, I64, P, P]),
+        }
+        for name, (res, args) in sig.items():
+            f = getattr(lib, name)
+            f.restype = res
+            f.argtypes = args
+        _lib = lib
+    return _lib
+
+
+def _ptr(a: Optional[np.ndarray]):
+    if a is None:
+        return None
+    assert a.flags["C_CONTIGUOUS"], "oracle inputs must be C-contiguous"
+    return a.ctypes.data
+
+
+def _ptr_array(arrs: Sequence[np.ndarray]):
+    arr = (ctypes.c_void_p * len(arrs))(*[_ptr(a) for a in arrs])
+    return arr
+
+
+# ---------------------------------------------------------------- formats
+def decode(dtype: str, codes: np.ndarray) -> np.ndarray:
+    codes = np.ascontiguousarray(codes)
+    st = np.dtype(_STORAGE[dtype])
+    codes = codes.view(st) if codes.dtype.itemsize == st.itemsize else codes.astype(st)
+    out = np.empty(codes.shape, dtype=np.float64)
+    if _load().orc_decode_array(DT[dtype], codes.size, _ptr(codes), _ptr(out)) != 0:
+        raise ValueError(dtype)
+    return out
+
+
+def encode(dtype: str, values: np.ndarray) -> np.ndarray:
+    values = np.ascontiguousarray(values, dtype=np.float64)
+    out = np.empty(values.shape, dtype=_STORAGE[dtype])
+    if _load().orc_encode_array(DT[dtype], values.size, _ptr(values), _ptr(out)) != 0:
+        raise ValueError(dtype)
+    return out
+
+
+# ---------------------------------------------------------------- AllGatherMatmul
+def allgather(shards: Sequence[np.ndarray]) -> np.ndarray:
+    shards = [np.ascontiguousarray(s) for s in shards]
+    m_local, k = shards[0].shape
+    out = np.empty((len(shards) * m_local, k), dtype=shards[0].dtype)
+    _load().orc_allgather(_ptr_array(shards), len(shards), m_local, k * shards[0].itemsize, _ptr(out))
+    return out
+
+
+def matmul(a: np.ndarray, b: np.ndarray, dtype: str, a_trans: bool = False,
+           b_trans: bool = False) -> np.ndarray:
+    """round(A @ B); a_trans: a holds A^T as (k, m); b_trans: b holds B^T as (n, k)."""
+    a = np.ascontiguousarray(a)
+    b = np.ascontiguousarray(b)
+    if a_trans:
+        k, m = a.shape
+    else:
+        m, k = a.shape
+    n = b.shape[0] if b_trans else b.shape[1]
+    assert (b.shape[1] if b_trans else b.shape[0]) == k
+    out = np.empty((m, n), dtype=_STORAGE[dtype])
+    _load().orc_matmul(_ptr(a), int(a_trans), _ptr(b), int(b_trans), m, n, k, DT[dtype], _ptr(out))
+    return out
+
+
+def allgather_matmul(shards: Sequence[np.ndarray], x2: np.ndarray, dtype: str,
+                     x2_trans: bool = False, gather_output: bool = True):
+    shards = [np.ascontiguousarray(s) for s in shards]
+    x2 = np.ascontiguousarray(x2)
+    r = len(shards)
+    m_local, k = shards[0].shape
+    n = x2.shape[0] if x2_trans else x2.shape[1]
+    out = np.empty((r * m_local, n), dtype=_STORAGE[dtype])
+    g = np.empty((r * m_local, k), dtype=_STORAGE[dtype]) if gather_output else None
+    _load().orc_allgather_matmul(_ptr_array(shards), r, m_local, k, _ptr(x2), n, int(x2_trans),
+                                 DT[dtype], _ptr(out), _ptr(g))
+    return out, g
+
+
+def matmul_grad_input(dy: np.ndarray, w: np.ndarray, dtype: str = "bf16") -> np.ndarray:
+    """dX_partial = dY @ W with W in nn.Linear (out, in) layout, i.e. (n_local, k)."""
+    return matmul(dy, w, dtype)
+
+
+def matmul_grad_weight(dy: np.ndarray, ag_x: np.ndarray, dtype: str = "bf16") -> np.ndarray:
+    """dW = dY^T @ AG(X)."""
+    return matmul(dy, ag_x, dtype, a_trans=True)
+
+
+# ---------------------------------------------------------------- AlltoAllQuantMatmul
+def permute(x1: np.ndarray, r: int) -> np.ndarray:
+    x1 = np.ascontiguousarray(x1)
+    bs, h = x1.shape
+    out = np.empty((bs // r, r * h), dtype=x1.dtype)
+    _load().orc_permute(_ptr(x1), r, bs, h, _ptr(out))
+    return out
+
+
+def smooth_quant(p: np.ndarray, smooth: Optional[np.ndarray], dtype: str = "bf16"):
+    p = np.ascontiguousarray(p)
+    rows, cols = p.shape
+    q = np.empty((rows, cols), dtype=np.int8)
+    s1 = np.empty(rows, dtype=np.float32)
+    sm = None if smooth is None else np.ascontiguousarray(smooth)
+    _load().orc_smooth_quant(_ptr(p), rows, cols, _ptr(sm), DT[dtype], _ptr(q), _ptr(s1))
+    return q, s1
+
+
+def int8_matmul(q: np.ndarray, x2: np.ndarray) -> np.ndarray:
+    q = np.ascontiguousarray(q, dtype=np.int8)
+    x2 = np.ascontiguousarray(x2, dtype=np.int8)
+    m, k = q.shape
+    n = x2.shape[1]
+    acc = np.empty((m, n), dtype=np.int32)
+    ovf = _load().orc_int8_matmul(_ptr(q), _ptr(x2), m, n, k, _ptr(acc))
+    if ovf:
+        raise OverflowError(f"{ovf} int32 overflows")
+    return acc
+
+
+def dequant(acc, s1, s2, bias, out_dtype: str = "bf16") -> np.ndarray:
+    acc = np.ascontiguousarray(acc, dtype=np.int32)
+    s1 = np.ascontiguousarray(s1, dtype=np.float32)
+    s2 = np.ascontiguousarray(s2, dtype=np.float32)
+    b = None if bias is None else np.ascontiguousarray(bias)
+    m, n = acc.shape
+    out = np.empty((m, n), dtype=_STORAGE[out_dtype])
+    _load().orc_dequant(_ptr(acc), _ptr(s1), _ptr(s2), _ptr(b), m, n, DT[out_dtype], _ptr(out))
+    return out
+
+
+def alltoall_quant_matmul(x1, r: int, x2, x2_scale, smooth=None, bias=None,
+                          dtype: str = "bf16") -> Dict[str, np.ndarray]:
+    x1 = np.ascontiguousarray(x1)
+    x2 = np.ascontiguousarray(x2, dtype=np.int8)
+    x2_scale = np.ascontiguousarray(x2_scale, dtype=np.float32)
+    bs, h = x1.shape
+    n = x2.shape[1]
+    rows, cols = bs // r, r * h
+    out = np.empty((rows, n), dtype=_STORAGE[dtype])
+    perm = np.empty((rows, cols), dtype=x1.dtype)
+    q = np.empty((rows, cols), dtype=np.int8)
+    s1 = np.empty(rows, dtype=np.float32)
+    acc = np.empty((rows, n), dtype=np.int32)
+    sm = None if smooth is None else np.ascontiguousarray(smooth)
+    b = None if bias is None else np.ascontiguousarray(bias)
+    ovf = _load().orc_alltoall_quant_matmul(_ptr(x1), r, bs, h, DT[dtype], _ptr(x2), n,
+                                            _ptr(x2_scale), _ptr(sm), _ptr(b), _ptr(out), _ptr(perm),
+                                            _ptr(q), _ptr(s1), _ptr(acc))
+    if ovf:
+        raise OverflowError(f"{ovf} int32 overflows")
+    return {"out": out, "permuted": perm, "q": q, "s1": s1, "acc": acc}
+
+
+# ---------------------------------------------------------------- QuantAllReduce
+def quant_all_reduce(xs: Sequence[np.ndarray], scales: Sequence[np.ndarray], x_dtype: str,
+                     scale_dtype: str, out_dtype: str) -> np.ndarray:
+    xs = [np.ascontiguousarray(x) for x in xs]
+    scales = [np.ascontiguousarray(s) for s in scales]
+    shape = xs[0].shape
+    h = shape[-1]
+    rows = int(np.prod(shape[:-1]))
+    out = np.empty(shape, dtype=_STORAGE[out_dtype])
+    rc = _load().orc_quant_all_reduce(_ptr_array(xs), _ptr_array(scales), len(xs), rows, h,
+                                      DT[x_dtype], DT[scale_dtype], _ptr(out), DT[out_dtype])
+    if rc != 0:
+        raise ValueError("unsupported dtype combination")
+    return out

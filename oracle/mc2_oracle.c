@@ -1,0 +1,401 @@
+/*
+ * mc2_oracle.c -- TEST INFRASTRUCTURE ONLY.
+ *
+ * A plain, slow, obviously correct CPU implementation of what the MC2
+ * per-rank operators compute.  Only the tests, the package smoke check and the
+ * benchmark's CPU-baseline leg may load it; the product path never does.  It
+ * shares no code with the GPU library: its number formats, loops and
+ * rounding are written here from the definitions.
+ *
+ * Sources (the operator documentation pages):
+ *  [AG]  torch_npu.npu_all_gather_base_mm (Ascend PyTorch API page):
+ *        "function" and "outputs" sections -- out = AllGather(input) @ x2 and
+ *        the gathered input as the second output; "constraints" -- 2-D (m, k),
+ *        (k, n), k in [256, 65535), x2 may be a transposed view.
+ *  [A2A] aclnnAlltoAllQuantMatmul (CANN API page): "function" section, the
+ *        dynamic-quant formula chain AlltoAll -> permute(1, 0, 2) -> Quant(
+ *        permutedOut * x1Scale) -> int8 matmul -> x x1_scale x x2_scale -> + bias.
+ *  [MC2] hyper_parallel tensor_parallel/mc2.py (coverage listing): module
+ *        docstring and AllGatherMatmulFunction.backward -- dX = dY @ W
+ *        (reduce-scattered across ranks), dW = dY^T @ AllGather(X).
+ *  [QAR] QuantAllReduce README (ops-transformer mc2/quant_all_reduce):
+ *        "function" formula output = Reduce(AllGather(scales) * AllGather(x))
+ *        with sum, parameter table (scale shapes (bs, H/128) fp32 or
+ *        (bs, H/64, 2) E8M0) and constraints (group size 128; mx).
+ *
+ * Precision: the float GEMMs and the dequantisation are evaluated in fp64 and
+ * rounded once to the output type (the definition, up to summation order).
+ * The per-token quantisation takes its integer decisions in fp32, the
+ * precision of the GPU kernel, because the pages fix none.  The int8 GEMM is
+ * exact (int64, checked to fit int32).  QuantAllReduce sums fp64 products in
+ * rank order; each product of an 8-bit code and its scale is exact in fp64.
+ *
+ * Build: gcc -O2 -fopenmp -ffp-contract=off (no fast-math).  OpenMP splits
+ * only independent output rows, so results do not depend on thread count.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+/* dtype codes of this file (independent of any other header) */
+enum { O_F32 = 0, O_F16 = 1, O_BF16 = 2, O_I8 = 3, O_I32 = 4, O_E4M3FN = 5, O_E5M2 = 6, O_E8M0 = 7 };
+
+/* ------------------------------------------------------------------------ */
+/* Number formats, from their published definitions.                         */
+/* ------------------------------------------------------------------------ */
+
+/* bf16: the upper 16 bits of an IEEE binary32. */
+double orc_bf16_to_f64(uint16_t b) {
+  uint32_t u = (uint32_t)b << 16;
+  float f;
+  memcpy(&f, &u, 4);
+  return (double)f;
+}
+
+/* IEEE binary16: 1 sign, 5 exponent (bias 15), 10 fraction bits. */
+double orc_f16_to_f64(uint16_t h) {
+  int s = h >> 15, e = (h >> 10) & 31, m = h & 1023;
+  double v;
+  if (e == 31)
+    v = m ? NAN : INFINITY;
+  else if (e == 0)
+    v = ldexp((double)m, -24);
+  else
+    v = ldexp(1.0 + m / 1024.0, e - 15);
+  return s ? -v : v;
+}
+
+/* OCP FLOAT8_E4M3FN: 1-4-3, bias 7, no infinities, S.1111.111 is NaN. */
+double orc_e4m3fn_to_f64(uint8_t c) {
+  int s = c >> 7, e = (c >> 3) & 15, m = c & 7;
+  double v;
+  if (e == 15 && m == 7)
+    v = NAN;
+  else if (e == 0)
+    v = ldexp((double)m, -9);
+  else
+    v = ldexp(1.0 + m / 8.0, e - 7);
+  return s ? -v : v;
+}
+
+/* OCP FLOAT8_E5M2: 1-5-2, bias 15, IEEE-style infinities and NaNs. */
+double orc_e5m2_to_f64(uint8_t c) {
+  int s = c >> 7, e = (c >> 2) & 31, m = c & 3;
+  double v;
+  if (e == 31)
+    v = m ? NAN : INFINITY;
+  else if (e == 0)
+    v = ldexp((double)m, -16);
+  else
+    v = ldexp(1.0 + m / 4.0, e - 15);
+  return s ? -v : v;
+}
+
+/* OCP FLOAT8_E8M0 (MX shared scale): 2^(b - 127); 0xFF is NaN. */
+double orc_e8m0_to_f64(uint8_t b) { return b == 0xFF ? NAN : ldexp(1.0, (int)b - 127); }
+
+/*
+ * Round x to the binary format with p significand bits (implicit bit
+ * included), minimum normal exponent emin and maximum exponent emax, ties to
+ * even, overflow to infinity.  Returns the rounded value as a double.
+ */
+static double round_to_format(double x, int p, int emin, int emax) {
+  if (isnan(x) || isinf(x) || x == 0.0) return x;
+  double a = fabs(x);
+  int e;
+  frexp(a, &e); /* a in [2^(e-1), 2^e) */
+  int E = e - 1;
+  if (E < emin) E = emin;                  /* subnormal spacing */
+  double q = ldexp(1.0, E - (p - 1));      /* spacing of the format at a */
+  double n = nearbyint(a / q);             /* exact scaling; ties to even */
+  double v = n * q;
+  double maxf = ldexp(2.0 - ldexp(1.0, 1 - p), emax);
+  if (v > maxf) v = INFINITY;
+  return x < 0 ? -v : v;
+}
+
+/* fp64 -> bf16, round to nearest even (bf16 = 8 significand bits, binary32 range). */
+uint16_t orc_f64_to_bf16(double x) {
+  if (isnan(x)) return (uint16_t)(signbit(x) ? 0xFFC0 : 0x7FC0);
+  float f = (float)round_to_format(x, 8, -126, 127); /* exact in binary32 */
+  uint32_t u;
+  memcpy(&u, &f, 4);
+  return (uint16_t)(u >> 16);
+}
+
+/* fp64 -> IEEE binary16, round to nearest even, overflow to infinity. */
+uint16_t orc_f64_to_f16(double x) {
+  uint16_t sign = signbit(x) ? 0x8000 : 0;
+  if (isnan(x)) return sign | 0x7E00;
+  double v = fabs(round_to_format(x, 11, -14, 15));
+  if (isinf(v)) return sign | 0x7C00;
+  if (v == 0.0) return sign;
+  if (v < ldexp(1.0, -14)) return sign | (uint16_t)(v * ldexp(1.0, 24)); /* subnormal */
+  int e;
+  double m = frexp(v, &e); /* v = m 2^e, m in [0.5, 1) */
+  int E = e - 1;
+  uint16_t frac = (uint16_t)((m * 2.0 - 1.0) * 1024.0);
+  return sign | (uint16_t)((E + 15) << 10) | frac;
+}
+
+/* fp64 -> binary32, round to nearest even (the C conversion). */
+float orc_f64_to_f32(double x) { return (float)x; }
+
+static double dec16(int dtype, uint16_t v) {
+  return dtype == O_BF16 ? orc_bf16_to_f64(v) : orc_f16_to_f64(v);
+}
+static uint16_t enc16(int dtype, double v) {
+  return dtype == O_BF16 ? orc_f64_to_bf16(v) : orc_f64_to_f16(v);
+}
+
+/* ------------------------------------------------------------------------ */
+/* [AG] AllGather on dim 0, rank order: gather_out rows [i m_l, (i+1) m_l)    */
+/* hold shard i.                                                             */
+/* ------------------------------------------------------------------------ */
+void orc_allgather(const void* const* shards, int r, int64_t m_local, int64_t row_bytes,
+                   void* gather_out) {
+  for (int i = 0; i < r; i++)
+    memcpy((char*)gather_out + (size_t)i * m_local * row_bytes, shards[i],
+           (size_t)m_local * row_bytes);
+}
+
+/*
+ * out (m, n) = round(A @ B) for 16-bit float A and B.
+ *   a_trans = 0: A stored (m, k) row-major;  1: A stored (k, m) row-major.
+ *   b_trans = 0: B stored (k, n) row-major;  1: B stored (n, k) row-major.
+ * The products of two 16-bit floats are exact in fp64; the sum runs over p
+ * ascending in fp64 and is rounded once to the output dtype.
+ */
+void orc_matmul(const uint16_t* a, int a_trans, const uint16_t* b, int b_trans, int64_t m,
+                int64_t n, int64_t k, int dtype, uint16_t* out) {
+  double* bd = (double*)malloc(sizeof(double) * (size_t)(k * n > 0 ? k * n : 1));
+  for (int64_t p = 0; p < k; p++)
+    for (int64_t j = 0; j < n; j++) bd[p * n + j] = dec16(dtype, b_trans ? b[j * k + p] : b[p * n + j]);
+#pragma omp parallel for schedule(dynamic, 4)
+  for (int64_t i = 0; i < m; i++) {
+    double* acc = (double*)calloc((size_t)(n > 0 ? n : 1), sizeof(double));
+    for (int64_t p = 0; p < k; p++) {
+      double av = dec16(dtype, a_trans ? a[p * m + i] : a[i * k + p]);
+      const double* brow = bd + p * n;
+      for (int64_t j = 0; j < n; j++) acc[j] += av * brow[j];
+    }
+    for (int64_t j = 0; j < n; j++) out[i * n + j] = enc16(dtype, acc[j]);
+    free(acc);
+  }
+  free(bd);
+}
+
+/*
+ * [AG] out = AllGather_m(shards) @ x2 and gather_out = AllGather_m(shards).
+ * Written as the two steps of the definition: gather, then multiply.
+ * gather_out may be NULL (the op's gather_output = false).
+ */
+void orc_allgather_matmul(const uint16_t* const* shards, int r, int64_t m_local, int64_t k,
+                          const uint16_t* x2, int64_t n, int x2_trans, int dtype, uint16_t* out,
+                          uint16_t* gather_out) {
+  uint16_t* g = (uint16_t*)malloc(sizeof(uint16_t) * (size_t)(r * m_local * k > 0 ? r * m_local * k : 1));
+  orc_allgather((const void* const*)shards, r, m_local, k * (int64_t)sizeof(uint16_t), g);
+  orc_matmul(g, 0, x2, x2_trans, r * m_local, n, k, dtype, out);
+  if (gather_out) memcpy(gather_out, g, sizeof(uint16_t) * (size_t)(r * m_local * k));
+  free(g);
+}
+
+/* ------------------------------------------------------------------------ */
+/* [A2A] AlltoAllQuantMatmul, dynamic per-token A16W8.                       */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * permutedOut = x1.view(r, bs/r, h).permute(1, 0, 2).view(bs/r, r h):
+ *   P[t][j h + c] = x1[j (bs/r) + t][c].
+ */
+void orc_permute(const uint16_t* x1, int r, int64_t bs, int64_t h, uint16_t* p) {
+  int64_t t_count = bs / r;
+  for (int64_t t = 0; t < t_count; t++)
+    for (int j = 0; j < r; j++)
+      for (int64_t c = 0; c < h; c++) p[t * (r * h) + j * h + c] = x1[(j * t_count + t) * h + c];
+}
+
+/*
+ * Quant(permutedOut * x1Scale), per token (row), symmetric int8:
+ *   y      = P * smooth              (fp32; exact: two 8-bit significands)
+ *   amax_t = max_c |y[t][c]|
+ *   s1_t   = amax_t / 127            (fp32 division, round to nearest)
+ *   q      = clamp(rint(y / s1_t), -127, 127)   (fp32 division, ties to even)
+ * An all-zero row gives s1 = 0 and q = 0.  smooth may be NULL (no smoothing).
+ */
+void orc_smooth_quant(const uint16_t* p, int64_t rows, int64_t cols, const uint16_t* smooth,
+                      int dtype, int8_t* q, float* s1) {
+#pragma omp parallel for schedule(static)
+  for (int64_t t = 0; t < rows; t++) {
+    float* y = (float*)malloc(sizeof(float) * (size_t)(cols > 0 ? cols : 1));
+    float amax = 0.0f;
+    for (int64_t c = 0; c < cols; c++) {
+      float pv = (float)dec16(dtype, p[t * cols + c]);
+      float sv = smooth ? (float)dec16(dtype, smooth[c]) : 1.0f;
+      y[c] = pv * sv;
+      float av = fabsf(y[c]);
+      if (av > amax) amax = av;
+    }
+    float s = amax / 127.0f;
+    s1[t] = s;
+    for (int64_t c = 0; c < cols; c++) {
+      int v = 0;
+      if (amax > 0.0f) {
+        float rq = rintf(y[c] / s);
+        if (rq > 127.0f) rq = 127.0f;
+        if (rq < -127.0f) rq = -127.0f;
+        v = (int)rq;
+      }
+      q[t * cols + c] = (int8_t)v;
+    }
+    free(y);
+  }
+}
+
+/*
+ * acc (m, n) = q (m, k) @ x2 (k, n), both int8 row-major, exact.
+ * Returns the number of entries whose exact value does not fit int32.
+ */
+int64_t orc_int8_matmul(const int8_t* q, const int8_t* x2, int64_t m, int64_t n, int64_t k,
+                        int32_t* acc) {
+  int64_t overflow = 0;
+#pragma omp parallel for schedule(dynamic, 1) reduction(+ : overflow)
+  for (int64_t i = 0; i < m; i++) {
+    int64_t* row = (int64_t*)calloc((size_t)(n > 0 ? n : 1), sizeof(int64_t));
+    for (int64_t p = 0; p < k; p++) {
+      int64_t qv = q[i * k + p];
+      const int8_t* brow = x2 + p * n;
+      for (int64_t j = 0; j < n; j++) row[j] += qv * (int64_t)brow[j];
+    }
+    for (int64_t j = 0; j < n; j++) {
+      if (row[j] > INT32_MAX || row[j] < INT32_MIN) overflow++;
+      acc[i * n + j] = (int32_t)row[j];
+    }
+    free(row);
+  }
+  return overflow;
+}
+
+/*
+ * output = output_quant x x1_scale x x2_scale + bias, per token x per channel,
+ * evaluated in fp64 and rounded once to out_dtype (bf16 or fp16).
+ * bias may be NULL (zero).
+ */
+void orc_dequant(const int32_t* acc, const float* s1, const float* s2, const uint16_t* bias,
+                 int64_t m, int64_t n, int out_dtype, uint16_t* out) {
+#pragma omp parallel for schedule(static)
+  for (int64_t i = 0; i < m; i++)
+    for (int64_t j = 0; j < n; j++) {
+      double v = (double)acc[i * n + j] * (double)s1[i] * (double)s2[j];
+      if (bias) v += dec16(out_dtype, bias[j]);
+      out[i * n + j] = enc16(out_dtype, v);
+    }
+}
+
+/*
+ * The whole chain for x1 of shape (bs, h) on r ranks.  Intermediate outputs
+ * (permuted, q, s1, acc) are returned when the pointers are non-NULL.
+ * Returns the int32 overflow count of the matmul.
+ */
+int64_t orc_alltoall_quant_matmul(const uint16_t* x1, int r, int64_t bs, int64_t h, int dtype,
+                                  const int8_t* x2, int64_t n, const float* x2_scale,
+                                  const uint16_t* smooth, const uint16_t* bias, uint16_t* out,
+                                  uint16_t* permuted, int8_t* q_out, float* s1_out,
+                                  int32_t* acc_out) {
+  int64_t rows = bs / r, cols = (int64_t)r * h;
+  uint16_t* p = (uint16_t*)malloc(sizeof(uint16_t) * (size_t)(rows * cols));
+  int8_t* q = (int8_t*)malloc((size_t)(rows * cols));
+  float* s1 = (float*)malloc(sizeof(float) * (size_t)rows);
+  int32_t* acc = (int32_t*)malloc(sizeof(int32_t) * (size_t)(rows * n));
+  orc_permute(x1, r, bs, h, p);
+  orc_smooth_quant(p, rows, cols, smooth, dtype, q, s1);
+  int64_t ovf = orc_int8_matmul(q, x2, rows, n, cols, acc);
+  orc_dequant(acc, s1, x2_scale, bias, rows, n, dtype, out);
+  if (permuted) memcpy(permuted, p, sizeof(uint16_t) * (size_t)(rows * cols));
+  if (q_out) memcpy(q_out, q, (size_t)(rows * cols));
+  if (s1_out) memcpy(s1_out, s1, sizeof(float) * (size_t)rows);
+  if (acc_out) memcpy(acc_out, acc, sizeof(int32_t) * (size_t)(rows * n));
+  free(p);
+  free(q);
+  free(s1);
+  free(acc);
+  return ovf;
+}
+
+/* ------------------------------------------------------------------------ */
+/* [QAR] QuantAllReduce: output = sum over ranks of scale * x.               */
+/* ------------------------------------------------------------------------ */
+
+static double dec_x(int x_dtype, const void* x, int64_t e) {
+  switch (x_dtype) {
+    case O_I8: return (double)((const int8_t*)x)[e];
+    case O_E4M3FN: return orc_e4m3fn_to_f64(((const uint8_t*)x)[e]);
+    case O_E5M2: return orc_e5m2_to_f64(((const uint8_t*)x)[e]);
+    default: return NAN;
+  }
+}
+
+/*
+ * x[i]: rank i's (rows, h) tensor; scales[i]: its scales.
+ *   scale_dtype F32 (per-token per-group, group 128): scale index row*(h/128) + c/128.
+ *   scale_dtype E8M0 (mx, block 32): the (rows, h/64, 2) tensor is the
+ *     row-major packing of (rows, h/32), scale index row*(h/32) + c/32.
+ * out[e] = sum_{i=0..r-1} dec(x_i[e]) * dec(scale_i[g(e)]), fp64 in rank
+ * order, rounded once to out_dtype (F32, BF16 or F16).  Returns 0, or -1 on
+ * an unsupported dtype combination.
+ */
+int orc_quant_all_reduce(const void* const* x, const void* const* scales, int r, int64_t rows,
+                         int64_t h, int x_dtype, int scale_dtype, void* out, int out_dtype) {
+  if (scale_dtype == O_F32 && !(x_dtype == O_I8 || x_dtype == O_E4M3FN || x_dtype == O_E5M2)) return -1;
+  if (scale_dtype == O_E8M0 && !(x_dtype == O_E4M3FN || x_dtype == O_E5M2)) return -1;
+  if (scale_dtype != O_F32 && scale_dtype != O_E8M0) return -1;
+  if (out_dtype != O_F32 && out_dtype != O_BF16 && out_dtype != O_F16) return -1;
+#pragma omp parallel for schedule(static)
+  for (int64_t t = 0; t < rows; t++)
+    for (int64_t c = 0; c < h; c++) {
+      int64_t e = t * h + c;
+      double sum = 0.0;
+      for (int i = 0; i < r; i++) {
+        double s = scale_dtype == O_F32 ? (double)((const float*)scales[i])[t * (h / 128) + c / 128]
+                                        : orc_e8m0_to_f64(((const uint8_t*)scales[i])[t * (h / 32) + c / 32]);
+        sum += dec_x(x_dtype, x[i], e) * s;
+      }
+      if (out_dtype == O_F32)
+        ((float*)out)[e] = orc_f64_to_f32(sum);
+      else
+        ((uint16_t*)out)[e] = enc16(out_dtype, sum);
+    }
+  return 0;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Array forms of the format routines (for the format tests).               */
+/* ------------------------------------------------------------------------ */
+int orc_decode_array(int dtype, int64_t n, const void* in, double* out) {
+  for (int64_t i = 0; i < n; i++) {
+    switch (dtype) {
+      case O_F32: out[i] = (double)((const float*)in)[i]; break;
+      case O_F16: out[i] = orc_f16_to_f64(((const uint16_t*)in)[i]); break;
+      case O_BF16: out[i] = orc_bf16_to_f64(((const uint16_t*)in)[i]); break;
+      case O_I8: out[i] = (double)((const int8_t*)in)[i]; break;
+      case O_E4M3FN: out[i] = orc_e4m3fn_to_f64(((const uint8_t*)in)[i]); break;
+      case O_E5M2: out[i] = orc_e5m2_to_f64(((const uint8_t*)in)[i]); break;
+      case O_E8M0: out[i] = orc_e8m0_to_f64(((const uint8_t*)in)[i]); break;
+      default: return -1;
+    }
+  }
+  return 0;
+}
+
+int orc_encode_array(int dtype, int64_t n, const double* in, void* out) {
+  for (int64_t i = 0; i < n; i++) {
+    switch (dtype) {
+      case O_F32: ((float*)out)[i] = orc_f64_to_f32(in[i]); break;
+      case O_F16: ((uint16_t*)out)[i] = orc_f64_to_f16(in[i]); break;
+      case O_BF16: ((uint16_t*)out)[i] = orc_f64_to_bf16(in[i]); break;
+      default: return -1;
+    }
+  }
+  return 0;
+}

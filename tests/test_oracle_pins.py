@@ -1,0 +1,362 @@
+"""Pins for the oracle's operators (CPU).
+
+Every check compares the oracle with something that is not the oracle: hand
+worked fixtures from the pages' formulas (tests/golden), exact rational brute
+force on tiny inputs, integer special cases that any correct implementation
+must reproduce exactly, library routines (numpy int64 / float64 matmul,
+reshape / transpose), and invariants the pages state (the fused result equals
+gather-then-multiply, dX / dW adjointness, the per-token quant error bound).
+"""
+import json
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+import mc2_inputs
+import oracle
+from brute import decode16, exact_matmul, near_tie, round_rne
+
+GOLD = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def gold(name):
+    with open(os.path.join(GOLD, name)) as f:
+        return json.load(f)
+
+
+def enc(vals, fmt):
+    """Brute-force encode of exact values (test-side, not the oracle's encoder)."""
+    arr = np.array([round_rne(v, fmt) for v in np.asarray(vals, dtype=np.float64).ravel()],
+                   dtype=np.uint16).reshape(np.shape(vals))
+    return arr.view(np.float16) if fmt == "f16" else arr
+
+
+def bits(a):
+    return np.asarray(a).view(np.uint16)
+
+
+# ----------------------------------------------------------------- AllGatherMatmul
+def test_ag_worked_example():
+    g = gold("worked_examples.json")["allgather_matmul"]
+    shards = [enc(s, "bf16") for s in g["shards"]]
+    out, gat = oracle.allgather_matmul(shards, enc(g["x2"], "bf16"), "bf16")
+    assert np.array_equal(bits(out), bits(enc(g["out"], "bf16")))
+    assert np.array_equal(bits(gat), bits(enc(g["gather_out"], "bf16")))
+
+
+def test_ag_example_shapes_and_gather_is_concat():
+    ex = gold("ag_example.json")
+    seed, dims, specs = mc2_inputs.CONFIGS["ag_tiny"]
+    assert dims["r"] == ex["world_size"]
+    assert (dims["r"] * dims["m_local"], dims["k"]) == tuple(ex["x1_shape"])
+    assert (dims["k"], dims["n"]) == tuple(ex["x2_shape"])
+    assert [dims["m_local"], dims["k"]] == ex["single_shape"]
+    assert ex["k_min"] <= dims["k"] < ex["k_max_exclusive"]
+    t = mc2_inputs.make("ag_tiny")
+    shards = [t[f"shard{i}"] for i in range(dims["r"])]
+    out, gat = oracle.allgather_matmul(shards, t["x2"], "f16")
+    assert out.shape == tuple(ex["out_shape"]) and gat.shape == tuple(ex["gather_out_shape"])
+    assert np.array_equal(bits(gat), bits(np.concatenate(shards, axis=0)))
+
+
+@pytest.mark.parametrize("r,m_l,k,n,dtype", [
+    (2, 1, 256, 1, "bf16"), (2, 3, 300, 7, "f16"), (4, 1, 256, 7, "bf16"), (8, 1, 257, 2, "f16"),
+])
+def test_ag_matches_exact_rational_brute_force(r, m_l, k, n, dtype):
+    specs = mc2_inputs.configs.scaled("ag", r=r, m_local=m_l, k=k, n=n, dtype=dtype)
+    t = mc2_inputs.make(specs, seed=100 + r + k)
+    shards = [t[f"shard{i}"] for i in range(r)]
+    out, _ = oracle.allgather_matmul(shards, t["x2"], dtype)
+    a = decode16(np.concatenate(shards), dtype)
+    b = decode16(t["x2"], dtype)
+    exact = exact_matmul(a, b)
+    for i in range(r * m_l):
+        for j in range(n):
+            want = round_rne(exact[i][j], dtype)
+            if near_tie(exact[i][j], dtype):
+                continue  # fp64 summation may legitimately land on either side
+            assert int(bits(out)[i, j]) == want, (i, j)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_ag_exact_integer_case(dtype):
+    """Small integers: every partial sum is an exact integer, so the result is the integer matmul."""
+    rng = np.random.default_rng(7)
+    r, m_l, k, n = 4, 5, 256, 9
+    ints = [rng.integers(-2, 3, (m_l, k)) for _ in range(r)]
+    x2i = rng.integers(-1, 2, (k, n))
+    shards = [enc(s, dtype) for s in ints]
+    out, _ = oracle.allgather_matmul(shards, enc(x2i, dtype), dtype)
+    want = np.concatenate(ints) @ x2i  # exact integers; rounded to the format by brute force
+    assert np.array_equal(bits(out), bits(enc(want, dtype)))
+
+
+def test_ag_fused_equals_unfused_and_block_invariance():
+    specs = mc2_inputs.configs.scaled("ag", r=4, m_local=6, k=320, n=40, dtype="bf16")
+    t = mc2_inputs.make(specs, seed=11)
+    shards = [t[f"shard{i}"] for i in range(4)]
+    out, gat = oracle.allgather_matmul(shards, t["x2"], "bf16")
+    assert np.array_equal(out, oracle.matmul(np.concatenate(shards), t["x2"], "bf16"))
+    perm = [2, 0, 3, 1]
+    out_p, _ = oracle.allgather_matmul([shards[i] for i in perm], t["x2"], "bf16")
+    for pos, src in enumerate(perm):
+        assert np.array_equal(out_p[pos * 6:(pos + 1) * 6], out[src * 6:(src + 1) * 6])
+
+
+def test_ag_x2_transposed_view():
+    specs = mc2_inputs.configs.scaled("ag", r=2, m_local=4, k=256, n=24, dtype="f16")
+    t = mc2_inputs.make(specs, seed=12)
+    shards = [t["shard0"], t["shard1"]]
+    out, _ = oracle.allgather_matmul(shards, t["x2"], "f16")
+    out_t, _ = oracle.allgather_matmul(shards, np.ascontiguousarray(t["x2"].T), "f16", x2_trans=True)
+    assert np.array_equal(bits(out), bits(out_t))
+
+
+def test_ag_against_float64_library_matmul():
+    """numpy float64 matmul, then brute-force rounding; near-ties excused."""
+    specs = mc2_inputs.configs.scaled("ag", r=8, m_local=2, k=512, n=33, dtype="bf16", x2_std=0.02)
+    t = mc2_inputs.make(specs, seed=13)
+    shards = [t[f"shard{i}"] for i in range(8)]
+    out, _ = oracle.allgather_matmul(shards, t["x2"], "bf16")
+    ref = decode16(np.concatenate(shards), "bf16") @ decode16(t["x2"], "bf16")
+    want = enc(ref, "bf16")
+    diff = np.nonzero(bits(out) != want)
+    for i, j in zip(*diff):
+        assert abs(int(bits(out)[i, j]) - int(want[i, j])) == 1 and near_tie(Fraction(ref[i, j]), "bf16", 1e-9)
+
+
+# ----------------------------------------------------------------- column-parallel backward
+def test_bwd_worked_example():
+    g = gold("worked_examples.json")["column_parallel_backward"]
+    dy, w, x = (enc(g[k], "bf16") for k in ("dy", "w", "ag_x"))
+    assert np.array_equal(bits(oracle.matmul_grad_input(dy, w)), bits(enc(g["dx"], "bf16")))
+    assert np.array_equal(bits(oracle.matmul_grad_weight(dy, x)), bits(enc(g["dw"], "bf16")))
+
+
+def test_bwd_adjoint_identity_exact():
+    """<dY, G W^T> = <dY W, G> = <dY^T G, W> with small integers, all exact."""
+    rng = np.random.default_rng(3)
+    m, n_l, k = 24, 16, 40
+    G = rng.integers(-3, 4, (m, k))
+    W = rng.integers(-3, 4, (n_l, k))
+    dY = rng.integers(-3, 4, (m, n_l))
+    Gb, Wb, dYb = enc(G, "bf16"), enc(W, "bf16"), enc(dY, "bf16")
+    Y = decode16(oracle.matmul(Gb, Wb, "bf16", b_trans=True), "bf16")       # forward G @ W^T
+    dX = decode16(oracle.matmul_grad_input(dYb, Wb), "bf16")
+    dW = decode16(oracle.matmul_grad_weight(dYb, Gb), "bf16")
+    assert np.array_equal(Y, G @ W.T) and np.array_equal(dX, dY @ W) and np.array_equal(dW, dY.T @ G)
+    lhs = np.sum(dY * Y)
+    assert lhs == np.sum(dX * G) == np.sum(dW * W)
+
+
+def test_bwd_dw_is_sum_over_gathered_blocks():
+    """dW = dY^T AG(X) = sum_i dY[block i]^T X_i (the gather / dW duality)."""
+    rng = np.random.default_rng(4)
+    r, m_l, n_l, k = 4, 6, 8, 12
+    X = [rng.integers(-3, 4, (m_l, k)) for _ in range(r)]
+    dY = rng.integers(-3, 4, (r * m_l, n_l))
+    dW = decode16(oracle.matmul_grad_weight(enc(dY, "bf16"), enc(np.concatenate(X), "bf16")), "bf16")
+    blocks = sum(dY[i * m_l:(i + 1) * m_l].T @ X[i] for i in range(r))
+    assert np.array_equal(dW, blocks)
+
+
+def test_bwd_against_float64_library_matmul():
+    specs = mc2_inputs.configs.scaled("bwd", m=64, n_local=96, k=80)
+    t = mc2_inputs.make(specs, seed=14)
+    dx = oracle.matmul_grad_input(t["dy"], t["w"])
+    dw = oracle.matmul_grad_weight(t["dy"], t["ag_x"])
+    for got, ref in ((dx, decode16(t["dy"], "bf16") @ decode16(t["w"], "bf16")),
+                     (dw, decode16(t["dy"], "bf16").T @ decode16(t["ag_x"], "bf16"))):
+        want = enc(ref, "bf16")
+        for i, j in zip(*np.nonzero(got != want)):
+            assert near_tie(Fraction(ref[i, j]), "bf16", 1e-9)
+
+
+# ----------------------------------------------------------------- AlltoAllQuantMatmul
+def test_permute_worked_example_and_library_form():
+    g = gold("worked_examples.json")["permute"]
+    x1 = np.array(g["x1"], dtype=np.uint16)
+    assert np.array_equal(oracle.permute(x1, g["rank_size"]), np.array(g["permuted"], dtype=np.uint16))
+    rng = np.random.default_rng(5)
+    for r, bs, h in ((2, 6, 5), (4, 8, 16), (8, 16, 3), (1, 5, 7)):
+        x = rng.integers(0, 65535, (bs, h)).astype(np.uint16)
+        p = oracle.permute(x, r)
+        assert np.array_equal(p, x.reshape(r, bs // r, h).transpose(1, 0, 2).reshape(bs // r, r * h))
+        back = p.reshape(bs // r, r, h).transpose(1, 0, 2).reshape(bs, h)  # inverse permute
+        assert np.array_equal(back, x)
+        if r == 1:
+            assert np.array_equal(p, x)
+
+
+def test_smooth_quant_worked_example():
+    g = gold("worked_examples.json")["smooth_quant"]
+    for row, sm, q_want, s_want in zip(g["p"], g["smooth_rows"], g["q"], g["s1"]):
+        q, s1 = oracle.smooth_quant(enc([row], "bf16"), enc(sm, "bf16"))
+        assert q.tolist() == [q_want] and float(s1[0]) == s_want
+
+
+def test_smooth_quant_bounds_and_closed_forms():
+    specs = mc2_inputs.configs.scaled("a16w8", r=4, bs=64, h=96, n=8)
+    t = mc2_inputs.make(specs, seed=15)
+    p = oracle.permute(t["x1"], 4)
+    q, s1 = oracle.smooth_quant(p, t["x1_smooth"])
+    y = decode16(p, "bf16") * decode16(t["x1_smooth"], "bf16")   # exact in fp64
+    amax = np.abs(y).max(axis=1)
+    assert np.all(s1 > 0)
+    # scale is the row absmax over 127, correctly rounded to fp32
+    for i in range(len(s1)):
+        assert Fraction(float(s1[i])) == Fraction(float(np.float32(Fraction(float(amax[i])) / 127)))
+    assert np.all(np.abs(q).max(axis=1) == 127)
+    # |q - y/s| <= 1/2 plus the fp32 division error of y/s (|y/s| <= 127: at most 2^-17)
+    err = np.abs(q * s1[:, None].astype(np.float64) - y)
+    assert np.all(err <= s1[:, None] * (0.5 + 2.0 ** -17))
+    # closed form: integer rows whose absmax is 127 with unit smoothing give scale 1, q = y
+    rng = np.random.default_rng(6)
+    ints = rng.integers(-127, 128, (5, 64))
+    ints[:, 3] = 127
+    q2, s2 = oracle.smooth_quant(enc(ints, "bf16"), None)
+    assert np.all(s2 == 1.0) and np.array_equal(q2, ints)
+    # zero row
+    q3, s3 = oracle.smooth_quant(np.zeros((2, 32), np.uint16), None)
+    assert np.all(q3 == 0) and np.all(s3 == 0)
+
+
+def test_int8_matmul_and_dequant_worked_example():
+    g = gold("worked_examples.json")["int8_matmul_dequant"]
+    acc = oracle.int8_matmul(np.array(g["q"], np.int8), np.array(g["x2"], np.int8))
+    assert acc.tolist() == g["acc"]
+    out = oracle.dequant(acc, np.array(g["s1"], np.float32), np.array(g["s2"], np.float32),
+                         enc(g["bias"], "bf16"))
+    assert np.array_equal(out, enc(g["out_bf16"], "bf16"))
+
+
+def test_int8_matmul_vs_int64_library_and_selection():
+    rng = np.random.default_rng(8)
+    q = rng.integers(-127, 128, (9, 300)).astype(np.int8)
+    x2 = rng.integers(-127, 128, (300, 17)).astype(np.int8)
+    assert np.array_equal(oracle.int8_matmul(q, x2), q.astype(np.int64) @ x2.astype(np.int64))
+    sel = np.zeros((300, 4), np.int8)
+    cols = [0, 299, 17, 150]
+    for j, c in enumerate(cols):
+        sel[c, j] = 1
+    assert np.array_equal(oracle.int8_matmul(q, sel), q[:, cols].astype(np.int32))
+    # the extreme that the rank_size * H <= 35000 constraint keeps inside int32
+    big = oracle.int8_matmul(np.full((1, 35000), -128, np.int8), np.full((35000, 1), -128, np.int8))
+    assert int(big[0, 0]) == 35000 * 128 * 128
+
+
+def test_dequant_unit_and_power_of_two_scales():
+    rng = np.random.default_rng(9)
+    acc = rng.integers(-2 ** 20, 2 ** 20, (6, 10)).astype(np.int32)
+    ones = np.ones(6, np.float32), np.ones(10, np.float32)
+    assert np.array_equal(oracle.dequant(acc, *ones, None), enc(acc.astype(np.float64), "bf16"))
+    s1 = np.exp2(rng.integers(-10, 3, 6)).astype(np.float32)
+    s2 = np.exp2(rng.integers(-12, 0, 10)).astype(np.float32)
+    want = enc(acc * s1[:, None].astype(np.float64) * s2[None, :], "bf16")
+    assert np.array_equal(oracle.dequant(acc, s1, s2, None), want)
+
+
+def test_alltoall_chain_is_composition_of_steps():
+    specs = mc2_inputs.configs.scaled("a16w8", r=4, bs=32, h=64, n=24)
+    t = mc2_inputs.make(specs, seed=16)
+    res = oracle.alltoall_quant_matmul(t["x1"], 4, t["x2"], t["x2_scale"], t["x1_smooth"], t["bias"])
+    p = oracle.permute(t["x1"], 4)
+    q, s1 = oracle.smooth_quant(p, t["x1_smooth"])
+    acc = oracle.int8_matmul(q, t["x2"])
+    assert np.array_equal(res["permuted"], p) and np.array_equal(res["q"], q)
+    assert np.array_equal(res["s1"], s1) and np.array_equal(res["acc"], acc)
+    assert np.array_equal(res["out"], oracle.dequant(acc, s1, t["x2_scale"], t["bias"]))
+    # and the float result is close to the unquantised smooth matmul (quantisation error only)
+    y = decode16(p, "bf16") * decode16(t["x1_smooth"], "bf16")
+    ref = (y @ t["x2"].astype(np.float64)) * t["x2_scale"].astype(np.float64) + decode16(t["bias"], "bf16")
+    got = decode16(res["out"], "bf16")
+    assert np.max(np.abs(got - ref)) <= 0.02 * np.sqrt(np.mean(ref ** 2)) + 0.01 * np.max(np.abs(ref))
+
+
+# ----------------------------------------------------------------- QuantAllReduce
+def test_qar_worked_examples():
+    w = gold("worked_examples.json")
+    g = w["quant_all_reduce_pergroup"]
+    h = g["h"]
+    xs = [np.repeat(np.array(v, np.int8), 128)[None, :] for v in g["x_group_values"]]
+    sc = [np.array([s], np.float32) for s in g["scales"]]
+    out = oracle.quant_all_reduce(xs, sc, "i8", "f32", "f32")
+    assert out.shape == (1, h)
+    assert np.array_equal(out[0], np.repeat(np.array(g["out_group_values"], np.float32), 128))
+    g = w["quant_all_reduce_mx"]
+    xs = [np.repeat(np.array(v, np.uint8), 32)[None, :] for v in g["x_block_codes"]]
+    sc = [np.array(s, np.uint8).reshape(1, g["h"] // 64, 2) for s in g["scale_codes"]]
+    out = oracle.quant_all_reduce(xs, sc, "e4m3fn", "e8m0", "bf16")
+    assert np.array_equal(out[0], enc(np.repeat(g["out_block_values"], 32), "bf16"))
+
+
+def test_qar_scale_sizes_match_pages():
+    for c in gold("qar_sizes.json")["cases"]:
+        specs = mc2_inputs.configs.scaled("qar_int8", r=2, shape=(c["b"], c["s"], c["H"]))
+        assert tuple(specs["scale0"].shape) == tuple(c["pergroup_scale_shape"])
+        assert np.prod(specs["x0"].shape) == c["x_bytes"]
+        assert np.prod(specs["scale0"].shape) * 4 == c["pergroup_scale_bytes"]
+        specs = mc2_inputs.configs.scaled("qar_mx", r=2, shape=(c["b"], c["s"], c["H"]))
+        assert tuple(specs["scale0"].shape) == tuple(c["mx_scale_shape"])
+        assert np.prod(specs["scale0"].shape) == c["mx_scale_bytes"]
+
+
+@pytest.mark.parametrize("r", [2, 4, 8])
+def test_qar_unit_scales_integer_sum(r):
+    rng = np.random.default_rng(r)
+    xs = [rng.integers(-127, 128, (3, 1024)).astype(np.int8) for _ in range(r)]
+    ones = [np.ones((3, 8), np.float32) for _ in range(r)]
+    out = oracle.quant_all_reduce(xs, ones, "i8", "f32", "f32")
+    assert np.array_equal(out, np.sum([x.astype(np.int64) for x in xs], axis=0).astype(np.float32))
+    # mx: E8M0 127 is 1.0; small integers are exact E4M3FN codes
+    vals = np.arange(-8, 9)
+    codes = {v: int(np.where(oracle.decode("e4m3fn", np.arange(256, dtype=np.uint8)) == v)[0][0]) for v in vals}
+    xi = [rng.integers(-8, 9, (2, 1024)) for _ in range(r)]
+    xc = [np.vectorize(codes.get)(x).astype(np.uint8) for x in xi]
+    s127 = [np.full((2, 16, 2), 127, np.uint8) for _ in range(r)]
+    out = oracle.quant_all_reduce(xc, s127, "e4m3fn", "e8m0", "bf16")
+    assert np.array_equal(out, enc(np.sum(xi, axis=0).astype(np.float64), "bf16"))
+
+
+def test_qar_group_mapping_against_library_repeat():
+    """Scales that differ per group reveal the element -> scale mapping."""
+    rng = np.random.default_rng(10)
+    rows, h, r = 3, 1024, 2
+    xs = [np.ones((rows, h), np.int8) for _ in range(r)]
+    sc = [np.exp2(rng.integers(-6, 6, (rows, h // 128))).astype(np.float32) for _ in range(r)]
+    out = oracle.quant_all_reduce(xs, sc, "i8", "f32", "f32")
+    assert np.array_equal(out, np.repeat(sc[0] + sc[1], 128, axis=1))
+    one = np.full((rows, h), 0x38, np.uint8)  # E4M3FN 1.0
+    e = [rng.integers(120, 135, (rows, h // 64, 2)).astype(np.uint8) for _ in range(r)]
+    out = oracle.quant_all_reduce([one, one], e, "e4m3fn", "e8m0", "f32")
+    per_block = np.exp2(e[0].reshape(rows, h // 32).astype(np.float64) - 127) + \
+        np.exp2(e[1].reshape(rows, h // 32).astype(np.float64) - 127)
+    assert np.array_equal(out, np.repeat(per_block, 32, axis=1).astype(np.float32))
+
+
+def test_qar_exact_rational_on_generated_inputs():
+    """Rounded once from the exact sum: compare with Fractions on a slice of the real workload."""
+    specs = mc2_inputs.configs.scaled("qar_int8", r=8, shape=(1, 2, 1024))
+    t = mc2_inputs.make(specs, seed=5)
+    xs = [t[f"x{i}"] for i in range(8)]
+    sc = [t[f"scale{i}"] for i in range(8)]
+    out = oracle.quant_all_reduce(xs, sc, "i8", "f32", "f32").reshape(2, 1024)
+    for tok in range(2):
+        for c in range(0, 1024, 37):
+            exact = sum(Fraction(int(xs[i].reshape(2, 1024)[tok, c])) *
+                        Fraction(float(sc[i].reshape(2, 8)[tok, c // 128])) for i in range(8))
+            assert float(out[tok, c]) == float(np.float32(float(exact))) or \
+                Fraction(float(out[tok, c])) == Fraction(float(np.float32(exact)))
+    specs = mc2_inputs.configs.scaled("qar_mx", r=8, shape=(1, 2, 1024))
+    t = mc2_inputs.make(specs, seed=5)
+    xs = [t[f"x{i}"] for i in range(8)]
+    sc = [t[f"scale{i}"] for i in range(8)]
+    out = oracle.quant_all_reduce(xs, sc, "e4m3fn", "e8m0", "bf16").reshape(2, 1024)
+    dx = [oracle.decode("e4m3fn", x).reshape(2, 1024) for x in xs]
+    for tok in range(2):
+        for c in range(0, 1024, 41):
+            exact = sum(Fraction(float(dx[i][tok, c])) *
+                        Fraction(2) ** (int(sc[i].reshape(2, 32)[tok, c // 32]) - 127) for i in range(8))
+            assert int(out[tok, c]) == round_rne(exact, "bf16")
