@@ -1,0 +1,327 @@
+"""Benchmark of the MC2 per-rank hot path on one MI355X.
+
+One step runs every operator once on its full-size synthetic workload, in
+this order (names as in the JSON "rows"):
+
+  ag_bf16_tp   AllGatherMatmul, 8 x bf16 (512, 4096) shards @ (4096, 1792), + gather_out
+  colpar_dx    column-parallel backward dX = dY (8192, 1792) @ W (1792, 4096)
+  colpar_dw    column-parallel backward dW = dY^T (1792, 8192) @ AG(X) (8192, 4096)
+  a16w8        AlltoAllQuantMatmul A16W8: permute+quant of bf16 (8192, 4096) on 8 ranks,
+               then int8 (1024, 32768) @ (32768, 7168) with per-token x per-channel dequant + bias
+  qar_int8     QuantAllReduce, 8 ranks x int8 (4, 2048, 7168) + fp32 group-128 scales -> fp32
+  qar_mx       QuantAllReduce, 8 ranks x E4M3FN (4, 2048, 7168) + E8M0 mx scales -> bf16
+
+Inputs are generated on the host, copied to HBM before timing, and stay
+resident.  W warm-up steps, then exactly K timed steps between two
+synchronisations.  Per-kernel durations come from HIP events recorded on the
+stream the kernels run on (torch's current stream, which libmc2 is handed).
+The headline value is the AllGatherMatmul's TFLOP/s; every row's figure and
+its roofline fraction are in "rows".  The oracle (CPU) is timed on a bounded
+sample of the AllGatherMatmul workload for the "cpu_baseline" entry.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16 = 2500.0     # TFLOP/s, dense MFMA, MI355X
+PEAK_INT8 = 5000.0     # TOP/s, dense MFMA, MI355X
+PEAK_HBM = 8000.0      # GB/s, MI355X HBM3E
+
+ALL_ROWS = ["ag_bf16_tp", "colpar_dx", "colpar_dw", "a16w8", "qar_int8", "qar_mx"]
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--rows", default=",".join(ALL_ROWS), help="comma-separated subset of rows")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-parity", action="store_true", help="skip the sampled oracle check")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target oracle work for the CPU baseline")
+    return ap.parse_args()
+
+
+class Row:
+    """One operator on its workload: setup -> callables run each step."""
+
+    def __init__(self, name, unit, bound, peak, work, launches):
+        self.name, self.unit, self.bound, self.peak, self.work = name, unit, bound, peak, work
+        self.launches = launches  # list of (kernel label, fn)
+        self.ms = []
+
+
+def setup_rows(names, mc2, torch):
+    import numpy as np
+
+    import mc2_inputs
+    T = mc2_inputs.to_torch
+    rows = {}
+    if "ag_bf16_tp" in names:
+        seed, d, specs = mc2_inputs.CONFIGS["ag_bf16_tp"]
+        t = mc2_inputs.make("ag_bf16_tp")
+        shards = [T(t[f"shard{i}"], "bf16") for i in range(d["r"])]
+        x2 = T(t["x2"], "bf16")
+        m, k, n = d["r"] * d["m_local"], d["k"], d["n"]
+        out = torch.empty((m, n), dtype=torch.bfloat16, device="cuda")
+        g = torch.empty((m, k), dtype=torch.bfloat16, device="cuda")
+        row = Row("ag_bf16_tp", "TFLOP/s", "mfma", PEAK_BF16, 2.0 * m * n * k,
+                  [("gemm_bf16", lambda shards=shards, x2=x2, out=out, g=g:
+                    mc2.mc2_allgather_matmul(shards, x2, out=out, gather_out=g))])
+        row.bytes = 2 * (m * k + k * n + m * n + m * k)
+        row.check = lambda t=t, d=d, out=out, g=g: check_ag(t, d, out, g)
+        rows[row.name] = row
+    if "colpar_dx" in names or "colpar_dw" in names:
+        seed, d, specs = mc2_inputs.CONFIGS["colpar_bwd"]
+        t = mc2_inputs.make("colpar_bwd")
+        dy, w, x = T(t["dy"], "bf16"), T(t["w"], "bf16"), T(t["ag_x"], "bf16")
+        m, nl, k = d["m"], d["n_local"], d["k"]
+        dx = torch.empty((m, k), dtype=torch.bfloat16, device="cuda")
+        dw = torch.empty((nl, k), dtype=torch.bfloat16, device="cuda")
+        if "colpar_dx" in names:
+            row = Row("colpar_dx", "TFLOP/s", "mfma", PEAK_BF16, 2.0 * m * nl * k,
+                      [("gemm_bf16", lambda dy=dy, w=w, dx=dx: mc2.mc2_matmul_grad_input(dy, w, out=dx))])
+            row.bytes = 2 * (m * nl + nl * k + m * k)
+            row.check = lambda t=t, dx=dx: check_bwd(t, dx, "dx")
+            rows[row.name] = row
+        if "colpar_dw" in names:
+            row = Row("colpar_dw", "TFLOP/s", "mfma", PEAK_BF16, 2.0 * m * nl * k,
+                      [("gemm_bf16", lambda dy=dy, x=x, dw=dw: mc2.mc2_matmul_grad_weight(dy, x, out=dw))])
+            row.bytes = 2 * (m * nl + m * k + nl * k)
+            row.check = lambda t=t, dw=dw: check_bwd(t, dw, "dw")
+            rows[row.name] = row
+    if "a16w8" in names:
+        seed, d, specs = mc2_inputs.CONFIGS["a16w8"]
+        t = mc2_inputs.make("a16w8")
+        r, bs, h, n = d["r"], d["bs"], d["h"], d["n"]
+        x1, x2 = T(t["x1"], "bf16"), T(t["x2"], "i8")
+        s2, sm, bias = T(t["x2_scale"], "f32"), T(t["x1_smooth"], "bf16"), T(t["bias"], "bf16")
+        rows_, cols = bs // r, r * h
+        out = torch.empty((rows_, n), dtype=torch.bfloat16, device="cuda")
+        ws = torch.empty(mc2.mc2_alltoall_quant_matmul_workspace_size(r, bs, h, n), dtype=torch.uint8, device="cuda")
+        row = Row("a16w8", "TOP/s", "mfma", PEAK_INT8, 2.0 * rows_ * cols * n,
+                  [("permute_quant+gemm_i8", lambda x1=x1, r=r, x2=x2, s2=s2, sm=sm, bias=bias, out=out, ws=ws:
+                    mc2.mc2_alltoall_quant_matmul(x1, r, x2, s2, sm, bias, out=out, workspace=ws))])
+        row.bytes = 2 * bs * h + 2 * cols + cols * n + 4 * n + 2 * n + 2 * rows_ * n
+        row.check = lambda t=t, d=d, out=out: check_a16w8(t, d, out, mc2, torch)
+        rows[row.name] = row
+    for name, xdt, sdt, odt in (("qar_int8", "i8", "f32", torch.float32), ("qar_mx", "e4m3fn", "e8m0", torch.bfloat16)):
+        if name not in names:
+            continue
+        seed, d, specs = mc2_inputs.CONFIGS[name]
+        t = mc2_inputs.make(name)
+        xs = [T(t[f"x{i}"], xdt) for i in range(d["r"])]
+        sc = [T(t[f"scale{i}"], sdt) for i in range(d["r"])]
+        out = torch.empty(d["shape"], dtype=odt, device="cuda")
+        elems = int(np.prod(d["shape"]))
+        sbytes = (4 * elems // 128) if sdt == "f32" else elems // 32
+        nbytes = d["r"] * (elems + sbytes) + elems * out.element_size()
+        row = Row(name, "GB/s", "hbm", PEAK_HBM, float(nbytes),
+                  [("dequant_sum", (lambda xs=xs, sc=sc, out=out, odt=odt:
+                                    mc2.mc2_quant_all_reduce(xs, sc, out_dtype=odt, out=out)))])
+        row.bytes = nbytes
+        row.check = (lambda t=t, d=d, out=out, xdt=xdt, sdt=sdt: check_qar(t, d, out, xdt, sdt))
+        rows[name] = row
+    return [rows[n] for n in ALL_ROWS if n in rows]
+
+
+# ---------------------------------------------------------------- sampled parity against the oracle
+def _tol16(got, want, dtype):
+    import numpy as np
+    dec = (lambda a: (a.astype(np.uint32) << 16).view(np.float32).astype(np.float64)) if dtype == "bf16" else \
+        (lambda a: a.view(np.float16).astype(np.float64))
+    g, w = dec(got), dec(want)
+    rms = np.sqrt(np.mean(w ** 2))
+    return bool(np.all(np.abs(g - w) <= 1e-2 * np.abs(w) + 1e-2 * rms))
+
+
+def check_ag(t, d, out, g):
+    import numpy as np
+
+    import mc2_inputs
+    import oracle
+    rng = np.random.default_rng(0)
+    rows = np.sort(rng.choice(d["r"] * d["m_local"], 24, replace=False))
+    G = np.concatenate([t[f"shard{i}"] for i in range(d["r"])])
+    want = oracle.matmul(np.ascontiguousarray(G[rows]), t["x2"], "bf16")
+    got = mc2_inputs.from_torch(out)[rows]
+    gat_ok = np.array_equal(mc2_inputs.from_torch(g), G)
+    return bool(gat_ok and _tol16(got, want, "bf16"))
+
+
+def check_bwd(t, res, which):
+    import numpy as np
+
+    import mc2_inputs
+    import oracle
+    rng = np.random.default_rng(1)
+    got = mc2_inputs.from_torch(res)
+    if which == "dx":
+        rows = np.sort(rng.choice(t["dy"].shape[0], 24, replace=False))
+        want = oracle.matmul(np.ascontiguousarray(t["dy"][rows]), t["w"], "bf16")
+    else:
+        rows = np.sort(rng.choice(t["dy"].shape[1], 24, replace=False))
+        want = oracle.matmul(np.ascontiguousarray(t["dy"][:, rows]), t["ag_x"], "bf16", a_trans=True)
+    return _tol16(got[rows], want, "bf16")
+
+
+def check_a16w8(t, d, out, mc2, torch):
+    import numpy as np
+
+    import mc2_inputs
+    import oracle
+    r = d["r"]
+    p = oracle.permute(t["x1"], r)
+    rng = np.random.default_rng(2)
+    toks = np.sort(rng.choice(p.shape[0], 6, replace=False))
+    q, s1 = oracle.smooth_quant(np.ascontiguousarray(p[toks]), t["x1_smooth"])
+    acc = oracle.int8_matmul(q, t["x2"])
+    want = oracle.dequant(acc, s1, t["x2_scale"], t["bias"])
+    return _tol16(mc2_inputs.from_torch(out)[toks], want, "bf16")
+
+
+def check_qar(t, d, out, xdt, sdt):
+    import numpy as np
+
+    import mc2_inputs
+    import oracle
+    r = d["r"]
+    h = d["shape"][-1]
+    rows = d["shape"][0] * d["shape"][1]
+    rng = np.random.default_rng(3)
+    sel = np.sort(rng.choice(rows, 16, replace=False))
+    per = h // 128 if sdt == "f32" else h // 32
+    xs = [np.ascontiguousarray(t[f"x{i}"].reshape(rows, h)[sel]) for i in range(r)]
+    sc = [np.ascontiguousarray(t[f"scale{i}"].reshape(rows, per)[sel]) for i in range(r)]
+    want = oracle.quant_all_reduce(xs, sc, xdt, sdt, "f32" if out.dtype.itemsize == 4 else "bf16")
+    got = mc2_inputs.from_torch(out).reshape(rows, h)[sel]
+    view = np.uint32 if want.dtype == np.float32 else np.uint16
+    return bool(np.array_equal(got.view(view), want.view(view)))
+
+
+# ---------------------------------------------------------------- CPU baseline (the oracle)
+def cpu_baseline(target_s):
+    """Oracle AllGatherMatmul on a row sample of the same workload, scaled to TFLOP/s."""
+    import numpy as np
+
+    import mc2_inputs
+    import oracle
+    seed, d, specs = mc2_inputs.CONFIGS["ag_bf16_tp"]
+    t = mc2_inputs.make("ag_bf16_tp")
+    r, k, n = d["r"], d["k"], d["n"]
+
+    def run(rows_per_shard):
+        shards = [np.ascontiguousarray(t[f"shard{i}"][:rows_per_shard]) for i in range(r)]
+        t0 = time.perf_counter()
+        oracle.allgather_matmul(shards, t["x2"], "bf16")
+        return time.perf_counter() - t0
+
+    probe = 2
+    dt = run(probe)
+    per_shard = int(min(d["m_local"], max(probe, probe * target_s / max(dt, 1e-3))))
+    dt = run(per_shard)
+    flops = 2.0 * r * per_shard * k * n
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": f"AllGatherMatmul rows {per_shard} of each of the {r} shards ({r * per_shard} of "
+                      f"{r * d['m_local']} output rows), k={k}, n={n}, bf16 in, fp64 accumulate; "
+                      f"{dt:.1f} s wall"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on exactly one GPU; --gpus above 1 is not supported "
+                                   "(the r ranks are simulated as r buffers on one device)"}))
+        sys.exit(2)
+    import torch
+
+    import comm_matmul_tensor_amd as mc2
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+    names = [s for s in args.rows.split(",") if s]
+    for s in names:
+        if s not in ALL_ROWS:
+            raise SystemExit(f"unknown row {s}")
+    t0 = time.time()
+    rows = setup_rows(names, mc2, torch)
+    torch.cuda.synchronize()
+    log(f"setup {time.time() - t0:.1f} s; rows: {[r.name for r in rows]}")
+
+    stream = torch.cuda.current_stream()
+
+    def step(record):
+        for row in rows:
+            if record:
+                ev0 = torch.cuda.Event(enable_timing=True)
+                ev1 = torch.cuda.Event(enable_timing=True)
+                ev0.record(stream)
+            for _, fn in row.launches:
+                fn()
+            if record:
+                ev1.record(stream)
+                row.events.append((ev0, ev1))
+
+    for row in rows:
+        row.events = []
+    for _ in range(args.warmup):
+        step(False)
+    torch.cuda.synchronize()
+    log("warm-up done")
+    t_start = time.perf_counter()
+    for _ in range(args.steps):
+        step(True)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_start
+    log(f"timed {args.steps} steps in {wall:.3f} s")
+
+    out_rows = {}
+    for row in rows:
+        ms = [a.elapsed_time(b) for a, b in row.events]
+        avg_ms = sum(ms) / len(ms)
+        achieved = row.work / (avg_ms * 1e-3) / (1e12 if row.unit != "GB/s" else 1e9)
+        out_rows[row.name] = {"achieved": round(achieved, 2), "unit": row.unit, "bound": row.bound,
+                              "peak": row.peak, "frac": round(achieved / row.peak, 4),
+                              "us_per_call": round(avg_ms * 1e3, 2), "min_us": round(min(ms) * 1e3, 2),
+                              "kernels": [k for k, _ in row.launches]}
+    if not args.no_parity:
+        for row in rows:
+            t1 = time.time()
+            out_rows[row.name]["parity"] = "pass" if row.check() else "FAIL"
+            log(f"parity {row.name}: {out_rows[row.name]['parity']} ({time.time() - t1:.1f} s)")
+
+    head = "ag_bf16_tp" if "ag_bf16_tp" in out_rows else rows[0].name
+    h = out_rows[head]
+    res = {
+        "metric": "TFLOPS/TOPS (% MFMA peak) for AG-GEMM & A16W8; GB/s for dequant-sum",
+        "value": h["achieved"], "unit": h["unit"], "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(wall / args.steps * 1e3, 3), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16" if head != "a16w8" else "int8", "data": "synthetic",
+        "config": {"workload": {"ag_bf16_tp": "AllGatherMatmul bf16 TP layer: 8 x (512, 4096) shards @ (4096, 1792)",
+                                }.get(head, head),
+                   "rows_in_step": [r.name for r in rows], "seeds": "workload number (1..5)"},
+        "roofline": {"bound": h["bound"], "achieved": h["achieved"], "peak": h["peak"],
+                     "unit": "TFLOP/s" if h["unit"] == "TFLOP/s" else h["unit"], "frac": h["frac"],
+                     "traffic": None, "kernel": h["kernels"][0]},
+        "rows": out_rows,
+    }
+    if not args.no_cpu_baseline:
+        t1 = time.time()
+        res["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
+        log(f"cpu baseline {time.time() - t1:.1f} s")
+    print(json.dumps(res))
+
+
+if __name__ == "__main__":
+    main()

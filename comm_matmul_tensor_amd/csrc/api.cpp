@@ -1,0 +1,263 @@
+// libmc2 C ABI: host-side validation, device checks and kernel dispatch.
+#include <hip/hip_runtime.h>
+
+#include <cstring>
+#include <mutex>
+#include <string>
+
+#include "kernels.hpp"
+#include "mc2.h"
+#include "validate.hpp"
+
+namespace mc2 {
+namespace {
+
+constexpr int kMaxDevices = 64;
+
+struct DeviceState {
+  bool checked = false;
+  bool ok = false;
+  // arrival emulation: copy stream, ready flags (one per rank block + one
+  // timeout flag) and a call counter that makes every call's flag values new
+  hipStream_t copy_stream = nullptr;
+  unsigned* flags = nullptr;
+  unsigned epoch = 0;
+};
+DeviceState g_dev[kMaxDevices];
+std::mutex g_dev_mutex;
+
+mc2_status hip_fail(hipError_t e, const char* where) {
+  return fail(MC2_ERR_HIP, std::string(where) + ": " + hipGetErrorString(e));
+}
+
+// The current device must be a gfx950 (MI355X class) GPU.
+mc2_status current_device(int* dev_out) {
+  int count = 0;
+  if (hipGetDeviceCount(&count) != hipSuccess || count < 1) {
+    (void)hipGetLastError();
+    return fail(MC2_ERR_NO_DEVICE, "no HIP device");
+  }
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) return fail(MC2_ERR_NO_DEVICE, "device index out of range");
+  std::lock_guard<std::mutex> lock(g_dev_mutex);
+  DeviceState& st = g_dev[dev];
+  if (!st.checked) {
+    hipDeviceProp_t p;
+    e = hipGetDeviceProperties(&p, dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDeviceProperties");
+    st.ok = std::strncmp(p.gcnArchName, "gfx950", 6) == 0;
+    st.checked = true;
+  }
+  if (!st.ok) return fail(MC2_ERR_NO_DEVICE, "the current device is not gfx950");
+  *dev_out = dev;
+  return MC2_OK;
+}
+
+int dt(mc2_dtype d) { return static_cast<int>(d); }
+
+size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+}  // namespace
+}  // namespace mc2
+
+using namespace mc2;
+
+extern "C" {
+
+const char* mc2_status_string(mc2_status s) {
+  switch (s) {
+    case MC2_OK: return "MC2_OK";
+    case MC2_ERR_NULL: return "MC2_ERR_NULL: a required pointer is NULL";
+    case MC2_ERR_SHAPE: return "MC2_ERR_SHAPE: a size breaks the operator's constraints";
+    case MC2_ERR_DTYPE: return "MC2_ERR_DTYPE: dtype not supported";
+    case MC2_ERR_UNSUPPORTED: return "MC2_ERR_UNSUPPORTED: not provided by this library";
+    case MC2_ERR_WORKSPACE: return "MC2_ERR_WORKSPACE: workspace missing or too small";
+    case MC2_ERR_NO_DEVICE: return "MC2_ERR_NO_DEVICE: no gfx950 device";
+    case MC2_ERR_HIP: return "MC2_ERR_HIP: HIP runtime error";
+    case MC2_ERR_ALIGN: return "MC2_ERR_ALIGN: tensor pointer not 16-byte aligned";
+  }
+  return "unknown mc2_status";
+}
+
+const char* mc2_last_error(void) { return last_error_text(); }
+
+mc2_status mc2_quant_all_reduce(const void* const* x, const void* const* scales, int world_size,
+                                int64_t rows, int64_t h, mc2_dtype x_dtype,
+                                mc2_dtype scale_dtype, void* out, mc2_dtype out_dtype,
+                                void* stream) {
+  clear_error();
+  mc2_status s = check_quant_all_reduce(x, scales, world_size, rows, h, x_dtype, scale_dtype, out, out_dtype);
+  if (s != MC2_OK) return s;
+  int dev;
+  if ((s = current_device(&dev)) != MC2_OK) return s;
+  QarArgs a{};
+  for (int i = 0; i < world_size; i++) {
+    a.x[i] = x[i];
+    a.scales[i] = scales[i];
+  }
+  a.out = out;
+  a.total = rows * h;
+  a.h = h;
+  a.r = world_size;
+  a.x_dtype = dt(x_dtype);
+  a.scale_dtype = dt(scale_dtype);
+  a.out_dtype = dt(out_dtype);
+  hipError_t e = launch_dequant_sum(a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "quant_all_reduce launch");
+  return MC2_OK;
+}
+
+mc2_status mc2_matmul_grad_input(const void* dy, const void* w, int64_t m, int64_t n_local,
+                                 int64_t k, mc2_dtype dtype, void* dx_partial, void* stream) {
+  clear_error();
+  mc2_status s = check_grad_input(dy, w, m, n_local, k, dtype, dx_partial);
+  if (s != MC2_OK) return s;
+  int dev;
+  if ((s = current_device(&dev)) != MC2_OK) return s;
+  GemmArgs a{};
+  a.a_parts[0] = dy;  // A = dY (m, n_local), K-contiguous
+  a.num_parts = 1;
+  a.rows_per_part = m;
+  a.a_kmajor = 1;
+  a.b = w;            // B = W (n_local, k): (k_contract, n) row-major
+  a.b_kmajor = 0;
+  a.c = dx_partial;
+  a.m = m;
+  a.n = k;
+  a.k = n_local;
+  a.dtype = dt(dtype);
+  hipError_t e = launch_gemm16(a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "matmul_grad_input launch");
+  return MC2_OK;
+}
+
+mc2_status mc2_matmul_grad_weight(const void* dy, const void* ag_x, int64_t m, int64_t n_local,
+                                  int64_t k, mc2_dtype dtype, void* dw, void* stream) {
+  clear_error();
+  mc2_status s = check_grad_weight(dy, ag_x, m, n_local, k, dtype, dw);
+  if (s != MC2_OK) return s;
+  int dev;
+  if ((s = current_device(&dev)) != MC2_OK) return s;
+  GemmArgs a{};
+  a.a_parts[0] = dy;  // A = dY^T: dy (m, n_local) is A stored transposed
+  a.num_parts = 1;
+  a.rows_per_part = n_local;
+  a.a_kmajor = 0;
+  a.b = ag_x;         // B = AG(X) (m, k): (k_contract, n) row-major
+  a.b_kmajor = 0;
+  a.c = dw;
+  a.m = n_local;
+  a.n = k;
+  a.k = m;
+  a.dtype = dt(dtype);
+  hipError_t e = launch_gemm16(a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "matmul_grad_weight launch");
+  return MC2_OK;
+}
+
+mc2_status mc2_allgather_matmul(const void* const* shards, int world_size, int64_t m_local,
+                                int64_t k, const void* x2, int64_t n, int x2_trans,
+                                mc2_dtype dtype, void* out, void* gather_out, mc2_ag_mode mode,
+                                int rank_id, void* stream) {
+  clear_error();
+  mc2_status s = check_allgather_matmul(shards, world_size, m_local, k, x2, n, dtype, out, gather_out,
+                                        static_cast<int>(mode), rank_id);
+  if (s != MC2_OK) return s;
+  int dev;
+  if ((s = current_device(&dev)) != MC2_OK) return s;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  GemmArgs a{};
+  a.rows_per_part = m_local;
+  a.a_kmajor = 1;
+  a.b = x2;
+  a.b_kmajor = x2_trans ? 1 : 0;
+  a.c = out;
+  a.m = (int64_t)world_size * m_local;
+  a.n = n;
+  a.k = k;
+  a.dtype = dt(dtype);
+  if (mode == MC2_AG_FUSED_WRITE) {
+    for (int i = 0; i < world_size; i++) a.a_parts[i] = shards[i];
+    a.num_parts = world_size;
+    a.gather_out = gather_out;
+    hipError_t e = launch_gemm16(a, st);
+    if (e != hipSuccess) return hip_fail(e, "allgather_matmul launch");
+    return MC2_OK;
+  }
+  return fail(MC2_ERR_UNSUPPORTED, "allgather_matmul: arrival mode not built yet");
+}
+
+mc2_status mc2_alltoall_quant_matmul_workspace_size(int rank_size, int64_t bs, int64_t h,
+                                                    int64_t n, size_t* bytes) {
+  clear_error();
+  if (!bytes) return fail(MC2_ERR_NULL, "workspace_size: bytes is NULL");
+  mc2_status s = check_alltoall_sizes(rank_size, bs, h, n);
+  if (s != MC2_OK) return s;
+  const int64_t rows = bs / rank_size, cols = (int64_t)rank_size * h;
+  *bytes = align_up((size_t)(rows * cols), 256) + align_up((size_t)rows * 4, 256) +
+           gemm_i8_workspace_bytes(rows, n, cols);
+  return MC2_OK;
+}
+
+mc2_status mc2_alltoall_quant_matmul(const void* x1, int rank_size, int64_t bs, int64_t h,
+                                     mc2_dtype x1_dtype, const int8_t* x2, int64_t n,
+                                     const float* x2_scale, const void* x1_smooth,
+                                     const void* bias, void* out, void* permuted_out,
+                                     int8_t* q_out, float* x1_scale_out, int32_t* acc_out,
+                                     void* workspace, size_t workspace_bytes, void* stream) {
+  clear_error();
+  size_t need = 0;
+  mc2_status s = mc2_alltoall_quant_matmul_workspace_size(rank_size, bs, h, n, &need);
+  if (s != MC2_OK) {
+    if (s == MC2_ERR_SHAPE && (!x1 || !x2 || !x2_scale || !out))
+      return fail(MC2_ERR_NULL, "alltoall_quant_matmul: x1, x2, x2_scale and out are required");
+    return s;
+  }
+  s = check_alltoall_quant_matmul(x1, rank_size, bs, h, x1_dtype, x2, n, x2_scale, x1_smooth, bias, out,
+                                  permuted_out, q_out, x1_scale_out, acc_out, workspace, workspace_bytes,
+                                  need);
+  if (s != MC2_OK) return s;
+  int dev;
+  if ((s = current_device(&dev)) != MC2_OK) return s;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const int64_t rows = bs / rank_size, cols = (int64_t)rank_size * h;
+  char* ws = static_cast<char*>(workspace);
+  int8_t* q = q_out ? q_out : reinterpret_cast<int8_t*>(ws);
+  ws += align_up((size_t)(rows * cols), 256);
+  float* s1 = x1_scale_out ? x1_scale_out : reinterpret_cast<float*>(ws);
+  ws += align_up((size_t)rows * 4, 256);
+
+  QuantArgs qa{};
+  qa.x1 = x1;
+  qa.smooth = x1_smooth;
+  qa.q = q;
+  qa.s1 = s1;
+  qa.permuted = permuted_out;
+  qa.bs = bs;
+  qa.h = h;
+  qa.r = rank_size;
+  qa.dtype = dt(x1_dtype);
+  hipError_t e = launch_permute_quant(qa, st);
+  if (e != hipSuccess) return hip_fail(e, "alltoall_quant_matmul quant launch");
+
+  GemmI8Args ga{};
+  ga.a = q;
+  ga.b = x2;
+  ga.s1 = s1;
+  ga.s2 = x2_scale;
+  ga.bias = bias;
+  ga.out = out;
+  ga.acc_out = acc_out;
+  ga.m = rows;
+  ga.n = n;
+  ga.k = cols;
+  ga.dtype = dt(x1_dtype);
+  ga.partials = reinterpret_cast<int32_t*>(ws);
+  e = launch_gemm_i8(ga, st);
+  if (e != hipSuccess) return hip_fail(e, "alltoall_quant_matmul gemm launch");
+  return MC2_OK;
+}
+
+}  // extern "C"

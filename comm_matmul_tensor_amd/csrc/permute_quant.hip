@@ -1,0 +1,178 @@
+// K2: AlltoAll permute + smooth scale + per-token dynamic int8 quantisation
+// (aclnnAlltoAllQuantMatmul page, "function" formulas: permutedOut =
+// commOut.permute(1, 0, 2).view(BS/rankSize, rankSize*H), then
+// Quant(permutedOut * x1Scale)).
+//
+// One workgroup per token t.  The permute is pure addressing: row t of P is
+// the concatenation over ranks j of x1 row j*(bs/r) + t, so consecutive
+// threads read consecutive 16-byte chunks of the r source rows (coalesced)
+// and nothing is written for P unless the caller asks for it.  The token's
+// values stay in registers between the two passes:
+//   pass 1  y = P * smooth in fp32 (exact: two 8- or 11-bit significands),
+//           absmax over the row (wavefront then workgroup reduction; max is
+//           exact in any order)
+//   s       = absmax / 127 (IEEE division)
+//   pass 2  q = clamp(rint(y / s), -127, 127) with IEEE division and
+//           round-half-to-even; an all-zero row gives s = 0 and q = 0.
+// HBM traffic: 2 B read + 1 B written per element, plus the 4-byte scale.
+#include "device.hpp"
+#include "kernels.hpp"
+
+namespace mc2 {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kMaxUnits = 9;  // 16-element units per thread: r*h <= 36864
+
+template <int DT>
+__device__ __forceinline__ float dec16(uint32_t bits) {
+  if constexpr (DT == DT_BF16) return bf16_bits_to_f32(bits & 0xFFFFu);
+  else return f16_bits_to_f32(bits & 0xFFFFu);
+}
+
+__device__ __forceinline__ float block_max(float v, float* red) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
+  const int wave = threadIdx.x / 64, lane = threadIdx.x % 64;
+  if (lane == 0) red[wave] = v;
+  __syncthreads();
+  float m = red[0];
+#pragma unroll
+  for (int w = 1; w < kThreads / 64; w++) m = fmaxf(m, red[w]);
+  return m;
+}
+
+__device__ __forceinline__ int quant1(float y, float s) {
+  float r = __builtin_rintf(y / s);
+  r = fminf(fmaxf(r, -127.0f), 127.0f);
+  return (int)r;
+}
+
+// Vector path: h % 16 == 0, so every 16-element unit of P lies inside one
+// source row and is 32-byte aligned.
+template <int DT>
+__global__ __launch_bounds__(kThreads) void permute_quant_vec(QuantArgs a) {
+  __shared__ float red[kThreads / 64];
+  const int64_t t = blockIdx.x;
+  const int64_t T = a.bs / a.r;
+  const int64_t cols = (int64_t)a.r * a.h;
+  const int units = (int)(cols / 16);
+  const uint16_t* x1 = static_cast<const uint16_t*>(a.x1);
+  const uint16_t* sm = static_cast<const uint16_t*>(a.smooth);
+
+  u32x4 raw[kMaxUnits][2];
+  u32x4 smr[kMaxUnits][2];
+  float amax = 0.0f;
+#pragma unroll
+  for (int v = 0; v < kMaxUnits; v++) {
+    const int u = threadIdx.x + v * kThreads;
+    if (u < units) {
+      const int64_t e = (int64_t)u * 16;          // column in P
+      const int64_t j = e / a.h, c = e - j * a.h;  // source rank block and column
+      const u32x4* src = reinterpret_cast<const u32x4*>(x1 + ((j * T + t) * a.h + c));
+      raw[v][0] = src[0];
+      raw[v][1] = src[1];
+      if (sm) {
+        const u32x4* s = reinterpret_cast<const u32x4*>(sm + e);
+        smr[v][0] = s[0];
+        smr[v][1] = s[1];
+      }
+#pragma unroll
+      for (int hlf = 0; hlf < 2; hlf++)
+#pragma unroll
+        for (int w = 0; w < 4; w++)
+#pragma unroll
+          for (int b = 0; b < 2; b++) {
+            float y = dec16<DT>(raw[v][hlf][w] >> (16 * b));
+            if (sm) y *= dec16<DT>(smr[v][hlf][w] >> (16 * b));
+            amax = fmaxf(amax, __builtin_fabsf(y));
+          }
+    }
+  }
+  amax = block_max(amax, red);
+  const float s = amax / 127.0f;
+  if (threadIdx.x == 0) a.s1[t] = s;
+
+#pragma unroll
+  for (int v = 0; v < kMaxUnits; v++) {
+    const int u = threadIdx.x + v * kThreads;
+    if (u < units) {
+      const int64_t e = (int64_t)u * 16;
+      u32x4 qv;
+#pragma unroll
+      for (int hlf = 0; hlf < 2; hlf++)
+#pragma unroll
+        for (int w = 0; w < 4; w += 2) {
+          uint32_t packed = 0;
+#pragma unroll
+          for (int ww = 0; ww < 2; ww++)
+#pragma unroll
+            for (int b = 0; b < 2; b++) {
+              float y = dec16<DT>(raw[v][hlf][w + ww] >> (16 * b));
+              if (sm) y *= dec16<DT>(smr[v][hlf][w + ww] >> (16 * b));
+              const int q = amax > 0.0f ? quant1(y, s) : 0;
+              packed |= ((uint32_t)q & 0xFFu) << (8 * (2 * ww + b));
+            }
+          qv[2 * hlf + w / 2] = packed;
+        }
+      *reinterpret_cast<u32x4*>(a.q + t * cols + e) = qv;
+      if (a.permuted) {
+        u32x4* dst = reinterpret_cast<u32x4*>(static_cast<uint16_t*>(a.permuted) + t * cols + e);
+        dst[0] = raw[v][0];
+        dst[1] = raw[v][1];
+      }
+    }
+  }
+}
+
+// General path (h not a multiple of 16): element by element, two passes
+// over global memory.  Same arithmetic as the vector path.
+template <int DT>
+__global__ __launch_bounds__(kThreads) void permute_quant_scalar(QuantArgs a) {
+  __shared__ float red[kThreads / 64];
+  const int64_t t = blockIdx.x;
+  const int64_t T = a.bs / a.r;
+  const int64_t cols = (int64_t)a.r * a.h;
+  const uint16_t* x1 = static_cast<const uint16_t*>(a.x1);
+  const uint16_t* sm = static_cast<const uint16_t*>(a.smooth);
+  auto load = [&](int64_t e) {
+    const int64_t j = e / a.h, c = e - j * a.h;
+    const uint16_t bits = x1[(j * T + t) * a.h + c];
+    float y = dec16<DT>(bits);
+    if (sm) y *= dec16<DT>(sm[e]);
+    return y;
+  };
+  float amax = 0.0f;
+  for (int64_t e = threadIdx.x; e < cols; e += kThreads) amax = fmaxf(amax, __builtin_fabsf(load(e)));
+  amax = block_max(amax, red);
+  const float s = amax / 127.0f;
+  if (threadIdx.x == 0) a.s1[t] = s;
+  for (int64_t e = threadIdx.x; e < cols; e += kThreads) {
+    a.q[t * cols + e] = (int8_t)(amax > 0.0f ? quant1(load(e), s) : 0);
+    if (a.permuted) {
+      const int64_t j = e / a.h, c = e - j * a.h;
+      static_cast<uint16_t*>(a.permuted)[t * cols + e] = x1[(j * T + t) * a.h + c];
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_permute_quant(const QuantArgs& a, hipStream_t s) {
+  const int64_t T = a.bs / a.r;
+  const int64_t cols = (int64_t)a.r * a.h;
+  if (T < 1 || cols < 1 || cols > (int64_t)kMaxUnits * kThreads * 16) return hipErrorInvalidValue;
+  const bool vec = a.h % 16 == 0;
+  if (a.dtype == DT_BF16) {
+    if (vec) permute_quant_vec<DT_BF16><<<(unsigned)T, kThreads, 0, s>>>(a);
+    else permute_quant_scalar<DT_BF16><<<(unsigned)T, kThreads, 0, s>>>(a);
+  } else if (a.dtype == DT_F16) {
+    if (vec) permute_quant_vec<DT_F16><<<(unsigned)T, kThreads, 0, s>>>(a);
+    else permute_quant_scalar<DT_F16><<<(unsigned)T, kThreads, 0, s>>>(a);
+  } else {
+    return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace mc2

@@ -1,0 +1,160 @@
+// Host-only argument validation.  Each rule cites the operator page that
+// states it; the checks run before any device call.
+#include "validate.hpp"
+
+#include <climits>
+
+namespace mc2 {
+
+namespace {
+thread_local std::string g_last_error;
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// world_size / rankSize: 2, 4 or 8 (npu_all_gather_base_mm "parameters";
+// aclnnAlltoAllQuantMatmul "constraints"; QuantAllReduce "constraints").
+bool valid_world(int r) { return r == 2 || r == 4 || r == 8; }
+
+bool is_half(mc2_dtype d) { return d == MC2_F16 || d == MC2_BF16; }
+
+std::string str(int64_t v) { return std::to_string(static_cast<long long>(v)); }
+}  // namespace
+
+mc2_status fail(mc2_status s, const std::string& msg) {
+  g_last_error = msg;
+  return s;
+}
+void clear_error() { g_last_error.clear(); }
+const char* last_error_text() { return g_last_error.c_str(); }
+
+mc2_status check_allgather_matmul(const void* const* shards, int world_size, int64_t m_local,
+                                  int64_t k, const void* x2, int64_t n, mc2_dtype dtype,
+                                  const void* out, const void* gather_out, int mode, int rank_id) {
+  if (!shards || !x2 || !out) return fail(MC2_ERR_NULL, "allgather_matmul: shards, x2 and out are required");
+  if (!valid_world(world_size))
+    return fail(MC2_ERR_SHAPE, "allgather_matmul: world_size must be 2, 4 or 8, got " + str(world_size));
+  for (int i = 0; i < world_size; i++)
+    if (!shards[i]) return fail(MC2_ERR_NULL, "allgather_matmul: shard " + str(i) + " is NULL");
+  // input and x2 are 2-D (m, k), (k, n) with 256 <= k < 65535 ("constraints")
+  if (k < 256 || k >= 65535)
+    return fail(MC2_ERR_SHAPE, "allgather_matmul: k must lie in [256, 65535), got " + str(k));
+  if (m_local < 1 || n < 1) return fail(MC2_ERR_SHAPE, "allgather_matmul: empty m_local or n");
+  if ((int64_t)world_size * m_local > INT32_MAX || n > INT32_MAX)
+    return fail(MC2_ERR_SHAPE, "allgather_matmul: m or n above INT32_MAX");
+  // input and x2 are FLOAT16 or BFLOAT16, of the same type ("parameters")
+  if (!is_half(dtype)) return fail(MC2_ERR_DTYPE, "allgather_matmul: dtype must be F16 or BF16");
+  if (mode != MC2_AG_FUSED_WRITE && mode != MC2_AG_ARRIVAL)
+    return fail(MC2_ERR_UNSUPPORTED, "allgather_matmul: unknown mode " + str(mode));
+  if (mode == MC2_AG_ARRIVAL) {
+    if (!gather_out) return fail(MC2_ERR_NULL, "allgather_matmul: arrival mode needs gather_out");
+    if (rank_id < 0 || rank_id >= world_size)
+      return fail(MC2_ERR_SHAPE, "allgather_matmul: rank_id out of range");
+  }
+  for (int i = 0; i < world_size; i++)
+    if (!aligned16(shards[i])) return fail(MC2_ERR_ALIGN, "allgather_matmul: shard not 16-byte aligned");
+  if (!aligned16(x2) || !aligned16(out) || (gather_out && !aligned16(gather_out)))
+    return fail(MC2_ERR_ALIGN, "allgather_matmul: tensor not 16-byte aligned");
+  return MC2_OK;
+}
+
+mc2_status check_grad_input(const void* dy, const void* w, int64_t m, int64_t n_local, int64_t k,
+                            mc2_dtype dtype, const void* dx) {
+  if (!dy || !w || !dx) return fail(MC2_ERR_NULL, "matmul_grad_input: dy, w and dx_partial are required");
+  // the fused kernel contracts over n_local, which must lie in [256, 65535)
+  // (hyper_parallel mc2.py module docstring and backward)
+  if (n_local < 256 || n_local >= 65535)
+    return fail(MC2_ERR_SHAPE, "matmul_grad_input: n_local must lie in [256, 65535), got " + str(n_local));
+  if (m < 1 || k < 1) return fail(MC2_ERR_SHAPE, "matmul_grad_input: empty m or k");
+  if (m > INT32_MAX || k > INT32_MAX) return fail(MC2_ERR_SHAPE, "matmul_grad_input: size above INT32_MAX");
+  if (!is_half(dtype)) return fail(MC2_ERR_DTYPE, "matmul_grad_input: dtype must be F16 or BF16");
+  if (!aligned16(dy) || !aligned16(w) || !aligned16(dx))
+    return fail(MC2_ERR_ALIGN, "matmul_grad_input: tensor not 16-byte aligned");
+  return MC2_OK;
+}
+
+mc2_status check_grad_weight(const void* dy, const void* ag_x, int64_t m, int64_t n_local,
+                             int64_t k, mc2_dtype dtype, const void* dw) {
+  if (!dy || !ag_x || !dw) return fail(MC2_ERR_NULL, "matmul_grad_weight: dy, ag_x and dw are required");
+  if (m < 1 || n_local < 1 || k < 1) return fail(MC2_ERR_SHAPE, "matmul_grad_weight: empty dimension");
+  if (m > INT32_MAX || n_local > INT32_MAX || k > INT32_MAX)
+    return fail(MC2_ERR_SHAPE, "matmul_grad_weight: size above INT32_MAX");
+  if (!is_half(dtype)) return fail(MC2_ERR_DTYPE, "matmul_grad_weight: dtype must be F16 or BF16");
+  if (!aligned16(dy) || !aligned16(ag_x) || !aligned16(dw))
+    return fail(MC2_ERR_ALIGN, "matmul_grad_weight: tensor not 16-byte aligned");
+  return MC2_OK;
+}
+
+mc2_status check_alltoall_sizes(int rank_size, int64_t bs, int64_t h, int64_t n) {
+  // aclnnAlltoAllQuantMatmul "constraints": rankSize 2/4/8; BS divisible by
+  // rankSize; BS and N at most INT32_MAX; no empty tensors; A16W8:
+  // rankSize * H divisible by 16 and within [1, 35000].
+  if (!valid_world(rank_size))
+    return fail(MC2_ERR_SHAPE, "alltoall_quant_matmul: rank_size must be 2, 4 or 8, got " + str(rank_size));
+  if (bs < 1 || h < 1 || n < 1) return fail(MC2_ERR_SHAPE, "alltoall_quant_matmul: empty tensor");
+  if (bs % rank_size != 0)
+    return fail(MC2_ERR_SHAPE, "alltoall_quant_matmul: bs must be divisible by rank_size");
+  if (bs > INT32_MAX || n > INT32_MAX)
+    return fail(MC2_ERR_SHAPE, "alltoall_quant_matmul: bs and n must not exceed INT32_MAX");
+  const int64_t kk = (int64_t)rank_size * h;
+  if (kk > 35000 || kk % 16 != 0)
+    return fail(MC2_ERR_SHAPE, "alltoall_quant_matmul: rank_size*h must be a multiple of 16 in [1, 35000], got " + str(kk));
+  return MC2_OK;
+}
+
+mc2_status check_alltoall_quant_matmul(const void* x1, int rank_size, int64_t bs, int64_t h,
+                                       mc2_dtype x1_dtype, const void* x2, int64_t n,
+                                       const void* x2_scale, const void* x1_smooth,
+                                       const void* bias, const void* out, const void* permuted_out,
+                                       const void* q_out, const void* x1_scale_out,
+                                       const void* acc_out, const void* workspace,
+                                       size_t workspace_bytes, size_t workspace_needed) {
+  // x1, x2, x2Scale and output must not be NULL ("constraints")
+  if (!x1 || !x2 || !x2_scale || !out)
+    return fail(MC2_ERR_NULL, "alltoall_quant_matmul: x1, x2, x2_scale and out are required");
+  mc2_status s = check_alltoall_sizes(rank_size, bs, h, n);
+  if (s != MC2_OK) return s;
+  // A16: 16-bit activations; the smooth scale has x1's dtype ("constraints")
+  if (!is_half(x1_dtype)) return fail(MC2_ERR_DTYPE, "alltoall_quant_matmul: x1 must be F16 or BF16");
+  if (!workspace || workspace_bytes < workspace_needed)
+    return fail(MC2_ERR_WORKSPACE, "alltoall_quant_matmul: workspace needs " + str((int64_t)workspace_needed) + " bytes");
+  const void* ptrs[] = {x1, x2, x2_scale, x1_smooth, bias, out, permuted_out, q_out, x1_scale_out, acc_out, workspace};
+  for (const void* p : ptrs)
+    if (p && !aligned16(p)) return fail(MC2_ERR_ALIGN, "alltoall_quant_matmul: tensor not 16-byte aligned");
+  return MC2_OK;
+}
+
+mc2_status check_quant_all_reduce(const void* const* x, const void* const* scales, int world_size,
+                                  int64_t rows, int64_t h, mc2_dtype x_dtype,
+                                  mc2_dtype scale_dtype, const void* out, mc2_dtype out_dtype) {
+  if (!x || !scales || !out) return fail(MC2_ERR_NULL, "quant_all_reduce: x, scales and out are required");
+  if (!valid_world(world_size))
+    return fail(MC2_ERR_SHAPE, "quant_all_reduce: world_size must be 2, 4 or 8, got " + str(world_size));
+  for (int i = 0; i < world_size; i++)
+    if (!x[i] || !scales[i]) return fail(MC2_ERR_NULL, "quant_all_reduce: x or scales of rank " + str(i) + " is NULL");
+  // no empty tensors; H in [1024, 8192] and 128-aligned ("constraints")
+  if (rows < 1) return fail(MC2_ERR_SHAPE, "quant_all_reduce: empty tensor");
+  if (h < 1024 || h > 8192 || h % 128 != 0)
+    return fail(MC2_ERR_SHAPE, "quant_all_reduce: h must be a multiple of 128 in [1024, 8192], got " + str(h));
+  // E8M0 scales go with E4M3FN / E5M2 x (mx); FLOAT scales with INT8,
+  // E4M3FN or E5M2 x (pertoken-pergroup, group 128).  HIFLOAT8 is not
+  // supported: the pages name it but never define it.
+  if (scale_dtype == MC2_E8M0) {
+    if (x_dtype != MC2_F8E4M3FN && x_dtype != MC2_F8E5M2)
+      return fail(MC2_ERR_DTYPE, "quant_all_reduce: E8M0 scales need E4M3FN or E5M2 x");
+  } else if (scale_dtype == MC2_F32) {
+    if (x_dtype != MC2_I8 && x_dtype != MC2_F8E4M3FN && x_dtype != MC2_F8E5M2)
+      return fail(MC2_ERR_DTYPE, "quant_all_reduce: FLOAT scales need INT8, E4M3FN or E5M2 x");
+  } else {
+    return fail(MC2_ERR_DTYPE, "quant_all_reduce: scales must be F32 or E8M0");
+  }
+  // output FLOAT, FLOAT16 or BFLOAT16 (parameter table)
+  if (out_dtype != MC2_F32 && out_dtype != MC2_F16 && out_dtype != MC2_BF16)
+    return fail(MC2_ERR_DTYPE, "quant_all_reduce: out must be F32, F16 or BF16");
+  for (int i = 0; i < world_size; i++)
+    if (!aligned16(x[i]) || !aligned16(scales[i]))
+      return fail(MC2_ERR_ALIGN, "quant_all_reduce: tensor not 16-byte aligned");
+  if (!aligned16(out)) return fail(MC2_ERR_ALIGN, "quant_all_reduce: out not 16-byte aligned");
+  return MC2_OK;
+}
+
+}  // namespace mc2

@@ -1,0 +1,206 @@
+/*
+ * mc2.h -- C ABI of libmc2: the per-rank compute of the MC2 fused
+ * communication + matmul operators on one AMD Instinct MI355X (gfx950).
+ *
+ * On one GPU the r ranks' shards are r separate device buffers, so the
+ * collective steps of each operator (AllGather, AlltoAll) become the gather
+ * and permute addressing the kernels do as they read.  No call here talks to
+ * another GPU.
+ *
+ * Conventions for every entry point
+ *  - Tensors are caller-owned DEVICE pointers (hipMalloc or torch storage),
+ *    row-major and contiguous unless a layout flag says otherwise.  Arrays of
+ *    pointers ("shards", "x", "scales") are HOST arrays of device pointers.
+ *    Every tensor pointer must be 16-byte aligned.
+ *  - `stream` is a hipStream_t passed as void*; NULL means the default
+ *    stream.  Work is enqueued asynchronously on it; the call returns once
+ *    the work is enqueued.
+ *  - Arguments are validated on the host before anything is enqueued.  On a
+ *    validation error nothing is written and no device call is made.
+ *  - Every call returns an mc2_status.  MC2_ERR_HIP means a HIP runtime call
+ *    failed; mc2_last_error() then gives the text (per thread).  Nothing
+ *    aborts and no C++ exception crosses this interface.
+ *  - The library allocates no caller-visible memory and frees none.  Results
+ *    are deterministic: the same inputs give the same bits on every run.
+ *  - Calls on different streams may run concurrently, except that
+ *    MC2_AG_ARRIVAL calls on one device must not overlap each other.
+ */
+#ifndef MC2_H_
+#define MC2_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MC2_OK = 0,
+  MC2_ERR_NULL = 1,        /* a required pointer is NULL */
+  MC2_ERR_SHAPE = 2,       /* a size breaks the operator's constraints */
+  MC2_ERR_DTYPE = 3,       /* dtype, or dtype combination, not supported */
+  MC2_ERR_UNSUPPORTED = 4, /* allowed by the operator but not provided here */
+  MC2_ERR_WORKSPACE = 5,   /* workspace NULL or smaller than required */
+  MC2_ERR_NO_DEVICE = 6,   /* no HIP device, or the current device is not gfx950 */
+  MC2_ERR_HIP = 7,         /* a HIP runtime call failed (see mc2_last_error) */
+  MC2_ERR_ALIGN = 8        /* a tensor pointer is not 16-byte aligned */
+} mc2_status;
+
+typedef enum {
+  MC2_F32 = 0,
+  MC2_F16 = 1,
+  MC2_BF16 = 2,
+  MC2_I8 = 3,
+  MC2_I32 = 4,
+  MC2_F8E4M3FN = 5, /* OCP FLOAT8_E4M3FN: bias 7, max 448, no infinities */
+  MC2_F8E5M2 = 6,   /* OCP FLOAT8_E5M2: bias 15, IEEE-style inf / NaN */
+  MC2_E8M0 = 7      /* OCP MX scale: unsigned exponent, value 2^(b - 127), 0xFF NaN */
+} mc2_dtype;
+
+/* Quant modes of the AlltoAllQuantMatmul page (x1QuantMode / x2QuantMode). */
+typedef enum {
+  MC2_QUANT_NONE = 0,
+  MC2_QUANT_PERTENSOR = 1,
+  MC2_QUANT_PERCHANNEL = 2,
+  MC2_QUANT_PERTOKEN = 3,
+  MC2_QUANT_PERGROUP = 4,
+  MC2_QUANT_PERBLOCK = 5,
+  MC2_QUANT_MX = 6,
+  MC2_QUANT_PERTOKEN_DYNAMIC = 7
+} mc2_quant_mode;
+
+typedef enum {
+  /* the GEMM reads each rank's rows straight from its shard and the
+     workgroups of the first column tile also write gather_out */
+  MC2_AG_FUSED_WRITE = 0,
+  /* arrival emulation: a side stream copies shard i into gather_out block i
+     and raises a per-block ready flag; the GEMM reads A from gather_out and
+     each workgroup starts its K loop once its row block has arrived, the
+     local rank (rank_id) first */
+  MC2_AG_ARRIVAL = 1
+} mc2_ag_mode;
+
+/*
+ * AllGatherMatmul -- torch_npu.npu_all_gather_base_mm (Ascend PyTorch API
+ * page, "function", "outputs" and "constraints" sections):
+ *   gather_out = AllGather_m(shards)           rows [i m_local, (i+1) m_local) = shard i
+ *   out        = gather_out @ x2               fp32 accumulation, rounded to `dtype`
+ *
+ * shards      host array of world_size device pointers, each (m_local, k) of `dtype`
+ * world_size  2, 4 or 8
+ * k           contraction size, 256 <= k < 65535
+ * x2          (k, n) row-major if x2_trans == 0; if x2_trans == 1 the buffer
+ *             holds x2^T as (n, k) row-major (a transposed view, which the
+ *             op accepts for x2 but not for the input)
+ * dtype       MC2_F16 or MC2_BF16, the type of shards, x2, out, gather_out
+ * out         (world_size m_local, n)
+ * gather_out  (world_size m_local, k), or NULL when the gathered input is not
+ *             wanted (the op's gather_output = false); MC2_AG_ARRIVAL needs it
+ * mode        MC2_AG_FUSED_WRITE or MC2_AG_ARRIVAL
+ * rank_id     the calling rank, 0 <= rank_id < world_size: its block is
+ *             local and is consumed first in MC2_AG_ARRIVAL mode (unused in
+ *             MC2_AG_FUSED_WRITE mode)
+ * The op's bias is not accepted (the page allows only a zero bias), and
+ * gather_index / comm_turn exist only with their default 0, so they are not
+ * arguments.
+ */
+mc2_status mc2_allgather_matmul(const void* const* shards, int world_size, int64_t m_local,
+                                int64_t k, const void* x2, int64_t n, int x2_trans,
+                                mc2_dtype dtype, void* out, void* gather_out, mc2_ag_mode mode,
+                                int rank_id, void* stream);
+
+/*
+ * Column-parallel backward, local share of dX -- hyper_parallel mc2.py,
+ * AllGatherMatmulFunction.backward: dX = ReduceScatter_m(dY @ W).  This call
+ * computes one rank's dY @ W before the reduce-scatter:
+ *   dx_partial (m, k) = dy (m, n_local) @ w (n_local, k)
+ * w is the nn.Linear weight in its (out, in) = (n_local, k) layout.  The
+ * contraction runs over n_local, which the fused kernel requires to lie in
+ * [256, 65535).  fp32 accumulation, output rounded to `dtype` (F16 / BF16).
+ */
+mc2_status mc2_matmul_grad_input(const void* dy, const void* w, int64_t m, int64_t n_local,
+                                 int64_t k, mc2_dtype dtype, void* dx_partial, void* stream);
+
+/*
+ * Column-parallel backward, weight gradient -- hyper_parallel mc2.py,
+ * AllGatherMatmulFunction.backward: dW = dY^T @ AllGather_m(X), where
+ * AllGather_m(X) is the gather_out saved by the forward.
+ *   dw (n_local, k) = dy (m, n_local)^T @ ag_x (m, k)
+ * fp32 accumulation, output rounded to `dtype` (F16 / BF16).
+ */
+mc2_status mc2_matmul_grad_weight(const void* dy, const void* ag_x, int64_t m, int64_t n_local,
+                                  int64_t k, mc2_dtype dtype, void* dw, void* stream);
+
+/*
+ * Workspace bytes mc2_alltoall_quant_matmul needs for these sizes (stage one
+ * of the two-stage call of the aclnnAlltoAllQuantMatmul page, "prototype").
+ */
+mc2_status mc2_alltoall_quant_matmul_workspace_size(int rank_size, int64_t bs, int64_t h,
+                                                    int64_t n, size_t* bytes);
+
+/*
+ * AlltoAllQuantMatmul, A16W8 with dynamic per-token quantisation (x1 mode 7,
+ * x2 mode 2) -- aclnnAlltoAllQuantMatmul page, "function" formulas:
+ *   commOut      = AlltoAll(x1.view(rank_size, bs / rank_size, h))
+ *   P            = commOut.permute(1, 0, 2).view(bs / rank_size, rank_size h)
+ *   q, x1_scale  = Quant(P * x1_smooth)       per token: scale = absmax / 127,
+ *                                              q = clamp(rint(y / scale), -127, 127)
+ *   acc          = q @ x2                      exact int32
+ *   out          = acc * x1_scale * x2_scale + bias
+ * On one GPU x1 is this rank's buffer after the AlltoAll: block j of
+ * x1.view(rank_size, bs / rank_size, h) is what rank j sent.
+ *
+ * x1          (bs, h) of x1_dtype (MC2_BF16 or MC2_F16)
+ * rank_size   2, 4 or 8; bs divisible by rank_size; bs, n <= INT32_MAX;
+ *             rank_size h divisible by 16 and in [1, 35000] (A16W8)
+ * x2          (rank_size h, n) int8, row-major, contiguous
+ * x2_scale    (n) fp32 per-channel scale
+ * x1_smooth   (rank_size h) of x1_dtype, or NULL for no smoothing
+ * bias        (n) of x1_dtype, or NULL for a zero bias
+ * out         (bs / rank_size, n) of x1_dtype
+ * permuted_out, q_out, x1_scale_out, acc_out: optional (NULL) copies of P
+ *             (x1_dtype), q (int8), x1_scale (fp32) and acc (int32)
+ * workspace   device memory of at least the size the sizing call returns
+ */
+mc2_status mc2_alltoall_quant_matmul(const void* x1, int rank_size, int64_t bs, int64_t h,
+                                     mc2_dtype x1_dtype, const int8_t* x2, int64_t n,
+                                     const float* x2_scale, const void* x1_smooth,
+                                     const void* bias, void* out, void* permuted_out,
+                                     int8_t* q_out, float* x1_scale_out, int32_t* acc_out,
+                                     void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * QuantAllReduce -- QuantAllReduce README ("function" formula, parameter
+ * table, constraints):
+ *   out = sum over ranks i of dequant(x[i])   with dequant = x * its scale
+ * The sum is exact in fp64, in rank order, and rounded once to out_dtype.
+ *
+ * x           host array of world_size device pointers, each (rows, h) of
+ *             x_dtype; rows = b s for a (b, s, h) tensor
+ * scales      host array of world_size device pointers:
+ *             scale_dtype MC2_F32 : (rows, h / 128) fp32, one scale per token
+ *                                   and 128-element group (pertoken-pergroup)
+ *             scale_dtype MC2_E8M0: (rows, h / 64, 2) E8M0, i.e. one scale per
+ *                                   32-element block (mx)
+ * x_dtype     with MC2_F32 scales: MC2_I8, MC2_F8E4M3FN or MC2_F8E5M2;
+ *             with MC2_E8M0 scales: MC2_F8E4M3FN or MC2_F8E5M2
+ * world_size  2, 4 or 8;  h in [1024, 8192] and a multiple of 128
+ * out         (rows, h) of out_dtype: MC2_F32, MC2_F16 or MC2_BF16
+ */
+mc2_status mc2_quant_all_reduce(const void* const* x, const void* const* scales, int world_size,
+                                int64_t rows, int64_t h, mc2_dtype x_dtype,
+                                mc2_dtype scale_dtype, void* out, mc2_dtype out_dtype,
+                                void* stream);
+
+/* Static text for a status code. */
+const char* mc2_status_string(mc2_status s);
+
+/* Text of the last error on this thread ("" if none). */
+const char* mc2_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MC2_H_ */

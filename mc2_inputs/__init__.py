@@ -83,3 +83,32 @@ def fill(seed: int, tid: int, dist: str, a: float, b: float, dtype: str, shape,
 
 
 from .configs import CONFIGS, TensorSpec, make, make_tensor  # noqa: E402,F401
+
+
+def to_torch(arr: np.ndarray, dtype: str, device="cuda"):
+    """numpy storage (see module doc) -> torch tensor of the matching torch dtype."""
+    import torch
+    arr = np.ascontiguousarray(arr)
+    if dtype == "bf16":
+        t = torch.from_numpy(arr.view(np.int16)).view(torch.bfloat16)
+    elif dtype == "e4m3fn":
+        t = torch.from_numpy(arr).view(torch.float8_e4m3fn)
+    elif dtype == "e5m2":
+        t = torch.from_numpy(arr).view(torch.float8_e5m2)
+    elif dtype == "e8m0":
+        t = torch.from_numpy(arr).view(torch.float8_e8m0fnu)
+    else:
+        t = torch.from_numpy(arr)
+    return t.to(device) if device is not None else t
+
+
+def from_torch(t) -> np.ndarray:
+    """torch tensor -> numpy storage (bf16 as uint16 bits, 8-bit floats as uint8 codes)."""
+    import torch
+    t = t.detach().contiguous().cpu()
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).numpy().view(np.uint16)
+    if t.dtype in (torch.float8_e4m3fn, torch.float8_e5m2) or \
+            (hasattr(torch, "float8_e8m0fnu") and t.dtype == torch.float8_e8m0fnu):
+        return t.view(torch.uint8).numpy()
+    return t.numpy()

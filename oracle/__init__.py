@@ -61,6 +61,7 @@ def _load():
             "orc_quant_all_reduce": (INT, [P, P, INT, I64, I64, INT, INT, P, INT]),
             "orc_decode_array": (INT, [INT, I64, P, P]),
             "orc_encode_array": (INT, [INT, I64, P, P]),
+            "orc_num_threads": (INT, []),
         }
         for name, (res, args) in sig.items():
             f = getattr(lib, name)
@@ -80,6 +81,11 @@ def _ptr(a: Optional[np.ndarray]):
 def _ptr_array(arrs: Sequence[np.ndarray]):
     arr = (ctypes.c_void_p * len(arrs))(*[_ptr(a) for a in arrs])
     return arr
+
+
+def num_threads() -> int:
+    """OpenMP threads the oracle's loops use."""
+    return int(_load().orc_num_threads())
 
 
 # ---------------------------------------------------------------- formats

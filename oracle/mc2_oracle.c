@@ -399,3 +399,11 @@ int orc_encode_array(int dtype, int64_t n, const double* in, void* out) {
   }
   return 0;
 }
+
+/* Threads the OpenMP loops above use (for reporting the CPU baseline). */
+#ifdef _OPENMP
+#include <omp.h>
+int orc_num_threads(void) { return omp_get_max_threads(); }
+#else
+int orc_num_threads(void) { return 1; }
+#endif

@@ -1,0 +1,144 @@
+"""The C-ABI library on the CPU: it loads, exports what include/mc2.h declares,
+and rejects bad arguments on the host before touching any device."""
+import ctypes
+import json
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mc2.h")
+LIB = os.path.join(ROOT, "comm_matmul_tensor_amd", "libmc2.so")
+
+# fake, 16-byte aligned addresses: only ever passed to calls that fail validation
+A = ctypes.c_void_p(0x10000)
+B = ctypes.c_void_p(0x20000)
+C = ctypes.c_void_p(0x30000)
+
+
+def _declared():
+    src = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:mc2_status|const char\*)\s+(mc2_\w+)\s*\(", src, re.M)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(LIB):
+        pytest.fail("libmc2.so is not built (run __graft_entry__.build())")
+    return ctypes.CDLL(LIB)
+
+
+def test_exports_every_declared_symbol(lib):
+    names = _declared()
+    assert len(names) == 8, names
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings(lib):
+    lib.mc2_status_string.restype = ctypes.c_char_p
+    for s in range(9):
+        assert lib.mc2_status_string(s).decode().startswith("MC2_")
+
+
+def test_quant_mode_enum_matches_pages():
+    gold = json.load(open(os.path.join(ROOT, "tests", "golden", "quant_modes.json")))
+    src = open(HEADER).read()
+    for name, val in gold["modes"].items():
+        m = re.search(rf"MC2_QUANT_{name.upper()}\s*=\s*(\d+)", src)
+        assert m and int(m.group(1)) == val, name
+
+
+def _ptrs(*ps):
+    return (ctypes.c_void_p * len(ps))(*[p.value if isinstance(p, ctypes.c_void_p) else p for p in ps])
+
+
+def _err(lib):
+    lib.mc2_last_error.restype = ctypes.c_char_p
+    return lib.mc2_last_error().decode()
+
+
+def test_allgather_matmul_validation(lib):
+    f = lib.mc2_allgather_matmul
+    f.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int64,
+                  ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_int,
+                  ctypes.c_void_p]
+    sh = _ptrs(A, A, A, A, A, A, A, A)
+    BF16, F32 = 2, 0
+    assert f(sh, 3, 16, 512, B, 64, 0, BF16, C, None, 0, 0, None) == 2            # world_size 3
+    assert "world_size" in _err(lib)
+    assert f(sh, 8, 16, 255, B, 64, 0, BF16, C, None, 0, 0, None) == 2            # k below 256
+    assert f(sh, 8, 16, 65535, B, 64, 0, BF16, C, None, 0, 0, None) == 2          # k at 65535
+    assert f(sh, 8, 0, 512, B, 64, 0, BF16, C, None, 0, 0, None) == 2             # empty
+    assert f(sh, 8, 16, 512, B, 64, 0, F32, C, None, 0, 0, None) == 3             # fp32 input
+    assert f(sh, 8, 16, 512, None, 64, 0, BF16, C, None, 0, 0, None) == 1         # x2 NULL
+    assert f(_ptrs(A, None), 2, 16, 512, B, 64, 0, BF16, C, None, 0, 0, None) == 1
+    assert f(sh, 8, 16, 512, B, 64, 0, BF16, C, None, 1, 0, None) == 1            # arrival w/o gather_out
+    assert f(sh, 8, 16, 512, B, 64, 0, BF16, C, A, 1, 9, None) == 2               # bad rank_id
+    assert f(sh, 8, 16, 512, B, 64, 0, BF16, C, None, 7, 0, None) == 4            # unknown mode
+    assert f(sh, 8, 16, 512, ctypes.c_void_p(0x20008), 64, 0, BF16, C, None, 0, 0, None) == 8  # misaligned
+
+
+def test_backward_validation(lib):
+    gi, gw = lib.mc2_matmul_grad_input, lib.mc2_matmul_grad_weight
+    for f in (gi, gw):
+        f.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+                      ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    assert gi(A, B, 8192, 255, 4096, 2, C, None) == 2     # contraction n_local below 256
+    assert gi(A, B, 8192, 65535, 4096, 2, C, None) == 2
+    assert gi(A, B, 8192, 1792, 4096, 3, C, None) == 3    # int8 dtype
+    assert gi(A, None, 8192, 1792, 4096, 2, C, None) == 1
+    assert gw(A, B, 0, 1792, 4096, 2, C, None) == 2
+    assert gw(A, B, 8192, 1792, 4096, 0, C, None) == 3
+
+
+def test_alltoall_validation(lib):
+    ws = lib.mc2_alltoall_quant_matmul_workspace_size
+    ws.argtypes = [ctypes.c_int, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.POINTER(ctypes.c_size_t)]
+    n = ctypes.c_size_t(0)
+    assert ws(8, 8192, 4096, 7168, ctypes.byref(n)) == 0 and n.value >= 1024 * 32768
+    assert ws(8, 8190, 4096, 7168, ctypes.byref(n)) == 2   # bs not divisible by rank_size
+    assert ws(8, 8192, 4376, 7168, ctypes.byref(n)) == 2   # rank_size*h above 35000
+    assert ws(4, 8192, 1002, 7168, ctypes.byref(n)) == 2   # rank_size*h not a multiple of 16
+    assert ws(3, 8192, 4096, 7168, ctypes.byref(n)) == 2
+    assert ws(8, 8192, 4096, 0, ctypes.byref(n)) == 2      # empty
+    assert ws(8, 8192, 4096, 2 ** 31, ctypes.byref(n)) == 2  # n above INT32_MAX
+    f = lib.mc2_alltoall_quant_matmul
+    f.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_int64, ctypes.c_int, ctypes.c_void_p,
+                  ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                  ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                  ctypes.c_size_t, ctypes.c_void_p]
+    assert ws(8, 64, 256, 32, ctypes.byref(n)) == 0
+    need = n.value
+    args = [A, 8, 64, 256, 2, B, 32, C, None, None, C, None, None, None, None, A, need, None]
+    bad = list(args); bad[0] = None
+    assert f(*bad) == 1                                    # x1 NULL
+    bad = list(args); bad[16] = need - 1
+    assert f(*bad) == 5                                    # workspace too small
+    bad = list(args); bad[4] = 0
+    assert f(*bad) == 3                                    # fp32 activations
+
+
+def test_quant_all_reduce_validation(lib):
+    f = lib.mc2_quant_all_reduce
+    f.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_int64, ctypes.c_int,
+                  ctypes.c_int, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p]
+    xs, ss = _ptrs(A, A), _ptrs(B, B)
+    I8, E4M3, E5M2, E8M0, F32, BF16, I32 = 3, 5, 6, 7, 0, 2, 4
+    assert f(xs, ss, 2, 8, 1000, I8, F32, C, F32, None) == 2      # h not 128-aligned / below 1024
+    assert f(xs, ss, 2, 8, 8320, I8, F32, C, F32, None) == 2      # h above 8192
+    assert f(xs, ss, 2, 0, 1024, I8, F32, C, F32, None) == 2      # empty
+    assert f(xs, ss, 6, 8, 1024, I8, F32, C, F32, None) == 2      # world size 6
+    assert f(xs, ss, 2, 8, 1024, I8, E8M0, C, F32, None) == 3     # E8M0 needs fp8 x
+    assert f(xs, ss, 2, 8, 1024, E4M3, I32, C, F32, None) == 3    # bad scale dtype
+    assert f(xs, ss, 2, 8, 1024, E5M2, E8M0, C, I32, None) == 3   # bad out dtype
+    assert f(xs, _ptrs(B, None), 2, 8, 1024, I8, F32, C, F32, None) == 1
+
+
+@pytest.mark.skipif(__import__("torch").cuda.is_available(), reason="checks the no-device path")
+def test_valid_call_without_device_reports_no_device(lib):
+    f = lib.mc2_quant_all_reduce
+    f.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_int64, ctypes.c_int,
+                  ctypes.c_int, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p]
+    assert f(_ptrs(A, A), _ptrs(B, B), 2, 8, 1024, 3, 0, C, 0, None) == 6

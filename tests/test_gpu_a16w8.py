@@ -1,0 +1,127 @@
+"""AlltoAllQuantMatmul A16W8 (dynamic per-token) on the GPU vs the oracle.
+
+Bit-exact: the permuted layout, the int8 codes, the per-token fp32 scales
+and the int32 accumulators.  The bf16 / fp16 output: |gpu - ref| <=
+1e-2 |ref| + 1e-2 rms(ref) (fp32 dequant on the GPU vs fp64 in the oracle).
+"""
+import numpy as np
+import pytest
+
+import mc2_inputs
+import oracle
+from parity import assert_bits_equal, assert_close16
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def mc2():
+    import torch
+    assert torch.cuda.is_available()
+    import comm_matmul_tensor_amd as m
+    return m
+
+
+def _run(mc2, r, bs, h, n, dtype="bf16", smooth=True, bias=True, seed=0, debug=True):
+    import torch
+    specs = mc2_inputs.configs.scaled("a16w8", r=r, bs=bs, h=h, n=n)
+    for key in ("x1", "x1_smooth", "bias"):
+        s = specs[key]
+        specs[key] = mc2_inputs.TensorSpec(s.tid, s.shape, s.dist, s.a, s.b, dtype)
+    t = mc2_inputs.make(specs, seed=seed)
+    T = mc2_inputs.to_torch
+    rows, cols = bs // r, r * h
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float16
+    dbg = {}
+    if debug:
+        dbg = dict(permuted_out=torch.empty((rows, cols), dtype=tdt, device="cuda"),
+                   q_out=torch.empty((rows, cols), dtype=torch.int8, device="cuda"),
+                   x1_scale_out=torch.empty((rows,), dtype=torch.float32, device="cuda"),
+                   acc_out=torch.empty((rows, n), dtype=torch.int32, device="cuda"))
+    sm = T(t["x1_smooth"], dtype) if smooth else None
+    b = T(t["bias"], dtype) if bias else None
+    out = mc2.mc2_alltoall_quant_matmul(T(t["x1"], dtype), r, T(t["x2"], "i8"), T(t["x2_scale"], "f32"), sm, b,
+                                        **dbg)
+    torch.cuda.synchronize()
+    ref = oracle.alltoall_quant_matmul(t["x1"], r, t["x2"], t["x2_scale"], t["x1_smooth"] if smooth else None,
+                                       t["bias"] if bias else None, dtype)
+    got = {"out": mc2_inputs.from_torch(out)}
+    got.update({k.replace("_out", "").replace("x1_scale", "s1"): mc2_inputs.from_torch(v) for k, v in dbg.items()})
+    return got, ref
+
+
+@pytest.mark.parametrize("r,bs,h,n", [
+    (2, 2, 256, 16), (4, 64, 256, 96), (8, 256, 512, 300), (8, 64, 2, 40), (2, 6, 136, 33),
+    (4, 520, 1024, 129), (8, 16, 4096, 64)])
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_a16w8_shapes(mc2, r, bs, h, n, dtype):
+    print(f"a16w8 r={r} bs={bs} h={h} n={n} {dtype}", flush=True)
+    got, ref = _run(mc2, r, bs, h, n, dtype, seed=r + bs + h + n)
+    assert_bits_equal(got["permuted"], ref["permuted"], "permuted")
+    assert_bits_equal(got["s1"], ref["s1"], "x1_scale")
+    assert_bits_equal(got["q"], ref["q"], "q")
+    assert_bits_equal(got["acc"], ref["acc"], "acc")
+    assert_close16(got["out"], ref["out"], dtype, "out")
+
+
+@pytest.mark.parametrize("smooth,bias", [(False, True), (True, False), (False, False)])
+def test_a16w8_optional_inputs(mc2, smooth, bias):
+    got, ref = _run(mc2, 4, 128, 512, 160, smooth=smooth, bias=bias, seed=3)
+    assert_bits_equal(got["q"], ref["q"], "q")
+    assert_bits_equal(got["s1"], ref["s1"], "x1_scale")
+    assert_close16(got["out"], ref["out"], "bf16", "out")
+
+
+def test_a16w8_zero_rows_and_ties(mc2):
+    """All-zero tokens quantise to 0 with scale 0; rows built so y / s hits .5 exactly round to even."""
+    import torch
+    r, h, n = 2, 64, 32
+    rows = np.zeros((4, r * h))
+    rows[1, :] = np.tile([127, -2.5, 3.5, 0.5, -0.5, 1.5, 126.5, -126.5], r * h // 8)
+    rows[2, ::3] = 1.0
+    x1_p = oracle.encode("bf16", rows)                         # the permuted layout (4, 128)
+    x1 = x1_p.reshape(4, r, h).transpose(1, 0, 2).reshape(4 * r, h).copy()  # inverse permute
+    x2 = np.random.default_rng(0).integers(-127, 128, (r * h, n)).astype(np.int8)
+    s2 = np.full(n, 0.01, np.float32)
+    T = mc2_inputs.to_torch
+    q = torch.empty((4, r * h), dtype=torch.int8, device="cuda")
+    s1 = torch.empty((4,), dtype=torch.float32, device="cuda")
+    out = mc2.mc2_alltoall_quant_matmul(T(x1, "bf16"), r, T(x2, "i8"), T(s2, "f32"), q_out=q, x1_scale_out=s1)
+    torch.cuda.synchronize()
+    ref = oracle.alltoall_quant_matmul(x1, r, x2, s2)
+    assert_bits_equal(mc2_inputs.from_torch(q), ref["q"], "q")
+    assert_bits_equal(mc2_inputs.from_torch(s1), ref["s1"], "s1")
+    assert float(ref["s1"][0]) == 0.0 and not ref["q"][0].any()
+    assert ref["q"][1, :8].tolist() == [127, -2, 4, 0, 0, 2, 126, -126]
+    assert_close16(mc2_inputs.from_torch(out), ref["out"], "bf16", "out")
+
+
+def test_a16w8_full_config(mc2):
+    """bf16 (8192, 4096) on 8 ranks -> (1024, 32768) @ int8 (32768, 7168): every permuted
+    value, code and scale; accumulators and outputs on sampled tokens."""
+    import torch
+    seed, d, specs = mc2_inputs.CONFIGS["a16w8"]
+    t = mc2_inputs.make("a16w8")
+    r, bs, h, n = d["r"], d["bs"], d["h"], d["n"]
+    rows, cols = bs // r, r * h
+    T = mc2_inputs.to_torch
+    q = torch.empty((rows, cols), dtype=torch.int8, device="cuda")
+    s1 = torch.empty((rows,), dtype=torch.float32, device="cuda")
+    acc = torch.empty((rows, n), dtype=torch.int32, device="cuda")
+    out = mc2.mc2_alltoall_quant_matmul(T(t["x1"], "bf16"), r, T(t["x2"], "i8"), T(t["x2_scale"], "f32"),
+                                        T(t["x1_smooth"], "bf16"), T(t["bias"], "bf16"),
+                                        q_out=q, x1_scale_out=s1, acc_out=acc)
+    out2 = mc2.mc2_alltoall_quant_matmul(T(t["x1"], "bf16"), r, T(t["x2"], "i8"), T(t["x2_scale"], "f32"),
+                                         T(t["x1_smooth"], "bf16"), T(t["bias"], "bf16"))
+    torch.cuda.synchronize()
+    p = oracle.permute(t["x1"], r)
+    q_ref, s1_ref = oracle.smooth_quant(p, t["x1_smooth"])
+    assert_bits_equal(mc2_inputs.from_torch(q), q_ref, "q")
+    assert_bits_equal(mc2_inputs.from_torch(s1), s1_ref, "s1")
+    o = mc2_inputs.from_torch(out)
+    assert_bits_equal(o, mc2_inputs.from_torch(out2), "run-to-run")
+    toks = np.unique(np.concatenate([[0, rows - 1], np.random.default_rng(2).choice(rows, 6, replace=False)]))
+    acc_ref = oracle.int8_matmul(np.ascontiguousarray(q_ref[toks]), t["x2"])
+    assert_bits_equal(mc2_inputs.from_torch(acc)[toks], acc_ref, "acc")
+    out_ref = oracle.dequant(acc_ref, s1_ref[toks], t["x2_scale"], t["bias"])
+    assert_close16(o[toks], out_ref, "bf16", "out")

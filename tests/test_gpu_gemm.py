@@ -1,0 +1,141 @@
+"""AllGatherMatmul and the column-parallel backward GEMMs on the GPU vs the oracle.
+
+Float outputs: |gpu - ref| <= 1e-2 |ref| + 1e-2 rms(ref) per element (fp32
+accumulation on the GPU vs fp64 in the oracle, both rounded to 16 bits).
+gather_out and the exact-integer cases: bit for bit.
+"""
+import numpy as np
+import pytest
+
+import mc2_inputs
+import oracle
+from parity import assert_bits_equal, assert_close16
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def mc2():
+    import torch
+    assert torch.cuda.is_available()
+    import comm_matmul_tensor_amd as m
+    return m
+
+
+def _ag(mc2, r, m_l, k, n, dtype, x2_trans=False, seed=0, gather=True, x2_std=1.0):
+    import torch
+    specs = mc2_inputs.configs.scaled("ag", r=r, m_local=m_l, k=k, n=n, dtype=dtype, x2_std=x2_std)
+    t = mc2_inputs.make(specs, seed=seed)
+    shards = [t[f"shard{i}"] for i in range(r)]
+    x2 = np.ascontiguousarray(t["x2"].T) if x2_trans else t["x2"]
+    T = mc2_inputs.to_torch
+    out, g = mc2.mc2_allgather_matmul([T(s, dtype) for s in shards], T(x2, dtype), x2_trans=x2_trans,
+                                      gather_output=gather)
+    torch.cuda.synchronize()
+    want, want_g = oracle.allgather_matmul(shards, x2, dtype, x2_trans=x2_trans, gather_output=gather)
+    return mc2_inputs.from_torch(out), (mc2_inputs.from_torch(g) if g is not None else None), want, want_g
+
+
+def test_ag_tiny_example(mc2):
+    """The API page's example: 8 ranks, gathered (128, 512) fp16 @ (512, 64)."""
+    seed, d, specs = mc2_inputs.CONFIGS["ag_tiny"]
+    out, g, want, want_g = _ag(mc2, d["r"], d["m_local"], d["k"], d["n"], "f16", seed=seed)
+    assert_bits_equal(g, want_g, "gather_out")
+    assert_close16(out, want, "f16", "out")
+
+
+@pytest.mark.parametrize("r,m_l,k,n", [
+    (2, 1, 256, 1), (2, 3, 300, 7), (4, 16, 512, 64), (8, 5, 1000, 130), (4, 100, 264, 200),
+    (8, 33, 768, 257), (2, 129, 256, 129)])
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("x2_trans", [False, True])
+def test_ag_shapes(mc2, r, m_l, k, n, dtype, x2_trans):
+    print(f"ag r={r} m_l={m_l} k={k} n={n} {dtype} trans={x2_trans}", flush=True)
+    out, g, want, want_g = _ag(mc2, r, m_l, k, n, dtype, x2_trans, seed=r * 1000 + k + n)
+    assert_bits_equal(g, want_g, "gather_out")
+    assert_close16(out, want, dtype, "out")
+
+
+def test_ag_without_gather_output(mc2):
+    out, g, want, _ = _ag(mc2, 4, 8, 256, 48, "bf16", gather=False, seed=5)
+    assert g is None
+    assert_close16(out, want, "bf16")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_ag_exact_integer_bit_exact(mc2, dtype):
+    """Small integers: fp32 accumulation is exact, so the GPU must equal the oracle bit for bit."""
+    import torch
+    rng = np.random.default_rng(11)
+    r, m_l, k, n = 4, 40, 512, 96
+    enc = lambda a: oracle.encode(dtype, a.astype(np.float64))
+    shards = [enc(rng.integers(-3, 4, (m_l, k))) for _ in range(r)]
+    x2 = enc(rng.integers(-2, 3, (k, n)))
+    T = mc2_inputs.to_torch
+    out, _ = mc2.mc2_allgather_matmul([T(s, dtype) for s in shards], T(x2, dtype))
+    want, _ = oracle.allgather_matmul(shards, x2, dtype)
+    assert_bits_equal(mc2_inputs.from_torch(out), want, "exact-integer out")
+
+
+def test_ag_max_k(mc2):
+    """k = 65534, the largest the op accepts."""
+    out, g, want, want_g = _ag(mc2, 2, 2, 65534, 16, "bf16", seed=7, x2_std=0.05)
+    assert_bits_equal(g, want_g, "gather_out")
+    assert_close16(out, want, "bf16")
+
+
+def test_ag_full_config_sampled(mc2):
+    """8 x bf16 (512, 4096) @ (4096, 1792): gather_out in full, 64 sampled output rows,
+    and bit-identical results on a second run."""
+    import torch
+    seed, d, specs = mc2_inputs.CONFIGS["ag_bf16_tp"]
+    t = mc2_inputs.make("ag_bf16_tp")
+    T = mc2_inputs.to_torch
+    shards = [T(t[f"shard{i}"], "bf16") for i in range(d["r"])]
+    x2 = T(t["x2"], "bf16")
+    out, g = mc2.mc2_allgather_matmul(shards, x2)
+    out2, _ = mc2.mc2_allgather_matmul(shards, x2)
+    torch.cuda.synchronize()
+    G = np.concatenate([t[f"shard{i}"] for i in range(d["r"])])
+    assert_bits_equal(mc2_inputs.from_torch(g), G, "gather_out")
+    o = mc2_inputs.from_torch(out)
+    assert_bits_equal(o, mc2_inputs.from_torch(out2), "run-to-run")
+    rows = np.sort(np.random.default_rng(0).choice(G.shape[0], 64, replace=False))
+    rows[:2] = [0, G.shape[0] - 1]
+    rows = np.unique(rows)
+    want = oracle.matmul(np.ascontiguousarray(G[rows]), t["x2"], "bf16")
+    assert_close16(o[rows], want, "bf16", "sampled rows")
+
+
+@pytest.mark.parametrize("m,n_l,k", [(64, 256, 32), (200, 300, 130), (1024, 256, 520), (33, 1000, 7)])
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_backward_shapes(mc2, m, n_l, k, dtype):
+    import torch
+    print(f"bwd m={m} n_l={n_l} k={k} {dtype}", flush=True)
+    specs = mc2_inputs.configs.scaled("bwd", m=m, n_local=n_l, k=k)
+    for s in specs:
+        specs[s] = mc2_inputs.TensorSpec(specs[s].tid, specs[s].shape, specs[s].dist, specs[s].a, specs[s].b, dtype)
+    t = mc2_inputs.make(specs, seed=m + n_l + k)
+    T = mc2_inputs.to_torch
+    dx = mc2.mc2_matmul_grad_input(T(t["dy"], dtype), T(t["w"], dtype))
+    dw = mc2.mc2_matmul_grad_weight(T(t["dy"], dtype), T(t["ag_x"], dtype))
+    torch.cuda.synchronize()
+    assert_close16(mc2_inputs.from_torch(dx), oracle.matmul_grad_input(t["dy"], t["w"], dtype), dtype, "dX")
+    assert_close16(mc2_inputs.from_torch(dw), oracle.matmul_grad_weight(t["dy"], t["ag_x"], dtype), dtype, "dW")
+
+
+def test_backward_full_config_sampled(mc2):
+    """dY (8192, 1792), W (1792, 4096), AG(X) (8192, 4096): 32 sampled rows of dX and of dW."""
+    import torch
+    t = mc2_inputs.make("colpar_bwd")
+    T = mc2_inputs.to_torch
+    dy, w, x = T(t["dy"], "bf16"), T(t["w"], "bf16"), T(t["ag_x"], "bf16")
+    dx = mc2_inputs.from_torch(mc2.mc2_matmul_grad_input(dy, w))
+    dw = mc2_inputs.from_torch(mc2.mc2_matmul_grad_weight(dy, x))
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(1)
+    rx = np.unique(np.concatenate([[0, 8191], rng.choice(8192, 30, replace=False)]))
+    assert_close16(dx[rx], oracle.matmul(np.ascontiguousarray(t["dy"][rx]), t["w"], "bf16"), "bf16", "dX rows")
+    rw = np.unique(np.concatenate([[0, 1791], rng.choice(1792, 30, replace=False)]))
+    want = oracle.matmul(np.ascontiguousarray(t["dy"][:, rw]), t["ag_x"], "bf16", a_trans=True)
+    assert_close16(dw[rw], want, "bf16", "dW rows")
