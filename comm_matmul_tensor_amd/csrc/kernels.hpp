@@ -36,6 +36,7 @@ struct GemmArgs {
   void* gather_out;  // optional copy of the gathered A (only with a_kmajor)
   int64_t m, n, k;
   int dtype;  // DT_F16 or DT_BF16
+  int tile_order_cols;  // set by the launcher: XCD tile order walks columns of tiles
   // arrival emulation: per-part ready flags (NULL when unused)
   const unsigned* ready_flags;
   unsigned ready_value;

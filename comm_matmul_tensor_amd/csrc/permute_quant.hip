@@ -12,8 +12,10 @@
 //           absmax over the row (wavefront then workgroup reduction; max is
 //           exact in any order)
 //   s       = absmax / 127 (IEEE division)
-//   pass 2  q = clamp(rint(y / s), -127, 127) with IEEE division and
-//           round-half-to-even; an all-zero row gives s = 0 and q = 0.
+//   pass 2  q = clamp(rint(y / s), -127, 127) with the result of the IEEE
+//           division and round-half-to-even (computed as y * (1/s) with an
+//           exact fallback near ties, see quant_fast); an all-zero row gives
+//           s = 0 and q = 0.
 // HBM traffic: 2 B read + 1 B written per element, plus the 4-byte scale.
 #include "device.hpp"
 #include "kernels.hpp"
@@ -21,8 +23,8 @@
 namespace mc2 {
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int kMaxUnits = 9;  // 16-element units per thread: r*h <= 36864
+constexpr int kThreads = 512;
+constexpr int kMaxUnits = 5;  // 16-element units per thread: r*h <= 40960
 
 template <int DT>
 __device__ __forceinline__ float dec16(uint32_t bits) {
@@ -48,6 +50,20 @@ __device__ __forceinline__ int quant1(float y, float s) {
   return (int)r;
 }
 
+// q = clamp(rint(y / s)) with the same result as the IEEE division, computed
+// as y * (1 / s).  With inv = RN(1 / s), RN(y * inv) is within
+// |y / s| (2^-23 + 2^-48) <= 1.6e-5 of y / s (|y / s| <= 127), and RN(y / s)
+// within 3.9e-6, so both round to the same integer unless y * inv lies within
+// 2e-5 of a half-integer; those rare elements take the exact division.
+__device__ __forceinline__ int quant_fast(float y, float s, float inv) {
+  const float qa = y * inv;
+  const float fl = __builtin_floorf(qa);
+  if (__builtin_fabsf(qa - fl - 0.5f) <= 3.0e-5f) return quant1(y, s);
+  float r = __builtin_rintf(qa);
+  r = fminf(fmaxf(r, -127.0f), 127.0f);
+  return (int)r;
+}
+
 // Vector path: h % 16 == 0, so every 16-element unit of P lies inside one
 // source row and is 32-byte aligned.
 template <int DT>
@@ -60,23 +76,36 @@ __global__ __launch_bounds__(kThreads) void permute_quant_vec(QuantArgs a) {
   const uint16_t* x1 = static_cast<const uint16_t*>(a.x1);
   const uint16_t* sm = static_cast<const uint16_t*>(a.smooth);
 
-  u32x4 raw[kMaxUnits][2];
-  u32x4 smr[kMaxUnits][2];
+  // issue every load of the token before using any of them
+  u32x4 raw[kMaxUnits][2], smr[kMaxUnits][2];
+#pragma unroll
+  for (int v = 0; v < kMaxUnits; v++) {
+    const int u = threadIdx.x + v * kThreads;
+    const int e = (u < units ? u : 0) * 16;  // column in P (r * h <= 40960)
+    const int hh = (int)a.h;
+    const int j = e / hh, c = e - j * hh;      // source rank block and column
+    const u32x4* src = reinterpret_cast<const u32x4*>(x1 + (((int64_t)j * T + t) * a.h + c));
+    if (u < units) {
+      raw[v][0] = src[0];
+      raw[v][1] = src[1];
+    }
+  }
+  if (sm) {
+#pragma unroll
+    for (int v = 0; v < kMaxUnits; v++) {
+      const int u = threadIdx.x + v * kThreads;
+      if (u < units) {
+        const u32x4* sp = reinterpret_cast<const u32x4*>(sm + (int64_t)u * 16);
+        smr[v][0] = sp[0];
+        smr[v][1] = sp[1];
+      }
+    }
+  }
   float amax = 0.0f;
 #pragma unroll
   for (int v = 0; v < kMaxUnits; v++) {
     const int u = threadIdx.x + v * kThreads;
     if (u < units) {
-      const int64_t e = (int64_t)u * 16;          // column in P
-      const int64_t j = e / a.h, c = e - j * a.h;  // source rank block and column
-      const u32x4* src = reinterpret_cast<const u32x4*>(x1 + ((j * T + t) * a.h + c));
-      raw[v][0] = src[0];
-      raw[v][1] = src[1];
-      if (sm) {
-        const u32x4* s = reinterpret_cast<const u32x4*>(sm + e);
-        smr[v][0] = s[0];
-        smr[v][1] = s[1];
-      }
 #pragma unroll
       for (int hlf = 0; hlf < 2; hlf++)
 #pragma unroll
@@ -92,6 +121,10 @@ __global__ __launch_bounds__(kThreads) void permute_quant_vec(QuantArgs a) {
   amax = block_max(amax, red);
   const float s = amax / 127.0f;
   if (threadIdx.x == 0) a.s1[t] = s;
+  // The error bound of quant_fast needs |y / s| <= 127 (1 + 2^-23), which holds
+  // when s is a normal number; rows with a subnormal scale use the division.
+  const float inv = 1.0f / s;
+  const bool fast = s >= 1.17549435e-38f;  // uniform over the workgroup
 
 #pragma unroll
   for (int v = 0; v < kMaxUnits; v++) {
@@ -110,7 +143,7 @@ __global__ __launch_bounds__(kThreads) void permute_quant_vec(QuantArgs a) {
             for (int b = 0; b < 2; b++) {
               float y = dec16<DT>(raw[v][hlf][w + ww] >> (16 * b));
               if (sm) y *= dec16<DT>(smr[v][hlf][w + ww] >> (16 * b));
-              const int q = amax > 0.0f ? quant1(y, s) : 0;
+              const int q = amax > 0.0f ? (fast ? quant_fast(y, s, inv) : quant1(y, s)) : 0;
               packed |= ((uint32_t)q & 0xFFu) << (8 * (2 * ww + b));
             }
           qv[2 * hlf + w / 2] = packed;
