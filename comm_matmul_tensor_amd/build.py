@@ -27,7 +27,12 @@ COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-result", f"-I{os.p
 
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [HIPCC] + COMMON + DEVICE_FLAGS + ["-c", src, "-o", obj]
+    extra = []
+    if os.path.basename(src).startswith("gemm_"):
+        # MFMA accumulators in VGPRs: the AGPR form made the register allocator
+        # rotate accumulators through copies inside the main loop.
+        extra = ["-mllvm", "-amdgpu-mfma-vgpr-form"]
+    cmd = [HIPCC] + COMMON + DEVICE_FLAGS + extra + ["-c", src, "-o", obj]
     if src.endswith(".cpp"):
         cmd = [HIPCC, "-x", "hip"] + COMMON + DEVICE_FLAGS + ["-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)

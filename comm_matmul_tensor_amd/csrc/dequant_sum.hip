@@ -49,7 +49,8 @@ __global__ __launch_bounds__(256) void dequant_sum_kernel(QarArgs a) {
 
   u32x4 xv[R];
 #pragma unroll
-  for (int i = 0; i < R; i++) xv[i] = *reinterpret_cast<const u32x4*>(static_cast<const uint8_t*>(a.x[i]) + e0);
+  for (int i = 0; i < R; i++)  // streamed once: non-temporal loads (measured faster; non-temporal stores were slower)
+    xv[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(static_cast<const uint8_t*>(a.x[i]) + e0));
 
   double sc[R];
 #pragma unroll

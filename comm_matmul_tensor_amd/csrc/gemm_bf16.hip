@@ -9,8 +9,9 @@
 // in gemm_mfma.hpp.  Specific to this kernel:
 //  - AllGather: A's row blocks are the rank shards, resolved per thread once
 //    before the K loop, so the "communication" is the addressing of the
-//    loads.  The workgroups of column tile 0 also store the A chunks they load
-//    into gather_out: the gathered copy costs one write and no extra read.
+//    loads.  The gathered copy (gather_out) is written from the A tiles
+//    already in LDS, each K step by one workgroup of the row of tiles (the
+//    work spreads evenly): one write per element and no extra global read.
 //  - Epilogue: fp32 -> bf16 / fp16 with round-to-nearest-even, staged through
 //    LDS and stored as 16-byte row chunks.
 #include "gemm_mfma.hpp"
@@ -37,11 +38,13 @@ struct Ops16 {
 template <int BM, int BN, bool AK, bool BKM, bool VEC, int DT>
 __global__ __launch_bounds__(kThreads, 1) void gemm16_kernel(Problem p, void* c) {
   constexpr int FM = BM / 32, FN = BN / 32;
-  __shared__ __attribute__((aligned(16))) uint8_t lds_raw[lds_bytes<2, BM, BN, AK, BKM>()];
-  uint16_t* lds = reinterpret_cast<uint16_t*>(lds_raw);
+  __shared__ __attribute__((aligned(1024))) uint8_t s0[lds_stage_array_bytes<BM, BN>()];
+  __shared__ __attribute__((aligned(1024))) uint8_t s1[lds_stage_array_bytes<BM, BN>()];
+  __shared__ __attribute__((aligned(1024))) uint8_t s2[lds_stage_array_bytes<BM, BN>()];
   int tm, tn;
   tile_of_block(p.m, p.n, BM, BN, p.tile_order_cols, tm, tn);
   const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
+  const int tiles_n = (int)((p.n + BN - 1) / BN);
 
   typename Ops16<DT>::Acc acc[FM][FN];
 #pragma unroll
@@ -49,10 +52,10 @@ __global__ __launch_bounds__(kThreads, 1) void gemm16_kernel(Problem p, void* c)
 #pragma unroll
     for (int j = 0; j < FN; j++) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  mainloop<2, BM, BN, AK, BKM, VEC, Ops16<DT>>(p, m0, n0, AK && tn == 0 && p.gather_out != nullptr, lds, acc);
+  run_mainloop<2, BM, BN, AK, BKM, VEC, Ops16<DT>>(p, m0, n0, tn, tiles_n, s0, s1, s2, acc);
 
-  store_c16<BM, BN, VEC>(lds, static_cast<uint16_t*>(c), p.m, p.n, m0, n0,
-                         [&](int i, int j, int r, int, int) { return Ops16<DT>::cvt(acc[i][j][r]); });
+  store_c16<BM, BN, VEC>(reinterpret_cast<uint16_t*>(s0), reinterpret_cast<uint16_t*>(s1), static_cast<uint16_t*>(c),
+                         p.m, p.n, m0, n0, [&](int i, int j, int r, int, int) { return Ops16<DT>::cvt(acc[i][j][r]); });
 }
 
 template <int BM, int BN, bool AK, bool BKM, int DT>

@@ -5,9 +5,10 @@
 //
 //   out[i][j] = round16( (float(acc[i][j]) * s1[i]) * s2[j] + bias[j] )
 //
-// A = q (m, k) int8 row-major (K-contiguous), B = x2 (k, n) int8 row-major
-// (N-contiguous, read through ds_read_b64_tr_b8).  Tiling, LDS layout and XCD
-// order are described in gemm_mfma.hpp.  Integer accumulation is exact, so
+// A = q (m, k) int8 row-major (K-contiguous, staged by direct-to-LDS loads),
+// B = x2 (k, n) int8 row-major (N-contiguous, transposed in registers to the
+// K-major LDS layout).  Tiling, LDS layout and XCD order are described in
+// gemm_mfma.hpp.  Integer accumulation is exact, so
 // the result does not depend on the order of the K loop; |acc| stays below
 // 2^31 because rank_size * h <= 35000 and |q|, |x2| <= 128.
 #include "gemm_mfma.hpp"
@@ -28,10 +29,13 @@ template <int BM, int BN, bool VEC, int DT>
 __global__ __launch_bounds__(kThreads, 1) void gemm_i8_kernel(Problem p, GemmI8Args g) {
   constexpr int FM = BM / 32, FN = BN / 32;
   constexpr int WM = BM / 2, WN = BN / 2;
-  __shared__ __attribute__((aligned(16))) uint8_t lds[lds_bytes<1, BM, BN, true, false>()];
+  __shared__ __attribute__((aligned(1024))) uint8_t s0[lds_stage_array_bytes<BM, BN>()];
+  __shared__ __attribute__((aligned(1024))) uint8_t s1[lds_stage_array_bytes<BM, BN>()];
+  __shared__ __attribute__((aligned(1024))) uint8_t s2[lds_stage_array_bytes<BM, BN>()];
   int tm, tn;
   tile_of_block(p.m, p.n, BM, BN, p.tile_order_cols, tm, tn);
   const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
+  const int tiles_n = (int)((p.n + BN - 1) / BN);
 
   i32x4 acc[FM][FN];
 #pragma unroll
@@ -39,7 +43,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_i8_kernel(Problem p, GemmI8A
 #pragma unroll
     for (int j = 0; j < FN; j++) acc[i][j] = i32x4{0, 0, 0, 0};
 
-  mainloop<1, BM, BN, true, false, VEC, OpsI8>(p, m0, n0, false, lds, acc);
+  run_mainloop<1, BM, BN, true, false, VEC, OpsI8>(p, m0, n0, tn, tiles_n, s0, s1, s2, acc);
 
   const int wave = threadIdx.x / 64, lane = threadIdx.x % 64;
   const int wm = wave / 2, wn = wave % 2;
@@ -57,7 +61,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_i8_kernel(Problem p, GemmI8A
       }
   }
   const uint16_t* bias = static_cast<const uint16_t*>(g.bias);
-  store_c16<BM, BN, VEC>(reinterpret_cast<uint16_t*>(lds), static_cast<uint16_t*>(g.out), p.m, p.n, m0, n0,
+  store_c16<BM, BN, VEC>(reinterpret_cast<uint16_t*>(s0), reinterpret_cast<uint16_t*>(s1), static_cast<uint16_t*>(g.out),
+                         p.m, p.n, m0, n0,
                          [&](int i, int j, int r, int row, int col) -> uint16_t {
                            const int64_t gr = m0 + row, gc = n0 + col;
                            if (gr >= p.m || gc >= p.n) return 0;

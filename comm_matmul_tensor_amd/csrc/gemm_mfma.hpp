@@ -5,25 +5,37 @@
 // held in separate buffers) or M-contiguous (stored (k, m)); B is either
 // K-contiguous (stored (n, k)) or N-contiguous ((k, n) row-major).
 //
-// Geometry is the same for both element sizes when counted in bytes: a
-// K step of the main loop covers 128 bytes of K, an MFMA consumes 64 bytes of
-// K per lane group (v_mfma_f32_16x16x32_{bf16,f16}: 32 elements;
-// v_mfma_i32_16x16x64_i8: 64 elements), every global load and LDS write is a
-// 16-byte chunk, and every MFMA operand fragment is 16 bytes per lane.
+// Geometry, counted in bytes, is the same for both element sizes: a step of
+// the main loop covers 128 bytes of K, an MFMA consumes 64 bytes of K
+// (v_mfma_f32_16x16x32_{bf16,f16}: 32 elements; v_mfma_i32_16x16x64_i8: 64),
+// and every LDS transfer and MFMA operand fragment is a 16-byte chunk.
 //
 // Workgroup: 256 threads = 4 wavefronts in a 2 x 2 grid; each wavefront owns a
-// (BM/2) x (BN/2) block of C as 16 x 16 MFMA tiles.  Operand tiles go global ->
-// registers -> LDS, double buffered: the global loads of step k+1 are issued
-// before the MFMAs of step k and written to the other LDS buffer after them,
-// with one barrier per step.  In LDS a K-contiguous operand is stored [mn][k]
-// and its fragments are read with ds_read_b128; an MN-contiguous operand is
-// stored [k][mn] exactly as loaded and its fragments come from the gfx950
-// transpose reads (within each 16-lane group):
-//   ds_read_b64_tr_b16: lane t reads 4 elements of row k0 + t/4 at column
-//                       n0 + 4 (t % 4) and receives column n0 + t of rows k0..k0+3
-//   ds_read_b64_tr_b8:  lane t reads 8 bytes of row k0 + t/2 at column
-//                       n0 + 8 (t % 2) and receives column n0 + t of rows k0..k0+7
-// LDS rows are padded (see kPadBytesK / kPadBytesMN) against bank conflicts.
+// (BM/2) x (BN/2) block of C as 16 x 16 MFMA tiles.
+//
+// LDS layout.  Both operand tiles are stored K-major: one 128-byte row per
+// m (or n) index, rows packed densely, and the eight 16-byte chunks of row r
+// permuted by XOR with r % 8.  Every MFMA fragment is then one ds_read_b128
+// per lane (16 lanes read 16 rows at the same logical chunk), which on
+// gfx950 measured faster than any padded layout and about twice as fast per
+// byte as the ds_read_b64_tr transpose reads.
+//
+// Staging, for tiles wholly inside the matrices:
+//  - K-contiguous operand: direct-to-LDS loads (global_load_lds_dwordx4).
+//    Each wavefront instruction fills one 1 KB block = 8 rows; lane l lands
+//    in physical chunk l % 8 of row l / 8 of the block, so it fetches logical
+//    chunk (l % 8) ^ (l / 8) from global memory.  No registers, no ds_write.
+//  - MN-contiguous operand: each thread loads a square block (8 k x 8 n for
+//    2-byte elements, 16 x 16 for int8) as 16-byte rows along n, transposes it
+//    in registers with v_perm_b32, and writes 8 or 16 K-major chunks with
+//    ds_write_b128.  Odd blocks write their rows in the order i ^ 1 (a
+//    per-lane byte selector makes that free), so each write instruction
+//    touches both halves of the 64 banks.
+// Two LDS stages (separate arrays, so the compiler can tell the DMA target
+// from the buffer being read) and two register sets: the DMA for step k+1 and
+// the global loads for step k+2 are in flight while the MFMAs of step k run;
+// one barrier per step.  Tiles that cross a matrix edge use a checked path:
+// bounds-tested register loads (zero fill) into the same layout.
 //
 // Tile order: workgroup b is dispatched to XCD b % 8.  Tiles are renumbered so
 // each XCD owns a contiguous 1/8 of them, walking along rows of tiles (the
@@ -39,41 +51,13 @@ namespace mc2 {
 namespace gemm {
 
 constexpr int kThreads = 256;
-constexpr int kBKBytes = 128;   // K bytes per main-loop step
-// LDS row padding: 32 bytes for [mn][k] tiles (a 160-byte pitch makes the
-// 16-lane ds_read_b128 fragment reads conflict-free; 144 does not), 16 bytes
-// for [k][mn] tiles (any pitch that is not a multiple of 256 bytes serves the
-// transpose reads equally).
-constexpr int kPadBytesK = 32;
-constexpr int kPadBytesMN = 16;
+constexpr int kRowBytes = 128;  // K bytes per main-loop step = bytes per LDS tile row
 
-typedef short i16x8 __attribute__((ext_vector_type(8)));
-typedef int i32x2 __attribute__((ext_vector_type(2)));
-typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
-typedef __attribute__((address_space(3))) i32x2 lds_i32x2;
+typedef __attribute__((address_space(1))) const void* gptr_t;
+typedef __attribute__((address_space(3))) void* lptr_t;
 
-// One operand tile: R (mn) x BK (k) elements of E bytes, in 16-byte chunks.
-template <int E, int R, bool KMAJ>
-struct Tile {
-  static constexpr int kCh = 16 / E;                 // elements per chunk
-  static constexpr int kBK = kBKBytes / E;           // K elements per step
-  static constexpr int kPad = (KMAJ ? kPadBytesK : kPadBytesMN) / E;  // padding in elements
-  static constexpr int kPitch = KMAJ ? kBK + kPad : R + kPad;
-  static constexpr int kLds = KMAJ ? R * kPitch : kBK * kPitch;  // elements
-  static constexpr int kChunks = R * kBK / kCh;
-  static constexpr int kPer = kChunks / kThreads;
-  static_assert(kChunks % kThreads == 0, "tile must split evenly into 16-byte chunks");
-  static __device__ __forceinline__ void coords(int c, int& mn, int& k) {
-    if constexpr (KMAJ) {
-      mn = c / (kBK / kCh);
-      k = (c % (kBK / kCh)) * kCh;
-    } else {
-      k = c / (R / kCh);
-      mn = (c % (R / kCh)) * kCh;
-    }
-  }
-  static __device__ __forceinline__ int lds_off(int mn, int k) { return KMAJ ? mn * kPitch + k : k * kPitch + mn; }
-};
+// Byte offset of logical 16-byte chunk c of row r in a swizzled tile.
+__device__ __forceinline__ int swz(int r, int c) { return r * kRowBytes + ((c ^ (r & 7)) << 4); }
 
 template <int E>
 struct Elem;
@@ -81,157 +65,6 @@ template <>
 struct Elem<2> { typedef uint16_t T; };
 template <>
 struct Elem<1> { typedef uint8_t T; };
-
-template <typename T, int N>
-struct VecOf {
-  typedef T type __attribute__((ext_vector_type(N)));
-};
-
-// Per-thread view of one operand: the source of each of its chunks.
-template <int E, int R, bool KMAJ>
-struct Loader {
-  using TS = Tile<E, R, KMAJ>;
-  using T = typename Elem<E>::T;
-  const T* ptr[TS::kPer];  // chunk source at k = 0
-  int64_t ld, k_ext, mn_ext, mn0;
-  T* gout;  // copy of what is loaded (gather_out), K-contiguous A only
-
-  // tile coordinates of chunk i of this thread (recomputed, not stored, to save registers)
-  static __device__ __forceinline__ int kofs(int i) {
-    int mn, k;
-    TS::coords(threadIdx.x + i * kThreads, mn, k);
-    return k;
-  }
-  static __device__ __forceinline__ int mnofs(int i) {
-    int mn, k;
-    TS::coords(threadIdx.x + i * kThreads, mn, k);
-    return mn;
-  }
-  __device__ __forceinline__ bool mn_ok(int i) const { return mn0 + mnofs(i) < mn_ext; }
-
-  __device__ __forceinline__ void init(const void* const* parts, int64_t rows_per_part, int64_t ld_,
-                                       int64_t mn_ext_, int64_t k_ext_, int64_t mn0_, void* gather_out) {
-    ld = ld_;
-    k_ext = k_ext_;
-    mn_ext = mn_ext_;
-    mn0 = mn0_;
-    gout = static_cast<T*>(gather_out);
-#pragma unroll
-    for (int i = 0; i < TS::kPer; i++) {
-      int mn, k;
-      TS::coords(threadIdx.x + i * kThreads, mn, k);
-      const int64_t gmn = mn0 + mn;
-      if constexpr (KMAJ) {
-        // row blocks of rows_per_part rows live in separate buffers
-        int part = 0;
-        int64_t local = gmn < mn_ext ? gmn : 0;
-        while (local >= rows_per_part) {
-          local -= rows_per_part;
-          part++;
-        }
-        ptr[i] = static_cast<const T*>(parts[part]) + local * ld + k;
-      } else {
-        ptr[i] = static_cast<const T*>(parts[0]) + (int64_t)k * ld + gmn;
-      }
-    }
-  }
-
-  // Loads the chunks of the K step starting at k0.  When the whole tile lies
-  // inside the matrix (the common case, decided uniformly per workgroup) the
-  // loads carry no bounds checks, so they issue back to back.
-  template <bool VEC>
-  __device__ __forceinline__ void load(int64_t k0, u32x4 (&regs)[TS::kPer]) const {
-    constexpr int CH = TS::kCh;
-    const bool full = VEC && (mn0 + R <= mn_ext) && (k0 + TS::kBK <= k_ext);
-    if (full) {
-#pragma unroll
-      for (int i = 0; i < TS::kPer; i++)
-        regs[i] = *reinterpret_cast<const u32x4*>(KMAJ ? ptr[i] + k0 : ptr[i] + k0 * ld);
-      return;
-    }
-#pragma unroll
-    for (int i = 0; i < TS::kPer; i++) {
-      const int64_t gk = k0 + kofs(i);
-      u32x4 v = {0u, 0u, 0u, 0u};
-      if constexpr (KMAJ) {
-        const T* p = ptr[i] + k0;
-        if (VEC) {
-          if (mn_ok(i) && gk + CH <= k_ext) v = *reinterpret_cast<const u32x4*>(p);
-        } else if (mn_ok(i)) {
-          T e[CH];
-#pragma unroll
-          for (int j = 0; j < CH; j++) e[j] = (gk + j < k_ext) ? p[j] : (T)0;
-          v = __builtin_bit_cast(u32x4, e);
-        }
-      } else {
-        const T* p = ptr[i] + k0 * ld;
-        if (gk < k_ext) {
-          if (VEC) {
-            if (mn_ok(i)) v = *reinterpret_cast<const u32x4*>(p);
-          } else {
-            const int64_t gmn = mn0 + mnofs(i);
-            T e[CH];
-#pragma unroll
-            for (int j = 0; j < CH; j++) e[j] = (gmn + j < mn_ext) ? p[j] : (T)0;
-            v = __builtin_bit_cast(u32x4, e);
-          }
-        }
-      }
-      regs[i] = v;
-    }
-  }
-
-  // Writes the loaded chunks of K step k0 to gather_out (K-contiguous A).
-  template <bool VEC>
-  __device__ __forceinline__ void store_gather(int64_t k0, const u32x4 (&regs)[TS::kPer]) const {
-    if constexpr (KMAJ) {
-      constexpr int CH = TS::kCh;
-#pragma unroll
-      for (int i = 0; i < TS::kPer; i++) {
-        const int64_t gk = k0 + kofs(i);
-        if (!mn_ok(i)) continue;
-        T* dst = gout + (mn0 + mnofs(i)) * k_ext + gk;
-        if (VEC) {
-          if (gk + CH <= k_ext) *reinterpret_cast<u32x4*>(dst) = regs[i];
-        } else {
-          const auto e = __builtin_bit_cast(typename VecOf<T, CH>::type, regs[i]);
-#pragma unroll
-          for (int j = 0; j < CH; j++)
-            if (gk + j < k_ext) dst[j] = e[j];
-        }
-      }
-    }
-  }
-
-  __device__ __forceinline__ void store(typename Elem<E>::T* lds, const u32x4 (&regs)[TS::kPer]) const {
-#pragma unroll
-    for (int i = 0; i < TS::kPer; i++) *reinterpret_cast<u32x4*>(lds + TS::lds_off(mnofs(i), kofs(i))) = regs[i];
-  }
-};
-
-// 16 (mn) x (64 bytes of k) fragment at tile offsets (mn0, k0): lane l gets the
-// 16 bytes of k starting at k0 + (l / 16) * 16 bytes, for row mn0 + l % 16.
-template <int E, int R, bool KMAJ>
-__device__ __forceinline__ u32x4 read_frag(const typename Elem<E>::T* lds, int mn0, int k0) {
-  using TS = Tile<E, R, KMAJ>;
-  const int l = threadIdx.x % 64;
-  const int t = l % 16, g = l / 16;
-  if constexpr (KMAJ) {
-    return *reinterpret_cast<const u32x4*>(lds + (mn0 + t) * TS::kPitch + k0 + g * TS::kCh);
-  } else if constexpr (E == 2) {
-    const uint16_t* p0 = lds + (k0 + 8 * g + t / 4) * TS::kPitch + mn0 + 4 * (t % 4);
-    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)p0);
-    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p0 + 4 * TS::kPitch));
-    const i16x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-    return __builtin_bit_cast(u32x4, v);
-  } else {
-    const uint8_t* p0 = lds + (k0 + 16 * g + t / 2) * TS::kPitch + mn0 + 8 * (t % 2);
-    const i32x2 lo = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)p0);
-    const i32x2 hi = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)(p0 + 8 * TS::kPitch));
-    const u32x4 v = {(uint32_t)lo[0], (uint32_t)lo[1], (uint32_t)hi[0], (uint32_t)hi[1]};
-    return v;
-  }
-}
 
 // Problem description handed to the shared kernel.
 struct Problem {
@@ -242,6 +75,524 @@ struct Problem {
   int64_t m, n, k;
   int tile_order_cols;
 };
+
+// Row pointer of K-contiguous operand row `row` (row blocks of rows_per_part
+// rows live in separate buffers; resolved once per thread, outside the K loop).
+__device__ __forceinline__ const uint8_t* kmajor_row(const void* const* parts, int64_t rows_per_part,
+                                                     int64_t ld_bytes, int64_t row) {
+  int part = 0;
+  int64_t local = row;
+  while (local >= rows_per_part) {
+    local -= rows_per_part;
+    part++;
+  }
+  return static_cast<const uint8_t*>(parts[part]) + local * ld_bytes;
+}
+
+// ---------------------------------------------------------------- MN-contiguous operand, transposed in registers
+// Thread t < kBlocks owns the square block kb = t % 8 (K chunk), nb = t / 8.
+template <int E, int R>
+struct TransLoader {
+  static constexpr int CH = 16 / E;          // elements per chunk = block side
+  static constexpr int kBlocks = 8 * (R / CH);
+  static_assert(kBlocks <= kThreads, "tile too wide for one block per thread");
+  using T = typename Elem<E>::T;
+  const T* src;  // element (k = CH * kb, n = n0 + CH * nb) at k0 = 0
+  int64_t ld;    // elements between consecutive k rows
+  bool active;
+
+  __device__ __forceinline__ void init(const void* base, int64_t ld_elems, int64_t n0) {
+    const int t = threadIdx.x, kb = t % 8, nb = t / 8;
+    active = t < kBlocks;
+    ld = ld_elems;
+    src = static_cast<const T*>(base) + (int64_t)(CH * kb) * ld + n0 + CH * (active ? nb : 0);
+  }
+  __device__ __forceinline__ void load(int64_t k0, u32x4 (&r)[CH]) const {
+    if (active) {
+#pragma unroll
+      for (int j = 0; j < CH; j++) r[j] = *reinterpret_cast<const u32x4*>(src + (k0 + j) * ld);
+    }
+  }
+  // Whether this wavefront issues the loads (some lane active); uniform.
+  static __device__ __forceinline__ bool wave_loads() {
+    return (__builtin_amdgcn_readfirstlane(threadIdx.x) & ~63) < kBlocks;
+  }
+  // Bounds-checked variant for edge tiles: rows k >= k_ext and columns >= n_ext read as zero.
+  __device__ __forceinline__ void load_checked(int64_t k0, int64_t k_ext, int64_t n_ext, int64_t n0,
+                                               u32x4 (&r)[CH]) const {
+    const int t = threadIdx.x, kb = t % 8, nb = t / 8;
+#pragma unroll
+    for (int j = 0; j < CH; j++) {
+      r[j] = u32x4{0u, 0u, 0u, 0u};
+      const int64_t kk = k0 + CH * kb + j;
+      if (!active || kk >= k_ext) continue;
+      const int64_t nn = n0 + CH * nb;
+      const T* p = src + (k0 + j) * ld;
+      if (nn + CH <= n_ext && (ld % CH) == 0 && (n0 % CH) == 0) {
+        r[j] = *reinterpret_cast<const u32x4*>(p);
+      } else {
+        T e[CH];
+#pragma unroll
+        for (int x = 0; x < CH; x++) e[x] = (nn + x < n_ext) ? p[x] : (T)0;
+        r[j] = __builtin_bit_cast(u32x4, e);
+      }
+    }
+  }
+  // Transpose and write: output i is row n = CH * nb + (i ^ s), s = nb & 1.
+  __device__ __forceinline__ void store(uint8_t* tile, const u32x4 (&r)[CH]) const {
+    if (!active) return;
+    const int t = threadIdx.x, kb = t % 8, nb = t / 8, s = nb & 1;
+    if constexpr (E == 2) {
+      // out dword d = element i' of r[2d] (low half) and of r[2d + 1] (high half);
+      // both sit in dword i'/2 = i/2, half i' % 2.
+      const uint32_t sel_even = s ? 0x07060302u : 0x05040100u;  // for i even (i' % 2 == s)
+      const uint32_t sel_odd = s ? 0x05040100u : 0x07060302u;
+#pragma unroll
+      for (int i = 0; i < 8; i++) {
+        const uint32_t sel = (i & 1) ? sel_odd : sel_even;
+        u32x4 o;
+#pragma unroll
+        for (int d = 0; d < 4; d++) o[d] = __builtin_amdgcn_perm(r[2 * d + 1][i / 2], r[2 * d][i / 2], sel);
+        const int row = CH * nb + (i ^ s);
+        *reinterpret_cast<u32x4*>(tile + swz(row, kb)) = o;
+      }
+    } else {
+      // out dword d = byte i' of r[4d], r[4d+1], r[4d+2], r[4d+3]; byte i' lives in
+      // dword i'/4 = i/4 at position x = (i % 4) ^ s.
+#pragma unroll
+      for (int i = 0; i < 16; i++) {
+        const uint32_t x = (uint32_t)((i & 3) ^ s);
+        const uint32_t sel = x | ((4 + x) << 8) | (x << 16) | ((4 + x) << 24);
+        u32x4 o;
+#pragma unroll
+        for (int d = 0; d < 4; d++) {
+          const uint32_t lo = __builtin_amdgcn_perm(r[4 * d + 1][i / 4], r[4 * d][i / 4], sel);
+          const uint32_t hi = __builtin_amdgcn_perm(r[4 * d + 3][i / 4], r[4 * d + 2][i / 4], sel);
+          o[d] = __builtin_amdgcn_perm(hi, lo, 0x05040100u);
+        }
+        const int row = CH * nb + (i ^ s);
+        *reinterpret_cast<u32x4*>(tile + swz(row, kb)) = o;
+      }
+    }
+  }
+};
+
+// ---------------------------------------------------------------- K-contiguous operand, checked register path
+template <int E, int R>
+struct RegLoaderK {
+  static constexpr int kPer = R / 32;  // 16-byte chunks per thread (R rows x 8 chunks / 256)
+  using T = typename Elem<E>::T;
+  const uint8_t* row_ptr[kPer];
+  int64_t k_ext, mn_ext, mn0;
+
+  __device__ __forceinline__ static int row_of(int i) { return (threadIdx.x + i * kThreads) / 8; }
+  __device__ __forceinline__ static int chunk_of(int i) { return (threadIdx.x + i * kThreads) % 8; }
+
+  __device__ __forceinline__ void init(const void* const* parts, int64_t rows_per_part, int64_t ld_bytes,
+                                       int64_t mn_ext_, int64_t k_ext_, int64_t mn0_) {
+    k_ext = k_ext_;
+    mn_ext = mn_ext_;
+    mn0 = mn0_;
+#pragma unroll
+    for (int i = 0; i < kPer; i++) {
+      const int64_t row = mn0 + row_of(i);
+      row_ptr[i] = kmajor_row(parts, rows_per_part, ld_bytes, row < mn_ext ? row : 0);
+    }
+  }
+  __device__ __forceinline__ void load(int64_t k0, u32x4 (&r)[kPer]) const {
+    constexpr int CH = 16 / E;
+#pragma unroll
+    for (int i = 0; i < kPer; i++) {
+      r[i] = u32x4{0u, 0u, 0u, 0u};
+      if (mn0 + row_of(i) >= mn_ext) continue;
+      const int64_t gk = k0 + CH * chunk_of(i);
+      const T* p = reinterpret_cast<const T*>(row_ptr[i]) + gk;
+      if (gk + CH <= k_ext && (k_ext % CH) == 0) {
+        r[i] = *reinterpret_cast<const u32x4*>(p);
+      } else {
+        T e[CH];
+#pragma unroll
+        for (int x = 0; x < CH; x++) e[x] = (gk + x < k_ext) ? p[x] : (T)0;
+        r[i] = __builtin_bit_cast(u32x4, e);
+      }
+    }
+  }
+  __device__ __forceinline__ void store(uint8_t* tile, const u32x4 (&r)[kPer]) const {
+#pragma unroll
+    for (int i = 0; i < kPer; i++) *reinterpret_cast<u32x4*>(tile + swz(row_of(i), chunk_of(i))) = r[i];
+  }
+};
+
+// ---------------------------------------------------------------- compute
+// 16 (mn) x 64-byte fragment: lane l gets logical chunk c0 + l / 16 of row mn0 + l % 16.
+__device__ __forceinline__ u32x4 read_frag(const uint8_t* tile, int mn0, int c0) {
+  const int l = threadIdx.x % 64;
+  return *reinterpret_cast<const u32x4*>(tile + swz(mn0 + l % 16, c0 + l / 16));
+}
+
+template <int BM, int BN, typename Ops>
+__device__ __forceinline__ void compute_step(const uint8_t* As, const uint8_t* Bs,
+                                             typename Ops::Acc (&acc)[BM / 32][BN / 32]) {
+  constexpr int WM = BM / 2, WN = BN / 2, FM = WM / 16, FN = WN / 16;
+  const int wave = threadIdx.x / 64, wm = wave / 2, wn = wave % 2;
+#pragma unroll
+  for (int c0 = 0; c0 < 8; c0 += 4) {
+    u32x4 fa[FM], fb[FN];
+#pragma unroll
+    for (int i = 0; i < FM; i++) fa[i] = read_frag(As, wm * WM + 16 * i, c0);
+#pragma unroll
+    for (int j = 0; j < FN; j++) fb[j] = read_frag(Bs, wn * WN + 16 * j, c0);
+#pragma unroll
+    for (int i = 0; i < FM; i++)
+#pragma unroll
+      for (int j = 0; j < FN; j++) acc[i][j] = Ops::mfma(fa[i], fb[j], acc[i][j]);
+  }
+}
+
+// Copies the A tile of the step held in LDS to gather_out (K-contiguous A).
+template <int E, int BM>
+__device__ __forceinline__ void copy_gather(const uint8_t* As, void* gout, int64_t m, int64_t k, int64_t m0,
+                                            int64_t k0) {
+  using T = typename Elem<E>::T;
+  constexpr int CH = 16 / E;
+#pragma unroll
+  for (int i = 0; i < BM / 32; i++) {
+    const int c = threadIdx.x + i * kThreads, row = c / 8, chunk = c % 8;
+    const int64_t grow = m0 + row, gk = k0 + CH * chunk;
+    if (grow >= m || gk >= k) continue;
+    const u32x4 v = *reinterpret_cast<const u32x4*>(As + swz(row, chunk));
+    T* dst = static_cast<T*>(gout) + grow * k + gk;
+    if (gk + CH <= k && (k % CH) == 0) {
+      *reinterpret_cast<u32x4*>(dst) = v;
+    } else {
+      T e[CH];
+      __builtin_memcpy(e, &v, 16);
+      for (int x = 0; x < CH; x++)
+        if (gk + x < k) dst[x] = e[x];
+    }
+  }
+}
+
+// vmcnt-only wait (gfx9 encoding: vmcnt bits [3:0] and [15:14]; expcnt and
+// lgkmcnt at their maxima, i.e. not waited on).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// Workgroup barrier without a memory fence: this wavefront's LDS accesses are
+// complete (lgkmcnt 0) and its global loads stay in flight.  (__syncthreads
+// would also wait for every outstanding global load.)
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+// ---------------------------------------------------------------- MN-contiguous LDS layout
+// Row k of the tile holds R elements (R * E bytes) as 16-byte chunks; chunk c
+// sits at position c ^ mn_swz(k).  The XOR spreads the rows that one
+// ds_read_b64_tr_b16 / _b8 instruction touches over all 64 banks (each half
+// wavefront hits every bank once), which gfx950 then serves without
+// conflicts.
+template <int E, int R>
+__device__ __forceinline__ int mn_swz(int k) {
+  static_assert((E == 2 || E == 1) && (R == 224 || R == 128), "no swizzle for this tile");
+  if constexpr (E == 2 && R == 224) return 2 * ((k >> 3) & 1);
+  else if constexpr (E == 2) return 2 * ((k & 3) | (((k >> 3) & 1) << 2));
+  else if constexpr (R == 224) return (k >> 4) & 1;
+  else return ((k >> 1) & 3) | (((k >> 4) & 1) << 2);
+}
+template <int E, int R>
+__device__ __forceinline__ int swz_mn(int k, int c) { return k * (R * E) + ((c ^ mn_swz<E, R>(k)) << 4); }
+
+// ---------------------------------------------------------------- direct-to-LDS staging
+// One operand tile per step (R rows x 128 bytes of K = 8R slots of 16 bytes).
+// Thread t fills slots s = t + 256 i, i < R / 32, so instruction i of
+// wavefront w writes the 1 KB block 256 i + 64 w + lane, in lane order as
+// global_load_lds requires; the global address of each lane is chosen so
+// that the block holds the swizzled layout.  Rows (K-major) or chunks
+// (MN-major) past the matrix edge are clamped to the last valid one: their
+// products land only in C elements the epilogue does not store.
+template <int E, int R, bool KMAJ>
+struct DmaOperand {
+  static constexpr int kN = R / 32;  // DMA instructions per thread and step
+  const uint8_t* src[kN];            // this lane's 16 bytes at step 0
+  int64_t step_bytes;                // global distance between consecutive steps
+
+  // K-contiguous operand: row r of the tile is matrix row mn0 + r, found in
+  // the row blocks `parts` (rows_per_part rows each, ld_bytes per row).
+  __device__ __forceinline__ void init_k(const void* const* parts, int64_t rows_per_part, int64_t ld_bytes,
+                                         int64_t mn0, int64_t mn_ext) {
+#pragma unroll
+    for (int i = 0; i < kN; i++) {
+      const int s = threadIdx.x + kThreads * i, row = s / 8, c = (s % 8) ^ (row & 7);
+      const int64_t r = mn0 + row < mn_ext ? mn0 + row : mn_ext - 1;
+      src[i] = kmajor_row(parts, rows_per_part, ld_bytes, r) + c * 16;
+    }
+    step_bytes = kRowBytes;
+  }
+  // MN-contiguous operand stored (k, mn) with ld_bytes between k rows;
+  // mn_ext is a multiple of the 16-byte chunk.
+  __device__ __forceinline__ void init_mn(const void* base, int64_t ld_bytes, int64_t mn0, int64_t mn_ext) {
+    constexpr int CH = 16 / E, kChunks = R * E / 16;
+#pragma unroll
+    for (int i = 0; i < kN; i++) {
+      const int s = threadIdx.x + kThreads * i, k = s / kChunks, c = (s % kChunks) ^ mn_swz<E, R>(k);
+      int64_t col = mn0 + (int64_t)c * CH;
+      if (col + CH > mn_ext) col = mn_ext - CH;
+      src[i] = static_cast<const uint8_t*>(base) + k * ld_bytes + col * E;
+    }
+    step_bytes = (int64_t)(kRowBytes / E) * ld_bytes;
+  }
+  __device__ __forceinline__ void issue(uint8_t* tile, int64_t off) const {
+    const int w = threadIdx.x / 64;
+#pragma unroll
+    for (int i = 0; i < kN; i++)
+      __builtin_amdgcn_global_load_lds((gptr_t)(src[i] + off), (lptr_t)(tile + 4096 * i + 1024 * w), 16, 0, 0);
+  }
+};
+
+// ---------------------------------------------------------------- fragment reads
+// NF fragments of 16 rows (m or n) starting at tile row row0, for the K
+// half kk (64 bytes of K) of a step.  MFMA operand layout: lane l holds row
+// l % 16 and the 16 bytes of K at 16 (l / 16).
+//  - K-major tile: one ds_read_b128 per fragment.
+//  - MN-major tile: two transpose reads.  Within each 16-lane group, lane t
+//    of ds_read_b64_tr_b16 receives element t % 4 of the 8-byte pieces
+//    addressed by lanes 4 j + t / 4 (j = 0..3), so lane s addresses k row
+//    s / 4, columns 4 (s % 4) .. + 3, and lane t ends up with column t of 4
+//    consecutive k rows; ds_read_b64_tr_b8 does the same for 8 rows of bytes
+//    (lane s: row s / 2, bytes 8 (s % 2) .. + 7).
+template <int E, int R, bool KMAJ, int NF>
+struct FragReader {
+  static constexpr int kOffs = KMAJ ? 2 : NF;
+  int off[kOffs];
+
+  __device__ __forceinline__ void init(int row0) {
+    const int l = threadIdx.x % 64, g = l / 16, s = l % 16;
+    if constexpr (KMAJ) {
+      const int row = row0 + s;
+#pragma unroll
+      for (int kk = 0; kk < 2; kk++) off[kk] = swz(row, 4 * kk + g);
+    } else if constexpr (E == 2) {
+#pragma unroll
+      for (int j = 0; j < NF; j++) {
+        const int k = 8 * g + s / 4, col = row0 + 16 * j + 4 * (s % 4);
+        off[j] = swz_mn<E, R>(k, col / 8) + (col % 8) * 2;
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < NF; j++) {
+        const int k = 16 * g + s / 2, col = row0 + 16 * j + 8 * (s % 2);
+        off[j] = swz_mn<E, R>(k, col / 16) + col % 16;
+      }
+    }
+  }
+  // The swizzles depend only on bits of k that kk and the second read leave unchanged.
+  __device__ __forceinline__ void read(const uint8_t* tile, int kk, u32x4 (&f)[NF]) const {
+    constexpr int P = R * E;  // bytes per k row of an MN-major tile
+    int o[kOffs];
+#pragma unroll
+    for (int j = 0; j < kOffs; j++) {
+      o[j] = off[j];
+      asm volatile("" : "+v"(o[j]));  // keep the stage base additions inside the loop
+    }
+#pragma unroll
+    for (int j = 0; j < NF; j++) {
+      if constexpr (KMAJ) {
+        f[j] = *reinterpret_cast<const u32x4*>(tile + o[kk] + 16 * kRowBytes * j);
+      } else if constexpr (E == 2) {
+        const uint8_t* q = tile + o[j] + 32 * kk * P;
+        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)q);
+        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(q + 4 * P));
+        const u32x2 a = __builtin_bit_cast(u32x2, lo), b = __builtin_bit_cast(u32x2, hi);
+        f[j] = u32x4{a[0], a[1], b[0], b[1]};
+      } else {
+        const uint8_t* q = tile + o[j] + 64 * kk * P;
+        const i32x2 lo = __builtin_amdgcn_ds_read_tr8_b64_v2i32((__attribute__((address_space(3))) i32x2*)q);
+        const i32x2 hi = __builtin_amdgcn_ds_read_tr8_b64_v2i32((__attribute__((address_space(3))) i32x2*)(q + 8 * P));
+        f[j] = u32x4{(uint32_t)lo[0], (uint32_t)lo[1], (uint32_t)hi[0], (uint32_t)hi[1]};
+      }
+    }
+  }
+};
+
+// Fast path: k is a multiple of the step and every operand row is 16-byte
+// aligned; tiles may cross the M / N edges (clamped loads).  Three LDS stages
+// (separate arrays, so the compiler can tell a DMA target from the buffer
+// being read) hold steps kt, kt+1, kt+2; the MFMA fragments of the two K
+// halves of a step alternate between two register sets.  Step kt:
+//   issue the DMA of step kt+2 (its stage was last read before the previous
+//   barrier); read half 1 of step kt; MFMAs of half 0;
+//   wait for the DMA of step kt+1, barrier;
+//   read half 0 of step kt+1; MFMAs of half 1.
+// The barrier sits between two blocks of MFMAs, and every LDS read has a
+// block of MFMAs to hide behind.
+template <int E, int BM, int BN, bool AK, bool BKM, bool GATHER, typename Ops>
+__device__ __forceinline__ void mainloop_fast(const Problem& p, int64_t m0, int64_t n0, int gather_phase,
+                                              int gather_every, uint8_t* L0, uint8_t* L1, uint8_t* L2,
+                                              typename Ops::Acc (&acc)[BM / 32][BN / 32]) {
+  constexpr int BK = kRowBytes / E;  // K elements per step
+  constexpr int kATile = BM * kRowBytes;
+  constexpr int WM = BM / 2, WN = BN / 2, FM = WM / 16, FN = WN / 16;
+  using DA = DmaOperand<E, BM, AK>;
+  using DB = DmaOperand<E, BN, BKM>;
+  constexpr int ND = DA::kN + DB::kN;  // DMA instructions per thread and step
+  constexpr int NG = BM / 32;          // gather_out stores per thread
+  DA da;
+  DB db;
+  if constexpr (AK) da.init_k(p.a_parts, p.rows_per_part, p.k * E, m0, p.m);
+  else da.init_mn(p.a_parts[0], p.m * E, m0, p.m);
+  if constexpr (BKM) {
+    const void* bparts[1] = {p.b};
+    db.init_k(bparts, p.n, p.k * E, n0, p.n);
+  } else {
+    db.init_mn(p.b, p.n * E, n0, p.n);
+  }
+  const int wave = threadIdx.x / 64, wm = wave / 2, wn = wave % 2;
+  FragReader<E, BM, AK, FM> ra;
+  FragReader<E, BN, BKM, FN> rb;
+  ra.init(wm * WM);
+  rb.init(wn * WN);
+  const int nk = (int)(p.k / BK);
+  int next_gather = gather_phase;
+  const bool m_inside = m0 + BM <= p.m;
+
+  u32x4 fa0[FM], fb0[FN], fa1[FM], fb1[FN];
+  auto dma = [&](uint8_t* L, int kt) {
+    da.issue(L, kt * da.step_bytes);
+    db.issue(L + kATile, kt * db.step_bytes);
+  };
+  auto mma = [&](const u32x4(&fa)[FM], const u32x4(&fb)[FN]) {
+#pragma unroll
+    for (int i = 0; i < FM; i++)
+#pragma unroll
+      for (int j = 0; j < FN; j++) acc[i][j] = Ops::mfma(fa[i], fb[j], acc[i][j]);
+  };
+  // FULL: steps kt+1 and kt+2 exist (no branches around the DMA and the reads).
+  auto step = [&](int kt, auto FULL_, uint8_t* cur, uint8_t* nxt, uint8_t* nn) {
+    constexpr bool FULL = decltype(FULL_)::value;
+    const bool dma2 = FULL || kt + 2 < nk;
+    if (dma2) dma(nn, kt + 2);
+    // gather_out copy of this step's A tile: NG stores per thread when the
+    // tile lies inside M (fewer at the edge, where the wait below is a full one)
+    bool gathered = false;
+    if (GATHER && kt == next_gather) {
+      copy_gather<E, BM>(cur, p.gather_out, p.m, p.k, m0, (int64_t)kt * BK);
+      next_gather += gather_every;
+      gathered = true;
+    }
+    ra.read(cur, 1, fa1);
+    rb.read(cur + kATile, 1, fb1);
+    mma(fa0, fb0);
+    // the DMA of step kt+1 has landed; only younger ones and gather stores may fly
+    if (dma2 && !(GATHER && gathered)) wait_vmcnt<ND>();
+    else if (dma2 && m_inside) wait_vmcnt<ND + NG>();
+    else wait_vmcnt<0>();
+    lds_barrier();
+    if (FULL || kt + 1 < nk) {
+      ra.read(nxt, 0, fa0);
+      rb.read(nxt + kATile, 0, fb0);
+    }
+    mma(fa1, fb1);
+  };
+
+  dma(L0, 0);
+  if (nk > 1) {
+    dma(L1, 1);
+    wait_vmcnt<ND>();
+  } else {
+    wait_vmcnt<0>();
+  }
+  lds_barrier();
+  ra.read(L0, 0, fa0);
+  rb.read(L0 + kATile, 0, fb0);
+  using Full = std::integral_constant<bool, true>;
+  using Part = std::integral_constant<bool, false>;
+  int kt = 0;
+  for (; kt + 4 < nk; kt += 3) {
+    step(kt, Full(), L0, L1, L2);
+    step(kt + 1, Full(), L1, L2, L0);
+    step(kt + 2, Full(), L2, L0, L1);
+  }
+  if (kt < nk) step(kt, Part(), L0, L1, L2);
+  if (kt + 1 < nk) step(kt + 1, Part(), L1, L2, L0);
+  if (kt + 2 < nk) step(kt + 2, Part(), L2, L0, L1);
+  if (kt + 3 < nk) step(kt + 3, Part(), L0, L1, L2);
+}
+
+// Checked path (edge tiles, ragged K): bounds-tested register
+// loads into the same LDS layout, loads of step k+1 overlapping step k.
+template <int E, int BM, int BN, bool AK, bool BKM, typename Ops>
+__device__ __forceinline__ void mainloop_checked(const Problem& p, int64_t m0, int64_t n0, int gather_phase,
+                                                 int gather_every, uint8_t* s0, uint8_t* s1,
+                                                 typename Ops::Acc (&acc)[BM / 32][BN / 32]) {
+  constexpr int BK = kRowBytes / E;
+  constexpr int kATile = BM * kRowBytes;
+  using LA = typename std::conditional<AK, RegLoaderK<E, BM>, TransLoader<E, BM>>::type;
+  using LB = typename std::conditional<BKM, RegLoaderK<E, BN>, TransLoader<E, BN>>::type;
+  constexpr int NA = AK ? BM / 32 : 16 / E;
+  constexpr int NB = BKM ? BN / 32 : 16 / E;
+  LA la;
+  LB lb;
+  if constexpr (AK) la.init(p.a_parts, p.rows_per_part, p.k * E, p.m, p.k, m0);
+  else la.init(p.a_parts[0], p.m, m0);
+  const void* bparts[1] = {p.b};
+  if constexpr (BKM) lb.init(bparts, p.n, p.k * E, p.n, p.k, n0);
+  else lb.init(p.b, p.n, n0);
+  auto loadA = [&](int64_t k0, u32x4 (&r)[NA]) {
+    if constexpr (AK) la.load(k0, r);
+    else la.load_checked(k0, p.k, p.m, m0, r);
+  };
+  auto loadB = [&](int64_t k0, u32x4 (&r)[NB]) {
+    if constexpr (BKM) lb.load(k0, r);
+    else lb.load_checked(k0, p.k, p.n, n0, r);
+  };
+  u32x4 ra[NA], rb[NB];
+  const int nk = (int)((p.k + BK - 1) / BK);
+  loadA(0, ra);
+  loadB(0, rb);
+  la.store(s0, ra);
+  lb.store(s0 + kATile, rb);
+  __syncthreads();
+  for (int kt = 0; kt < nk; kt++) {
+    uint8_t* cur = (kt & 1) ? s1 : s0;
+    uint8_t* nxt = (kt & 1) ? s0 : s1;
+    if (kt + 1 < nk) {
+      loadA((int64_t)(kt + 1) * BK, ra);
+      loadB((int64_t)(kt + 1) * BK, rb);
+    }
+    if (AK && gather_every > 0 && kt % gather_every == gather_phase)
+      copy_gather<E, BM>(cur, p.gather_out, p.m, p.k, m0, (int64_t)kt * BK);
+    compute_step<BM, BN, Ops>(cur, cur + kATile, acc);
+    if (kt + 1 < nk) {
+      la.store(nxt, ra);
+      lb.store(nxt + kATile, rb);
+    }
+    __syncthreads();
+  }
+}
+
+// LDS bytes per stage: the two K-major operand tiles.
+template <int BM, int BN>
+constexpr int stage_bytes() { return (BM + BN) * kRowBytes; }
+
+// Runs the main loop variant this workgroup needs.  gather: copy the gathered
+// A to p.gather_out, spread over the workgroups of the row of tiles (the
+// workgroup of column tile tn copies the steps kt with kt % tiles_n == tn).
+template <int E, int BM, int BN, bool AK, bool BKM, bool VEC, typename Ops>
+__device__ __forceinline__ void run_mainloop(const Problem& p, int64_t m0, int64_t n0, int tn, int tiles_n,
+                                             uint8_t* L0, uint8_t* L1, uint8_t* L2,
+                                             typename Ops::Acc (&acc)[BM / 32][BN / 32]) {
+  constexpr int BK = kRowBytes / E;
+  const int gather_every = (AK && p.gather_out != nullptr) ? tiles_n : 0;
+  if constexpr (VEC) {
+    if (p.k % BK == 0) {
+      if (AK && gather_every > 0) mainloop_fast<E, BM, BN, AK, BKM, AK, Ops>(p, m0, n0, tn, gather_every, L0, L1, L2, acc);
+      else mainloop_fast<E, BM, BN, AK, BKM, false, Ops>(p, m0, n0, tn, gather_every, L0, L1, L2, acc);
+      return;
+    }
+  }
+  mainloop_checked<E, BM, BN, AK, BKM, Ops>(p, m0, n0, tn, gather_every, L0, L1, acc);
+}
 
 // Choose the XCD-aware tile of workgroup blockIdx.x.
 __device__ __forceinline__ void tile_of_block(int64_t m, int64_t n, int bm, int bn, int cols_order, int& tm, int& tn) {
@@ -258,107 +609,20 @@ __device__ __forceinline__ void tile_of_block(int64_t m, int64_t n, int bm, int 
   }
 }
 
-// Main loop: accumulates the (BM/2) x (BN/2) block of this wavefront into acc.
-// Ops supplies: typedef Acc (f32x4 / i32x4); static Acc mfma(u32x4 a, u32x4 b, Acc c).
-template <int E, int BM, int BN, bool AK, bool BKM, bool VEC, typename Ops>
-__device__ __forceinline__ void mainloop(const Problem& p, int64_t m0, int64_t n0, bool write_gather,
-                                         typename Elem<E>::T* lds,
-                                         typename Ops::Acc (&acc)[BM / 32][BN / 32]) {
-  using TA = Tile<E, BM, AK>;
-  using TB = Tile<E, BN, BKM>;
-  using T = typename Elem<E>::T;
-  constexpr int WM = BM / 2, WN = BN / 2;
-  constexpr int FM = WM / 16, FN = WN / 16;
-  constexpr int kStage = TA::kLds + TB::kLds;
-  constexpr int BK = TA::kBK;
-  constexpr int MK = 64 / E;  // K elements per MFMA
-
-  Loader<E, BM, AK> la;
-  Loader<E, BN, BKM> lb;
-  la.init(p.a_parts, AK ? p.rows_per_part : p.m, AK ? p.k : p.m, p.m, p.k, m0, p.gather_out);
-  lb.init(&p.b, p.n, BKM ? p.k : p.n, p.n, p.k, n0, nullptr);
-
-  const int wave = threadIdx.x / 64;
-  const int wm = wave / 2, wn = wave % 2;
-
-  // Global loads run two K steps ahead of the MFMAs: register set s % 2 holds
-  // step s between its load and its LDS write.  Step kt is computed from LDS
-  // buffer kt % 2 while step kt + 1 waits in registers and step kt + 2 is in
-  // flight; after the MFMAs, step kt + 1 is written to the other buffer and
-  // one barrier closes the step.
-  u32x4 ra[2][TA::kPer], rb[2][TB::kPer];
-  const int nk = (int)((p.k + BK - 1) / BK);
-  const bool gather = write_gather;
-
-  auto compute = [&](const T* As, const T* Bs) {
-#pragma unroll
-    for (int kk = 0; kk < BK; kk += MK) {
-      u32x4 fa[FM], fb[FN];
-#pragma unroll
-      for (int i = 0; i < FM; i++) fa[i] = read_frag<E, BM, AK>(As, wm * WM + 16 * i, kk);
-#pragma unroll
-      for (int j = 0; j < FN; j++) fb[j] = read_frag<E, BN, BKM>(Bs, wn * WN + 16 * j, kk);
-#pragma unroll
-      for (int i = 0; i < FM; i++)
-#pragma unroll
-        for (int j = 0; j < FN; j++) acc[i][j] = Ops::mfma(fa[i], fb[j], acc[i][j]);
-    }
-  };
-
-  la.template load<VEC>(0, ra[0]);
-  lb.template load<VEC>(0, rb[0]);
-  if (nk > 1) {
-    la.template load<VEC>(BK, ra[1]);
-    lb.template load<VEC>(BK, rb[1]);
-  }
-  la.store(lds, ra[0]);
-  lb.store(lds + TA::kLds, rb[0]);
-  if (gather) la.template store_gather<VEC>(0, ra[0]);
-  __syncthreads();
-
-  // one K step; S is the register set of step kt (static so the sets stay in registers)
-  auto step = [&](int kt, auto S_) {
-    constexpr int S = decltype(S_)::value;
-    const T* As = lds + S * kStage;
-    if (kt + 2 < nk) {
-      la.template load<VEC>((int64_t)(kt + 2) * BK, ra[S]);
-      lb.template load<VEC>((int64_t)(kt + 2) * BK, rb[S]);
-    }
-    compute(As, As + TA::kLds);
-    if (kt + 1 < nk) {
-      T* nxt = lds + (S ^ 1) * kStage;
-      la.store(nxt, ra[S ^ 1]);
-      lb.store(nxt + TA::kLds, rb[S ^ 1]);
-      if (gather) la.template store_gather<VEC>((int64_t)(kt + 1) * BK, ra[S ^ 1]);
-    }
-    __syncthreads();
-  };
-  for (int kt = 0; kt < nk; kt += 2) {
-    step(kt, std::integral_constant<int, 0>());
-    if (kt + 1 < nk) step(kt + 1, std::integral_constant<int, 1>());
-  }
-}
-
-// LDS elements the kernel needs: two operand stages, or the 16-bit C tile.
-template <int E, int BM, int BN, bool AK, bool BKM>
-constexpr int lds_bytes() {
-  constexpr int stages = 2 * (Tile<E, BM, AK>::kLds + Tile<E, BN, BKM>::kLds) * E;
-  constexpr int ctile = BM * (BN + 8) * 2;
-  return stages > ctile ? stages : ctile;
-}
-
-// Writes a wavefront's rounded 16-bit C fragments to the LDS C tile, then the
-// whole workgroup stores the tile with 16-byte row-contiguous stores.
-// cvt(i, j, r, row, col) returns the 16-bit output bits of element r of
-// fragment (i, j) at tile coordinates (row, col).
+// Writes a wavefront's rounded 16-bit C fragments to an LDS copy of the C tile
+// (rows [0, BM/2) in h0, rows [BM/2, BM) in h1), then the whole workgroup
+// stores the tile with 16-byte row-contiguous stores.  cvt(i, j, r, row, col)
+// returns the 16-bit output of element r of fragment (i, j) at tile
+// coordinates (row, col).
 template <int BM, int BN, bool VEC, typename Cvt>
-__device__ __forceinline__ void store_c16(uint16_t* lds, uint16_t* C, int64_t m, int64_t n, int64_t m0, int64_t n0,
-                                          Cvt cvt) {
+__device__ __forceinline__ void store_c16(uint16_t* h0, uint16_t* h1, uint16_t* C, int64_t m, int64_t n, int64_t m0,
+                                          int64_t n0, Cvt cvt) {
   constexpr int WM = BM / 2, WN = BN / 2;
   constexpr int FM = WM / 16, FN = WN / 16;
   constexpr int kPitch = BN + 8;
   const int wave = threadIdx.x / 64, lane = threadIdx.x % 64;
   const int wm = wave / 2, wn = wave % 2;
+  uint16_t* half = wm ? h1 : h0;
 #pragma unroll
   for (int i = 0; i < FM; i++)
 #pragma unroll
@@ -366,8 +630,8 @@ __device__ __forceinline__ void store_c16(uint16_t* lds, uint16_t* C, int64_t m,
       const int col = wn * WN + 16 * j + lane % 16;
 #pragma unroll
       for (int r = 0; r < 4; r++) {
-        const int row = wm * WM + 16 * i + 4 * (lane / 16) + r;
-        lds[row * kPitch + col] = cvt(i, j, r, row, col);
+        const int row = 16 * i + 4 * (lane / 16) + r;  // row inside the half
+        half[row * kPitch + col] = cvt(i, j, r, wm * WM + row, col);
       }
     }
   __syncthreads();
@@ -376,7 +640,7 @@ __device__ __forceinline__ void store_c16(uint16_t* lds, uint16_t* C, int64_t m,
     const int row = c / kRowChunks, col = (c % kRowChunks) * 8;
     const int64_t grow = m0 + row, gcol = n0 + col;
     if (grow >= m) continue;
-    const uint16_t* src = lds + row * kPitch + col;
+    const uint16_t* src = (row < WM ? h0 + row * kPitch : h1 + (row - WM) * kPitch) + col;
     if (VEC && gcol + 8 <= n) {
       *reinterpret_cast<u32x4*>(C + grow * n + gcol) = *reinterpret_cast<const u32x4*>(src);
     } else {
@@ -384,6 +648,14 @@ __device__ __forceinline__ void store_c16(uint16_t* lds, uint16_t* C, int64_t m,
         if (gcol + j < n) C[grow * n + gcol + j] = src[j];
     }
   }
+}
+
+// LDS bytes of one stage array: an operand stage, or half of the 16-bit C tile.
+template <int BM, int BN>
+constexpr int lds_stage_array_bytes() {
+  constexpr int st = stage_bytes<BM, BN>();
+  constexpr int half_c = (BM / 2) * (BN + 8) * 2;
+  return st > half_c ? st : half_c;
 }
 
 // Bytes the L2s fetch with a row-wise vs a column-wise tile order: each XCD

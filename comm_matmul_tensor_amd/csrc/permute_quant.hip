@@ -50,22 +50,23 @@ __device__ __forceinline__ int quant1(float y, float s) {
   return (int)r;
 }
 
-// q = clamp(rint(y / s)) with the same result as the IEEE division, computed
-// as y * (1 / s).  With inv = RN(1 / s), RN(y * inv) is within
-// |y / s| (2^-23 + 2^-48) <= 1.6e-5 of y / s (|y / s| <= 127), and RN(y / s)
-// within 3.9e-6, so both round to the same integer unless y * inv lies within
-// 2e-5 of a half-integer; those rare elements take the exact division.
-__device__ __forceinline__ int quant_fast(float y, float s, float inv) {
-  const float qa = y * inv;
-  const float fl = __builtin_floorf(qa);
-  if (__builtin_fabsf(qa - fl - 0.5f) <= 3.0e-5f) return quant1(y, s);
-  float r = __builtin_rintf(qa);
-  r = fminf(fmaxf(r, -127.0f), 127.0f);
-  return (int)r;
-}
+// Why y * (1 / s) may replace the IEEE quotient y / s: with inv = RN(1 / s),
+// RN(y * inv) is within |y / s| (2^-23 + 2^-48) <= 1.6e-5 of y / s when
+// |y / s| <= 127 (1 + 2^-23), and RN(y / s) is within 3.9e-6 of y / s, so
+// both round to the same integer unless y * inv lies within 2e-5 of a
+// half-integer.  The kernel flags every element within 3e-5 and redoes it
+// with the division.
 
 // Vector path: h % 16 == 0, so every 16-element unit of P lies inside one
-// source row and is 32-byte aligned.
+// source row and is 32-byte aligned.  All of the token's loads are issued
+// first; y = P * smooth stays in registers between the two passes.
+//
+// Pass 2 per element, with inv = 1/s:  qa = y * inv;  c = med3(qa, -127, 127);
+// m = c + 1.5 * 2^23, which rounds c to an integer with ties to even and
+// leaves that integer's two's-complement low byte in the low byte of m's bit
+// pattern (|c| <= 127 < 2^22), so the int8 code is one byte of m.  If
+// |qa - rint(c)| >= 0.5 - 3e-5 the element is near a half-integer and the
+// wavefront recomputes its codes with the IEEE division (see quant_fast).
 template <int DT>
 __global__ __launch_bounds__(kThreads) void permute_quant_vec(QuantArgs a) {
   __shared__ float red[kThreads / 64];
@@ -76,7 +77,6 @@ __global__ __launch_bounds__(kThreads) void permute_quant_vec(QuantArgs a) {
   const uint16_t* x1 = static_cast<const uint16_t*>(a.x1);
   const uint16_t* sm = static_cast<const uint16_t*>(a.smooth);
 
-  // issue every load of the token before using any of them
   u32x4 raw[kMaxUnits][2], smr[kMaxUnits][2];
 #pragma unroll
   for (int v = 0; v < kMaxUnits; v++) {
@@ -101,6 +101,8 @@ __global__ __launch_bounds__(kThreads) void permute_quant_vec(QuantArgs a) {
       }
     }
   }
+  // y, element 2w+b of half hlf of unit v: y[v][hlf*8 + 2w + b]
+  float y[kMaxUnits][16];
   float amax = 0.0f;
 #pragma unroll
   for (int v = 0; v < kMaxUnits; v++) {
@@ -112,9 +114,10 @@ __global__ __launch_bounds__(kThreads) void permute_quant_vec(QuantArgs a) {
         for (int w = 0; w < 4; w++)
 #pragma unroll
           for (int b = 0; b < 2; b++) {
-            float y = dec16<DT>(raw[v][hlf][w] >> (16 * b));
-            if (sm) y *= dec16<DT>(smr[v][hlf][w] >> (16 * b));
-            amax = fmaxf(amax, __builtin_fabsf(y));
+            float yy = dec16<DT>(raw[v][hlf][w] >> (16 * b));
+            if (sm) yy *= dec16<DT>(smr[v][hlf][w] >> (16 * b));
+            y[v][hlf * 8 + 2 * w + b] = yy;
+            amax = fmaxf(amax, __builtin_fabsf(yy));
           }
     }
   }
@@ -125,34 +128,42 @@ __global__ __launch_bounds__(kThreads) void permute_quant_vec(QuantArgs a) {
   // when s is a normal number; rows with a subnormal scale use the division.
   const float inv = 1.0f / s;
   const bool fast = s >= 1.17549435e-38f;  // uniform over the workgroup
+  constexpr float kMagic = 12582912.0f;    // 1.5 * 2^23
 
 #pragma unroll
   for (int v = 0; v < kMaxUnits; v++) {
     const int u = threadIdx.x + v * kThreads;
     if (u < units) {
       const int64_t e = (int64_t)u * 16;
-      u32x4 qv;
+      u32x4 qv = {0u, 0u, 0u, 0u};
+      if (amax > 0.0f) {
+        bool near = !fast;
+        uint32_t mb[16];
 #pragma unroll
-      for (int hlf = 0; hlf < 2; hlf++)
-#pragma unroll
-        for (int w = 0; w < 4; w += 2) {
-          uint32_t packed = 0;
-#pragma unroll
-          for (int ww = 0; ww < 2; ww++)
-#pragma unroll
-            for (int b = 0; b < 2; b++) {
-              float y = dec16<DT>(raw[v][hlf][w + ww] >> (16 * b));
-              if (sm) y *= dec16<DT>(smr[v][hlf][w + ww] >> (16 * b));
-              const int q = amax > 0.0f ? (fast ? quant_fast(y, s, inv) : quant1(y, s)) : 0;
-              packed |= ((uint32_t)q & 0xFFu) << (8 * (2 * ww + b));
-            }
-          qv[2 * hlf + w / 2] = packed;
+        for (int i = 0; i < 16; i++) {
+          const float qa = y[v][i] * inv;
+          const float c = __builtin_amdgcn_fmed3f(qa, -127.0f, 127.0f);
+          const float m = c + kMagic;
+          near |= __builtin_fabsf(qa - (m - kMagic)) >= 0.49997f;
+          mb[i] = __float_as_uint(m);
         }
+        if (near) {  // rare: redo this unit with the IEEE division
+#pragma unroll
+          for (int i = 0; i < 16; i++) mb[i] = (uint32_t)quant1(y[v][i], s);
+        }
+#pragma unroll
+        for (int w = 0; w < 4; w++)
+          qv[w] = (mb[4 * w] & 0xFFu) | ((mb[4 * w + 1] & 0xFFu) << 8) | ((mb[4 * w + 2] & 0xFFu) << 16) |
+                  (mb[4 * w + 3] << 24);
+      }
       *reinterpret_cast<u32x4*>(a.q + t * cols + e) = qv;
-      if (a.permuted) {
+      if (a.permuted) {  // optional copy of P: reload the unit rather than keep it in registers
+        const int hh = (int)a.h;
+        const int j = (int)e / hh, c = (int)e - j * hh;
+        const u32x4* src = reinterpret_cast<const u32x4*>(x1 + (((int64_t)j * T + t) * a.h + c));
         u32x4* dst = reinterpret_cast<u32x4*>(static_cast<uint16_t*>(a.permuted) + t * cols + e);
-        dst[0] = raw[v][0];
-        dst[1] = raw[v][1];
+        dst[0] = src[0];
+        dst[1] = src[1];
       }
     }
   }
