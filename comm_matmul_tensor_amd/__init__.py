@@ -7,7 +7,7 @@ CPU or PyTorch fallback: if ``libmc2.so`` is missing, importing this package
 raises.
 
 Functions carry the C names:
-  mc2_allgather_matmul, mc2_matmul_grad_input, mc2_matmul_grad_weight,
+  mc2_allgather_matmul, mc2_allgather_arrival_fallbacks, mc2_matmul_grad_input, mc2_matmul_grad_weight,
   mc2_alltoall_quant_matmul_workspace_size, mc2_alltoall_quant_matmul,
   mc2_quant_all_reduce, mc2_status_string, mc2_last_error.
 """
@@ -55,6 +55,7 @@ _SIGS = {
     "mc2_alltoall_quant_matmul": [_P, _INT, _I64, _I64, _INT, _P, _I64, _P, _P, _P, _P, _P, _P, _P, _P,
                                   _P, ctypes.c_size_t, _P],
     "mc2_quant_all_reduce": [_P, _P, _INT, _I64, _I64, _INT, _INT, _P, _INT, _P],
+    "mc2_allgather_arrival_fallbacks": [_INT, ctypes.POINTER(ctypes.c_uint)],
 }
 for _name, _args in _SIGS.items():
     _f = getattr(_lib, _name)
@@ -142,6 +143,14 @@ def mc2_allgather_matmul(shards: Sequence[torch.Tensor], x2: torch.Tensor, *, x2
     return out, gather_out
 
 
+def mc2_allgather_arrival_fallbacks(reset: bool = False) -> int:
+    """GEMM workgroups of MC2_AG_ARRIVAL calls whose wait for a row block timed
+    out (they read the shard directly); waits for the device to be idle."""
+    n = ctypes.c_uint(0)
+    _check(_lib.mc2_allgather_arrival_fallbacks(int(reset), ctypes.byref(n)))
+    return n.value
+
+
 def mc2_matmul_grad_input(dy: torch.Tensor, w: torch.Tensor, *, out: Optional[torch.Tensor] = None,
                           stream=None) -> torch.Tensor:
     """dX_partial = dY @ W, W in nn.Linear (out, in) = (n_local, k) layout."""
@@ -222,7 +231,7 @@ def mc2_quant_all_reduce(x: Sequence[torch.Tensor], scales: Sequence[torch.Tenso
 
 
 __all__ = [
-    "mc2_allgather_matmul", "mc2_matmul_grad_input", "mc2_matmul_grad_weight",
+    "mc2_allgather_matmul", "mc2_allgather_arrival_fallbacks", "mc2_matmul_grad_input", "mc2_matmul_grad_weight",
     "mc2_alltoall_quant_matmul_workspace_size", "mc2_alltoall_quant_matmul", "mc2_quant_all_reduce",
     "mc2_status_string", "mc2_last_error", "Mc2Error", "LIB_PATH",
 ]

@@ -17,9 +17,12 @@ constexpr int kMaxDevices = 64;
 struct DeviceState {
   bool checked = false;
   bool ok = false;
-  // arrival emulation: copy stream, ready flags (one per rank block + one
-  // timeout flag) and a call counter that makes every call's flag values new
+  // arrival emulation: copy stream, fork / join events, ready flags (one per
+  // rank block, then the fallback counter) and a call counter that makes
+  // every call's flag value new
+  bool arrival_ready = false;
   hipStream_t copy_stream = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr;
   unsigned* flags = nullptr;
   unsigned epoch = 0;
 };
@@ -56,6 +59,34 @@ mc2_status current_device(int* dev_out) {
 }
 
 int dt(mc2_dtype d) { return static_cast<int>(d); }
+
+// Arrival flags: kMaxRanks blocks x kArrivalChunks chunks, then the count of
+// timed-out waits.
+constexpr int kArrivalChunks = 16;
+constexpr int kFallbackSlot = kMaxRanks * kArrivalChunks;
+constexpr size_t kFlagBytes = 4096;
+static_assert((kFallbackSlot + 1) * sizeof(unsigned) <= kFlagBytes, "flag buffer");
+
+// Creates the arrival-emulation resources of device `dev` once.  The flags
+// sit in uncached device memory so that the GEMM's polls read memory, not a
+// stale cache line; that memory is kept until the process ends.
+mc2_status arrival_setup(int dev, DeviceState** out) {
+  std::lock_guard<std::mutex> lock(g_dev_mutex);
+  DeviceState& st = g_dev[dev];
+  if (!st.arrival_ready) {
+    hipError_t e = hipStreamCreateWithFlags(&st.copy_stream, hipStreamNonBlocking);
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&st.fork, hipEventDisableTiming);
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&st.join, hipEventDisableTiming);
+    if (e == hipSuccess)
+      e = hipExtMallocWithFlags(reinterpret_cast<void**>(&st.flags), kFlagBytes, hipDeviceMallocUncached);
+    if (e == hipSuccess) e = hipMemset(st.flags, 0, kFlagBytes);
+    if (e == hipSuccess) e = hipDeviceSynchronize();
+    if (e != hipSuccess) return hip_fail(e, "arrival emulation set-up");
+    st.arrival_ready = true;
+  }
+  *out = &st;
+  return MC2_OK;
+}
 
 size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
@@ -186,7 +217,62 @@ mc2_status mc2_allgather_matmul(const void* const* shards, int world_size, int64
     if (e != hipSuccess) return hip_fail(e, "allgather_matmul launch");
     return MC2_OK;
   }
-  return fail(MC2_ERR_UNSUPPORTED, "allgather_matmul: arrival mode not built yet");
+  // Arrival emulation.  Fork a copy stream off `stream`; on it a copy kernel
+  // moves shard i into gather_out block i in chunks of rows, local block
+  // first, each chunk followed by its ready flag (= this call's epoch).  The
+  // GEMM on `stream` reads A from gather_out, each workgroup once the chunks
+  // its tile covers have arrived.  `stream` then joins the copy stream, so
+  // work enqueued after this call sees the whole gather_out.
+  DeviceState* ds = nullptr;
+  if ((s = arrival_setup(dev, &ds)) != MC2_OK) return s;
+  unsigned epoch = ++ds->epoch;
+  if (epoch == 0) epoch = ++ds->epoch;  // flags start at 0: never wait for 0
+  ArrivalArgs c{};
+  for (int i = 0; i < world_size; i++) c.shards[i] = shards[i];
+  c.gather_out = gather_out;
+  c.flags = ds->flags;
+  c.block_rows = m_local;
+  c.row_bytes = k * 2;
+  c.chunks = (int)(m_local < kArrivalChunks ? m_local : kArrivalChunks);
+  c.chunk_rows = (m_local + c.chunks - 1) / c.chunks;
+  c.chunks = (int)((m_local + c.chunk_rows - 1) / c.chunk_rows);
+  c.r = world_size;
+  c.first = rank_id;
+  c.epoch = epoch;
+  hipError_t e = hipEventRecord(ds->fork, st);
+  if (e == hipSuccess) e = hipStreamWaitEvent(ds->copy_stream, ds->fork, 0);
+  if (e == hipSuccess) e = launch_arrival_copy(c, ds->copy_stream);
+  if (e != hipSuccess) return hip_fail(e, "allgather_matmul arrival copy");
+  for (int i = 0; i < world_size; i++) a.a_parts[i] = shards[i];
+  a.num_parts = world_size;
+  a.gather_out = gather_out;
+  a.ready_flags = ds->flags;
+  a.ready_value = epoch;
+  a.first_part = rank_id;
+  a.chunks = c.chunks;
+  a.chunk_rows = c.chunk_rows;
+  a.status_flag = ds->flags + kFallbackSlot;
+  e = launch_gemm16(a, st);
+  if (e == hipSuccess) e = hipEventRecord(ds->join, ds->copy_stream);
+  if (e == hipSuccess) e = hipStreamWaitEvent(st, ds->join, 0);
+  if (e != hipSuccess) return hip_fail(e, "allgather_matmul arrival launch");
+  return MC2_OK;
+}
+
+mc2_status mc2_allgather_arrival_fallbacks(int reset, unsigned* count) {
+  clear_error();
+  if (!count) return fail(MC2_ERR_NULL, "allgather_arrival_fallbacks: count is NULL");
+  int dev;
+  mc2_status s = current_device(&dev);
+  if (s != MC2_OK) return s;
+  DeviceState* ds = nullptr;
+  if ((s = arrival_setup(dev, &ds)) != MC2_OK) return s;
+  hipError_t e = hipDeviceSynchronize();
+  if (e == hipSuccess) e = hipMemcpy(count, ds->flags + kFallbackSlot, sizeof(unsigned), hipMemcpyDeviceToHost);
+  if (e == hipSuccess && reset) e = hipMemset(ds->flags + kFallbackSlot, 0, sizeof(unsigned));
+  if (e == hipSuccess && reset) e = hipDeviceSynchronize();
+  if (e != hipSuccess) return hip_fail(e, "allgather_arrival_fallbacks");
+  return MC2_OK;
 }
 
 mc2_status mc2_alltoall_quant_matmul_workspace_size(int rank_size, int64_t bs, int64_t h,

@@ -42,7 +42,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm16_kernel(Problem p, void* c)
   __shared__ __attribute__((aligned(1024))) uint8_t s1[lds_stage_array_bytes<BM, BN>()];
   __shared__ __attribute__((aligned(1024))) uint8_t s2[lds_stage_array_bytes<BM, BN>()];
   int tm, tn;
-  tile_of_block(p.m, p.n, BM, BN, p.tile_order_cols, tm, tn);
+  const int first_tile = p.ready ? (int)(p.first_block * p.rows_per_part / BM) : 0;
+  tile_of_block(p.m, p.n, BM, BN, p.tile_order_cols, tm, tn, first_tile);
   const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
   const int tiles_n = (int)((p.n + BN - 1) / BN);
 
@@ -52,7 +53,12 @@ __global__ __launch_bounds__(kThreads, 1) void gemm16_kernel(Problem p, void* c)
 #pragma unroll
     for (int j = 0; j < FN; j++) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  run_mainloop<2, BM, BN, AK, BKM, VEC, Ops16<DT>>(p, m0, n0, tn, tiles_n, s0, s1, s2, acc);
+  if (AK && p.ready) {
+    const Problem q = arrival_problem(p, m0, BM);
+    run_mainloop<2, BM, BN, AK, BKM, VEC, Ops16<DT>>(q, m0, n0, tn, tiles_n, s0, s1, s2, acc);
+  } else {
+    run_mainloop<2, BM, BN, AK, BKM, VEC, Ops16<DT>>(p, m0, n0, tn, tiles_n, s0, s1, s2, acc);
+  }
 
   store_c16<BM, BN, VEC>(reinterpret_cast<uint16_t*>(s0), reinterpret_cast<uint16_t*>(s1), static_cast<uint16_t*>(c),
                          p.m, p.n, m0, n0, [&](int i, int j, int r, int, int) { return Ops16<DT>::cvt(acc[i][j][r]); });
@@ -89,6 +95,16 @@ hipError_t launch_dt(const GemmArgs& g, hipStream_t s) {
   p.m = g.m;
   p.n = g.n;
   p.k = g.k;
+  if (g.ready_flags) {  // arrival emulation: A arrives in gather_out, which the kernel only reads
+    p.ready = g.ready_flags;
+    p.ready_value = g.ready_value;
+    p.fallbacks = g.status_flag;
+    p.arrived = g.gather_out;
+    p.first_block = g.first_part;
+    p.chunks = g.chunks;
+    p.chunk_rows = g.chunk_rows;
+    p.gather_out = nullptr;
+  }
   if (g.a_kmajor && g.b_kmajor) return launch_layout<true, true, DT>(p, g.c, s);
   if (g.a_kmajor && !g.b_kmajor) return launch_layout<true, false, DT>(p, g.c, s);
   if (!g.a_kmajor && !g.b_kmajor) return launch_layout<false, false, DT>(p, g.c, s);
@@ -101,6 +117,9 @@ hipError_t launch_gemm16(const GemmArgs& g, hipStream_t s) {
   if (g.m < 1 || g.n < 1 || g.k < 1 || g.num_parts < 1 || g.num_parts > kMaxRanks) return hipErrorInvalidValue;
   if (g.num_parts * g.rows_per_part != g.m) return hipErrorInvalidValue;
   if (g.gather_out && !g.a_kmajor) return hipErrorInvalidValue;
+  if (g.ready_flags && (!g.gather_out || !g.status_flag || g.first_part < 0 || g.first_part >= g.num_parts ||
+                        g.chunks < 1 || g.chunk_rows < 1 || g.chunks * g.chunk_rows < g.rows_per_part))
+    return hipErrorInvalidValue;
   if (g.dtype == DT_BF16) return launch_dt<DT_BF16>(g, s);
   if (g.dtype == DT_F16) return launch_dt<DT_F16>(g, s);
   return hipErrorInvalidValue;

@@ -74,7 +74,65 @@ struct Problem {
   void* gather_out;       // optional copy of the gathered A
   int64_t m, n, k;
   int tile_order_cols;
+  // Arrival emulation (ready == NULL: off).  Rows of row block i are read
+  // from `arrived` once the flags of their chunks equal ready_value (flag
+  // i * chunks + c: rows [c chunk_rows, (c+1) chunk_rows) of block i); a
+  // workgroup whose wait times out reads its rows from a_parts instead and
+  // counts itself in *fallbacks.
+  const unsigned* ready;
+  unsigned ready_value;
+  unsigned* fallbacks;
+  const void* arrived;
+  int first_block;        // the local block: its tiles are handed out first
+  int chunks;
+  int64_t chunk_rows;
 };
+
+// Longest wait for one row block, in ticks of the 100 MHz real-time counter.
+constexpr uint64_t kArrivalTimeoutTicks = 20000000ull;  // 200 ms
+
+// Waits until *flag == value (raised by the copy kernel once the chunk's
+// bytes are visible device-wide) or the time limit passes.  Returns whether
+// the chunk arrived.  The flag lives in uncached memory, so every poll reads
+// memory; the acquire fence orders the tile's loads after the poll.
+__device__ __forceinline__ bool wait_block(const unsigned* flag, unsigned value) {
+  const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+  for (;;) {
+    if (__hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM) == value) {
+      __atomic_thread_fence(__ATOMIC_ACQUIRE);
+      return true;
+    }
+    if (__builtin_amdgcn_s_memrealtime() - t0 > kArrivalTimeoutTicks) return false;
+    __builtin_amdgcn_s_sleep(4);
+  }
+}
+
+// Arrival prologue of a workgroup whose tile covers rows [m0, m0 + bm): waits
+// for the row blocks of those rows and returns the Problem its main loop
+// reads (A from the arrived buffer, or from the shards after a time-out).
+__device__ __forceinline__ Problem arrival_problem(const Problem& p, int64_t m0, int bm) {
+  __shared__ int s_ok;
+  if (threadIdx.x == 0) {
+    const int64_t end = m0 + bm < p.m ? m0 + bm : p.m;
+    bool ok = true;
+    for (int64_t i = m0 / p.rows_per_part; ok && i <= (end - 1) / p.rows_per_part; i++) {
+      const int64_t base = i * p.rows_per_part;
+      const int64_t lo = (m0 > base ? m0 : base) - base;
+      const int64_t hi = (end < base + p.rows_per_part ? end : base + p.rows_per_part) - base;
+      for (int64_t c = lo / p.chunk_rows; ok && c <= (hi - 1) / p.chunk_rows; c++)
+        ok = wait_block(p.ready + i * p.chunks + c, p.ready_value);
+    }
+    if (!ok) __hip_atomic_fetch_add(p.fallbacks, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    s_ok = ok;
+  }
+  __syncthreads();
+  Problem q = p;
+  if (s_ok) {
+    for (int i = 0; i < kMaxRanks; i++) q.a_parts[i] = p.arrived;
+    q.rows_per_part = p.m;
+  }
+  return q;
+}
 
 // Row pointer of K-contiguous operand row `row` (row blocks of rows_per_part
 // rows live in separate buffers; resolved once per thread, outside the K loop).
@@ -594,8 +652,10 @@ __device__ __forceinline__ void run_mainloop(const Problem& p, int64_t m0, int64
   mainloop_checked<E, BM, BN, AK, BKM, Ops>(p, m0, n0, tn, gather_every, L0, L1, acc);
 }
 
-// Choose the XCD-aware tile of workgroup blockIdx.x.
-__device__ __forceinline__ void tile_of_block(int64_t m, int64_t n, int bm, int bn, int cols_order, int& tm, int& tn) {
+// Choose the XCD-aware tile of workgroup blockIdx.x.  first_row_tile rotates
+// the row tiles so that the tiles holding that row tile come first.
+__device__ __forceinline__ void tile_of_block(int64_t m, int64_t n, int bm, int bn, int cols_order, int& tm, int& tn,
+                                              int first_row_tile = 0) {
   const int tiles_m = (int)((m + bm - 1) / bm), tiles_n = (int)((n + bn - 1) / bn);
   const int tiles = tiles_m * tiles_n;
   int lin = blockIdx.x;
@@ -607,6 +667,7 @@ __device__ __forceinline__ void tile_of_block(int64_t m, int64_t n, int bm, int 
     tm = lin / tiles_n;
     tn = lin % tiles_n;
   }
+  tm = (tm + first_row_tile) % tiles_m;
 }
 
 // Writes a wavefront's rounded 16-bit C fragments to an LDS copy of the C tile

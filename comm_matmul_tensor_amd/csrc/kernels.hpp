@@ -37,13 +37,35 @@ struct GemmArgs {
   int64_t m, n, k;
   int dtype;  // DT_F16 or DT_BF16
   int tile_order_cols;  // set by the launcher: XCD tile order walks columns of tiles
-  // arrival emulation: per-part ready flags (NULL when unused)
+  // arrival emulation (ready_flags NULL when unused): rows of part i of A
+  // are read from gather_out once the flags of their chunks equal
+  // ready_value (flag i * chunks + c covers rows [c chunk_rows, (c+1)
+  // chunk_rows) of part i); the tiles of part first_part come first;
+  // *status_flag counts workgroups whose wait timed out (they read the part
+  // from a_parts instead)
   const unsigned* ready_flags;
   unsigned ready_value;
   int first_part;
-  unsigned* status_flag;  // set non-zero if a wait timed out
+  int chunks;
+  int64_t chunk_rows;
+  unsigned* status_flag;
 };
 hipError_t launch_gemm16(const GemmArgs& a, hipStream_t s);
+
+// ---- arrival emulation: copy of the shards into gather_out, chunk by chunk,
+// each chunk followed by its ready flag (flags[b * chunks + c] = epoch)
+struct ArrivalArgs {
+  const void* shards[kMaxRanks];
+  void* gather_out;
+  unsigned* flags;
+  int64_t block_rows;  // rows per shard
+  int64_t row_bytes;   // bytes per row
+  int64_t chunk_rows;  // rows per chunk
+  int chunks;          // chunks per shard
+  int r, first;        // shard count; the block copied first
+  unsigned epoch;
+};
+hipError_t launch_arrival_copy(const ArrivalArgs& a, hipStream_t s);
 
 // ---- K2: permute + smooth + per-token dynamic int8 quantisation
 struct QuantArgs {

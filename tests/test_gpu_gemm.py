@@ -139,3 +139,68 @@ def test_backward_full_config_sampled(mc2):
     rw = np.unique(np.concatenate([[0, 1791], rng.choice(1792, 30, replace=False)]))
     want = oracle.matmul(np.ascontiguousarray(t["dy"][:, rw]), t["ag_x"], "bf16", a_trans=True)
     assert_close16(dw[rw], want, "bf16", "dW rows")
+
+
+# ---------------------------------------------------------------- arrival emulation (MC2_AG_ARRIVAL)
+def _arrival_case(mc2, r, m_l, k, n, dtype, rank_id, seed, x2_trans=False):
+    import torch
+    specs = mc2_inputs.configs.scaled("ag", r=r, m_local=m_l, k=k, n=n, dtype=dtype, x2_std=0.05)
+    t = mc2_inputs.make(specs, seed=seed)
+    T = mc2_inputs.to_torch
+    shards_np = [t[f"shard{i}"] for i in range(r)]
+    x2_np = np.ascontiguousarray(t["x2"].T) if x2_trans else t["x2"]
+    shards = [T(s, dtype) for s in shards_np]
+    x2 = T(x2_np, dtype)
+    fused, _ = mc2.mc2_allgather_matmul(shards, x2, x2_trans=x2_trans)
+    g = torch.full((r * m_l, k), float("nan"), dtype=shards[0].dtype, device="cuda")
+    out, _ = mc2.mc2_allgather_matmul(shards, x2, x2_trans=x2_trans, gather_out=g, mode=mc2.MC2_AG_ARRIVAL,
+                                      rank_id=rank_id)
+    torch.cuda.synchronize()
+    return shards_np, x2_np, mc2_inputs.from_torch(fused), mc2_inputs.from_torch(out), mc2_inputs.from_torch(g)
+
+
+@pytest.mark.parametrize("r,m_l,k,n,rank_id", [
+    (2, 1, 256, 1, 1), (4, 16, 512, 64, 2), (8, 5, 1000, 130, 7), (4, 100, 264, 200, 0),
+    (8, 33, 768, 257, 3), (2, 129, 256, 129, 1), (8, 128, 512, 224, 5)])
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_ag_arrival_shapes(mc2, r, m_l, k, n, rank_id, dtype):
+    """Arrival mode reads the copied gather_out: same bits as the fused mode, gather_out exact."""
+    print(f"arrival r={r} m_l={m_l} k={k} n={n} rank={rank_id} {dtype}", flush=True)
+    mc2.mc2_allgather_arrival_fallbacks(reset=True)
+    shards, x2, fused, out, g = _arrival_case(mc2, r, m_l, k, n, dtype, rank_id, seed=7000 + r * 100 + m_l)
+    want, want_g = oracle.allgather_matmul(shards, x2, dtype)
+    assert_bits_equal(g, want_g, "gather_out")
+    assert_bits_equal(out, fused, "arrival vs fused")
+    assert_close16(out, want, dtype, "out")
+    assert mc2.mc2_allgather_arrival_fallbacks() == 0
+
+
+def test_ag_arrival_repeated_calls(mc2):
+    """Consecutive arrival calls on new data: every call waits for its own copies."""
+    import torch
+    mc2.mc2_allgather_arrival_fallbacks(reset=True)
+    for it in range(3):
+        shards, x2, fused, out, g = _arrival_case(mc2, 4, 64, 512, 96, "bf16", rank_id=it % 4, seed=7500 + it,
+                                                  x2_trans=bool(it % 2))
+        want, want_g = oracle.allgather_matmul(shards, x2, "bf16", x2_trans=bool(it % 2))
+        assert_bits_equal(g, want_g, f"gather_out call {it}")
+        assert_bits_equal(out, fused, f"arrival vs fused call {it}")
+    assert mc2.mc2_allgather_arrival_fallbacks() == 0
+
+
+def test_ag_arrival_full_config(mc2):
+    """8 x bf16 (512, 4096) @ (4096, 1792) in arrival mode: bit-identical to the fused mode."""
+    import torch
+    seed, d, specs = mc2_inputs.CONFIGS["ag_bf16_tp"]
+    t = mc2_inputs.make("ag_bf16_tp")
+    T = mc2_inputs.to_torch
+    shards = [T(t[f"shard{i}"], "bf16") for i in range(d["r"])]
+    x2 = T(t["x2"], "bf16")
+    mc2.mc2_allgather_arrival_fallbacks(reset=True)
+    fused, _ = mc2.mc2_allgather_matmul(shards, x2)
+    out, g = mc2.mc2_allgather_matmul(shards, x2, mode=mc2.MC2_AG_ARRIVAL, rank_id=3)
+    torch.cuda.synchronize()
+    G = np.concatenate([t[f"shard{i}"] for i in range(d["r"])])
+    assert_bits_equal(mc2_inputs.from_torch(g), G, "gather_out")
+    assert_bits_equal(mc2_inputs.from_torch(out), mc2_inputs.from_torch(fused), "arrival vs fused")
+    assert mc2.mc2_allgather_arrival_fallbacks() == 0
