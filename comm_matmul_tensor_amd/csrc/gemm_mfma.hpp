@@ -401,10 +401,13 @@ struct DmaOperand {
     step_bytes = (int64_t)(kRowBytes / E) * ld_bytes;
   }
   __device__ __forceinline__ void issue(uint8_t* tile, int64_t off) const {
-    const int w = threadIdx.x / 64;
 #pragma unroll
-    for (int i = 0; i < kN; i++)
-      __builtin_amdgcn_global_load_lds((gptr_t)(src[i] + off), (lptr_t)(tile + 4096 * i + 1024 * w), 16, 0, 0);
+    for (int i = 0; i < kN; i++) issue_one(tile, off, i);
+  }
+  // Instruction i alone.
+  __device__ __forceinline__ void issue_one(uint8_t* tile, int64_t off, int i) const {
+    const int w = threadIdx.x / 64;
+    __builtin_amdgcn_global_load_lds((gptr_t)(src[i] + off), (lptr_t)(tile + 4096 * i + 1024 * w), 16, 0, 0);
   }
 };
 
@@ -446,29 +449,25 @@ struct FragReader {
   }
   // The swizzles depend only on bits of k that kk and the second read leave unchanged.
   __device__ __forceinline__ void read(const uint8_t* tile, int kk, u32x4 (&f)[NF]) const {
+#pragma unroll
+    for (int j = 0; j < NF; j++) f[j] = read_one(tile, kk, j);
+  }
+  // Fragment j alone (one LDS read for a K-major tile, two for an MN-major one).
+  __device__ __forceinline__ u32x4 read_one(const uint8_t* tile, int kk, int j) const {
     constexpr int P = R * E;  // bytes per k row of an MN-major tile
-    int o[kOffs];
-#pragma unroll
-    for (int j = 0; j < kOffs; j++) {
-      o[j] = off[j];
-      asm volatile("" : "+v"(o[j]));  // keep the stage base additions inside the loop
-    }
-#pragma unroll
-    for (int j = 0; j < NF; j++) {
-      if constexpr (KMAJ) {
-        f[j] = *reinterpret_cast<const u32x4*>(tile + o[kk] + 16 * kRowBytes * j);
-      } else if constexpr (E == 2) {
-        const uint8_t* q = tile + o[j] + 32 * kk * P;
-        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)q);
-        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(q + 4 * P));
-        const u32x2 a = __builtin_bit_cast(u32x2, lo), b = __builtin_bit_cast(u32x2, hi);
-        f[j] = u32x4{a[0], a[1], b[0], b[1]};
-      } else {
-        const uint8_t* q = tile + o[j] + 64 * kk * P;
-        const i32x2 lo = __builtin_amdgcn_ds_read_tr8_b64_v2i32((__attribute__((address_space(3))) i32x2*)q);
-        const i32x2 hi = __builtin_amdgcn_ds_read_tr8_b64_v2i32((__attribute__((address_space(3))) i32x2*)(q + 8 * P));
-        f[j] = u32x4{(uint32_t)lo[0], (uint32_t)lo[1], (uint32_t)hi[0], (uint32_t)hi[1]};
-      }
+    if constexpr (KMAJ) {
+      return *reinterpret_cast<const u32x4*>(tile + off[kk] + 16 * kRowBytes * j);
+    } else if constexpr (E == 2) {
+      const uint8_t* q = tile + off[j] + 32 * kk * P;
+      const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)q);
+      const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(q + 4 * P));
+      const u32x2 a = __builtin_bit_cast(u32x2, lo), b = __builtin_bit_cast(u32x2, hi);
+      return u32x4{a[0], a[1], b[0], b[1]};
+    } else {
+      const uint8_t* q = tile + off[j] + 64 * kk * P;
+      const i32x2 lo = __builtin_amdgcn_ds_read_tr8_b64_v2i32((__attribute__((address_space(3))) i32x2*)q);
+      const i32x2 hi = __builtin_amdgcn_ds_read_tr8_b64_v2i32((__attribute__((address_space(3))) i32x2*)(q + 8 * P));
+      return u32x4{(uint32_t)lo[0], (uint32_t)lo[1], (uint32_t)hi[0], (uint32_t)hi[1]};
     }
   }
 };
@@ -494,7 +493,6 @@ __device__ __forceinline__ void mainloop_fast(const Problem& p, int64_t m0, int6
   using DA = DmaOperand<E, BM, AK>;
   using DB = DmaOperand<E, BN, BKM>;
   constexpr int ND = DA::kN + DB::kN;  // DMA instructions per thread and step
-  constexpr int NG = BM / 32;          // gather_out stores per thread
   DA da;
   DB db;
   if constexpr (AK) da.init_k(p.a_parts, p.rows_per_part, p.k * E, m0, p.m);
@@ -512,45 +510,67 @@ __device__ __forceinline__ void mainloop_fast(const Problem& p, int64_t m0, int6
   rb.init(wn * WN);
   const int nk = (int)(p.k / BK);
   int next_gather = gather_phase;
-  const bool m_inside = m0 + BM <= p.m;
 
   u32x4 fa0[FM], fb0[FN], fa1[FM], fb1[FN];
   auto dma = [&](uint8_t* L, int kt) {
     da.issue(L, kt * da.step_bytes);
     db.issue(L + kATile, kt * db.step_bytes);
   };
-  auto mma = [&](const u32x4(&fa)[FM], const u32x4(&fb)[FN]) {
+  // One K half: the FM x FN MFMAs on (fa, fb), with DMA instructions
+  // [d0, d1) of step kt_dma (when dma_on) and the FM + FN fragment reads of
+  // half kk of stage rd (when rd_on) spread evenly between them, in an order
+  // the scheduler keeps (sched_barrier after every slot).  With one wavefront
+  // per SIMD a burst of loads backs up the load path and stalls the
+  // wavefront's MFMA issue; a few loads and reads between consecutive MFMAs
+  // keep the matrix pipe fed.
+  auto half = [&](const u32x4(&fa)[FM], const u32x4(&fb)[FN], auto D0_, auto D1_, bool dma_on, uint8_t* L,
+                  int kt_dma, bool rd_on, const uint8_t* rd, int kk, u32x4(&ra_out)[FM], u32x4(&rb_out)[FN]) {
+    constexpr int D0 = decltype(D0_)::value, D1 = decltype(D1_)::value;
+    constexpr int NM = FM * FN, NF = FM + FN, NDH = D1 - D0;
+    const int64_t offa = (int64_t)kt_dma * da.step_bytes, offb = (int64_t)kt_dma * db.step_bytes;
 #pragma unroll
-    for (int i = 0; i < FM; i++)
+    for (int q = 0; q < NM; q++) {
+      acc[q / FN][q % FN] = Ops::mfma(fa[q / FN], fb[q % FN], acc[q / FN][q % FN]);
 #pragma unroll
-      for (int j = 0; j < FN; j++) acc[i][j] = Ops::mfma(fa[i], fb[j], acc[i][j]);
+      for (int d = 0; d < NDH; d++)
+        if ((d * NM) / NDH == q && dma_on) {
+          if (D0 + d < DA::kN) da.issue_one(L, offa, D0 + d);
+          else db.issue_one(L + kATile, offb, D0 + d - DA::kN);
+        }
+#pragma unroll
+      for (int f = 0; f < NF; f++)
+        if ((f * NM) / NF == q && rd_on) {
+          if (f < FM) ra_out[f] = ra.read_one(rd, kk, f);
+          else rb_out[f - FM] = rb.read_one(rd + kATile, kk, f - FM);
+        }
+      __builtin_amdgcn_sched_barrier(0);
+    }
   };
+  using C0 = std::integral_constant<int, 0>;
+  using CD = std::integral_constant<int, ND>;
   // FULL: steps kt+1 and kt+2 exist (no branches around the DMA and the reads).
   auto step = [&](int kt, auto FULL_, uint8_t* cur, uint8_t* nxt, uint8_t* nn) {
     constexpr bool FULL = decltype(FULL_)::value;
     const bool dma2 = FULL || kt + 2 < nk;
-    if (dma2) dma(nn, kt + 2);
-    // gather_out copy of this step's A tile: NG stores per thread when the
-    // tile lies inside M (fewer at the edge, where the wait below is a full one)
-    bool gathered = false;
+    // gather_out copy of this step's A tile (NG stores per thread, older than
+    // every load issued below, so the wait below covers them)
     if (GATHER && kt == next_gather) {
       copy_gather<E, BM>(cur, p.gather_out, p.m, p.k, m0, (int64_t)kt * BK);
       next_gather += gather_every;
-      gathered = true;
     }
-    ra.read(cur, 1, fa1);
-    rb.read(cur + kATile, 1, fb1);
-    mma(fa0, fb0);
-    // the DMA of step kt+1 has landed; only younger ones and gather stores may fly
-    if (dma2 && !(GATHER && gathered)) wait_vmcnt<ND>();
-    else if (dma2 && m_inside) wait_vmcnt<ND + NG>();
+    __builtin_amdgcn_sched_barrier(0);
+    // half 0 of step kt; the DMA of step kt+2 (its stage was last read
+    // before the previous barrier); reads of half 1 of step kt
+    half(fa0, fb0, C0(), CD(), dma2, nn, kt + 2, true, cur, 1, fa1, fb1);
+    // the DMA of step kt+1 (issued during step kt-1) has landed; only this
+    // step's may still fly
+    if (dma2) wait_vmcnt<ND>();
     else wait_vmcnt<0>();
     lds_barrier();
-    if (FULL || kt + 1 < nk) {
-      ra.read(nxt, 0, fa0);
-      rb.read(nxt + kATile, 0, fb0);
-    }
-    mma(fa1, fb1);
+    __builtin_amdgcn_sched_barrier(0);
+    // half 1 of step kt; reads of half 0 of step kt+1
+    half(fa1, fb1, C0(), C0(), false, nn, kt + 2, FULL || kt + 1 < nk, nxt, 0, fa0, fb0);
+    __builtin_amdgcn_sched_barrier(0);
   };
 
   dma(L0, 0);
