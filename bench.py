@@ -4,6 +4,8 @@ One step runs every operator once on its full-size synthetic workload, in
 this order (names as in the JSON "rows"):
 
   ag_bf16_tp   AllGatherMatmul, 8 x bf16 (512, 4096) shards @ (4096, 1792), + gather_out
+  ag_arrival   the same in arrival-emulation mode: a side-stream copy kernel lands the
+               shards in gather_out chunk by chunk and the GEMM waits per chunk
   colpar_dx    column-parallel backward dX = dY (8192, 1792) @ W (1792, 4096)
   colpar_dw    column-parallel backward dW = dY^T (1792, 8192) @ AG(X) (8192, 4096)
   a16w8        AlltoAllQuantMatmul A16W8: permute+quant of bf16 (8192, 4096) on 8 ranks,
@@ -12,7 +14,10 @@ this order (names as in the JSON "rows"):
   qar_mx       QuantAllReduce, 8 ranks x E4M3FN (4, 2048, 7168) + E8M0 mx scales -> bf16
 
 Inputs are generated on the host, copied to HBM before timing, and stay
-resident.  W warm-up steps, then exactly K timed steps between two
+resident.  --copy-calib adds a plain 256 MiB device copy to every step (the
+reference kernel for scaling FETCH_SIZE / WRITE_SIZE counters to bytes);
+--summarize DIR turns a directory of rocprofv3 CSV output into the summary
+kept under profiles/.  W warm-up steps, then exactly K timed steps between two
 synchronisations.  Per-kernel durations come from HIP events recorded on the
 stream the kernels run on (torch's current stream, which libmc2 is handed).
 The headline value is the AllGatherMatmul's TFLOP/s; every row's figure and
@@ -35,7 +40,14 @@ PEAK_BF16 = 2500.0     # TFLOP/s, dense MFMA, MI355X
 PEAK_INT8 = 5000.0     # TOP/s, dense MFMA, MI355X
 PEAK_HBM = 8000.0      # GB/s, MI355X HBM3E
 
-ALL_ROWS = ["ag_bf16_tp", "colpar_dx", "colpar_dw", "a16w8", "qar_int8", "qar_mx"]
+ALL_ROWS = ["ag_bf16_tp", "ag_arrival", "colpar_dx", "colpar_dw", "a16w8", "qar_int8", "qar_mx"]
+EXTRA_ROWS = ["copy_calib"]
+COPY_CALIB_BYTES = 256 << 20
+
+# Kernel sources whose hash keys the stored traffic counters of the dominant kernel.
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_gemm_bf16_ag.json")
+TRAFFIC_SOURCES = ["comm_matmul_tensor_amd/csrc/gemm_mfma.hpp", "comm_matmul_tensor_amd/csrc/gemm_bf16.hip",
+                   "comm_matmul_tensor_amd/csrc/device.hpp", "comm_matmul_tensor_amd/csrc/kernels.hpp"]
 
 
 def log(msg):
@@ -51,6 +63,10 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-parity", action="store_true", help="skip the sampled oracle check")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target oracle work for the CPU baseline")
+    ap.add_argument("--copy-calib", action="store_true", help="add a plain 256 MiB device copy to every step")
+    ap.add_argument("--summarize", metavar="DIR", help="summarise rocprofv3 CSV output in DIR and exit")
+    ap.add_argument("--write-traffic", action="store_true",
+                    help="with --summarize: store the dominant kernel's scaled traffic for later bench lines")
     return ap.parse_args()
 
 
@@ -82,6 +98,22 @@ def setup_rows(names, mc2, torch):
                     mc2.mc2_allgather_matmul(shards, x2, out=out, gather_out=g))])
         row.bytes = 2 * (m * k + k * n + m * n + m * k)
         row.check = lambda t=t, d=d, out=out, g=g: check_ag(t, d, out, g)
+        rows[row.name] = row
+    if "ag_arrival" in names:
+        seed, d, specs = mc2_inputs.CONFIGS["ag_bf16_tp"]
+        t = mc2_inputs.make("ag_bf16_tp")
+        shards = [T(t[f"shard{i}"], "bf16") for i in range(d["r"])]
+        x2 = T(t["x2"], "bf16")
+        m, k, n = d["r"] * d["m_local"], d["k"], d["n"]
+        out = torch.empty((m, n), dtype=torch.bfloat16, device="cuda")
+        g = torch.empty((m, k), dtype=torch.bfloat16, device="cuda")
+        row = Row("ag_arrival", "TFLOP/s", "mfma", PEAK_BF16, 2.0 * m * n * k,
+                  [("arrive_copy+gemm_bf16", lambda shards=shards, x2=x2, out=out, g=g:
+                    mc2.mc2_allgather_matmul(shards, x2, out=out, gather_out=g, mode=mc2.MC2_AG_ARRIVAL,
+                                             rank_id=0))])
+        row.bytes = 2 * (m * k + k * n + m * n + m * k)
+        row.check = lambda t=t, d=d, out=out, g=g, mc2=mc2: (check_ag(t, d, out, g) and
+                                                            mc2.mc2_allgather_arrival_fallbacks() == 0)
         rows[row.name] = row
     if "colpar_dx" in names or "colpar_dw" in names:
         seed, d, specs = mc2_inputs.CONFIGS["colpar_bwd"]
@@ -134,7 +166,15 @@ def setup_rows(names, mc2, torch):
         row.bytes = nbytes
         row.check = (lambda t=t, d=d, out=out, xdt=xdt, sdt=sdt: check_qar(t, d, out, xdt, sdt))
         rows[name] = row
-    return [rows[n] for n in ALL_ROWS if n in rows]
+    if "copy_calib" in names:
+        src = torch.empty(COPY_CALIB_BYTES, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        row = Row("copy_calib", "GB/s", "hbm", PEAK_HBM, 2.0 * COPY_CALIB_BYTES,
+                  [("copy", lambda src=src, dst=dst: dst.copy_(src))])
+        row.bytes = 2 * COPY_CALIB_BYTES
+        row.check = lambda src=src, dst=dst: bool(torch.equal(src, dst))
+        rows[row.name] = row
+    return [rows[n] for n in ALL_ROWS + EXTRA_ROWS if n in rows]
 
 
 # ---------------------------------------------------------------- sampled parity against the oracle
@@ -250,8 +290,98 @@ def cpu_baseline(target_s):
                       f"the {r} bf16 shards, k={k}, n={n}, run {reps} time(s): {total:.1f} s wall"}
 
 
+# ---------------------------------------------------------------- profile summaries and stored traffic
+def _source_hash():
+    import hashlib
+    h = hashlib.sha256()
+    for rel in TRAFFIC_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def _short(name):
+    name = name.replace("(anonymous namespace)::", "").replace("void mc2::", "")
+    return name.split("(")[0]
+
+
+def summarize(d, write_traffic):
+    """Markdown summary of rocprofv3 CSV output under d: kernel-trace stats
+    (*kernel_stats.csv) and per-dispatch counters (*counter_collection.csv in
+    sub-directories named after the counter).  FETCH_SIZE and WRITE_SIZE are
+    scaled by the ratio of the copy kernel's known bytes to what the same
+    counter reads for it."""
+    import csv
+    import glob
+    from collections import defaultdict
+    lines = []
+    for f in sorted(glob.glob(os.path.join(d, "**", "*kernel_stats.csv"), recursive=True)):
+        lines.append(f"Kernel trace ({os.path.relpath(f, d)}):\n")
+        lines.append("| kernel | calls | avg us | min us | max us |")
+        lines.append("|---|---|---|---|---|")
+        for r in csv.DictReader(open(f)):
+            lines.append(f"| {_short(r['Name'])} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+                         f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} |")
+        lines.append("")
+    counters = defaultdict(lambda: defaultdict(list))
+    for f in sorted(glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)):
+        for r in csv.DictReader(open(f)):
+            counters[_short(r["Kernel_Name"])][r["Counter_Name"]].append(float(r["Counter_Value"]))
+    scale = {}
+    copy_names = [k for k in counters if "copy" in k.lower() or "elementwise_kernel" in k]
+    for c in ("FETCH_SIZE", "WRITE_SIZE"):
+        vals = [v for k in copy_names for v in counters[k].get(c, []) if v * 1024 > COPY_CALIB_BYTES / 2]
+        if vals:
+            scale[c] = COPY_CALIB_BYTES / (1024.0 * sum(vals) / len(vals))
+    if counters:
+        names = sorted({c for k in counters for c in counters[k]})
+        lines.append("Counters, average per dispatch (FETCH_SIZE / WRITE_SIZE in KiB as read, and in MB after "
+                     "scaling by the 256 MiB copy):\n")
+        lines.append("| kernel | dispatches | " + " | ".join(names) + " | fetch MB (scaled) | write MB (scaled) |")
+        lines.append("|---|---|" + "---|" * len(names) + "---|---|")
+        for k, cs in sorted(counters.items()):
+            avg = {c: sum(v) / len(v) for c, v in cs.items()}
+            n = max(len(v) for v in cs.values())
+            fm = avg.get("FETCH_SIZE", 0) * 1024 * scale.get("FETCH_SIZE", 1.0) / 1e6
+            wm = avg.get("WRITE_SIZE", 0) * 1024 * scale.get("WRITE_SIZE", 1.0) / 1e6
+            lines.append(f"| {k} | {n} | " + " | ".join(f"{avg.get(c, 0):.0f}" for c in names) +
+                         f" | {fm:.1f} | {wm:.1f} |")
+        lines.append("")
+        lines.append("Copy-kernel scale factors (known bytes / counted bytes): " +
+                     ", ".join(f"{c} {v:.4f}" for c, v in scale.items()) + "\n")
+    print("\n".join(lines))
+    if write_traffic:
+        ag = [k for k in counters if k.startswith("gemm16_kernel<128, 224, true, false, true, 2>")]
+        if not ag or not all(c in counters[ag[0]] for c in ("FETCH_SIZE", "WRITE_SIZE")):
+            raise SystemExit("no FETCH_SIZE / WRITE_SIZE for the AllGatherMatmul kernel in " + d)
+        cs = counters[ag[0]]
+        fetch = sum(cs["FETCH_SIZE"]) / len(cs["FETCH_SIZE"]) * 1024 * scale.get("FETCH_SIZE", 1.0)
+        write = sum(cs["WRITE_SIZE"]) / len(cs["WRITE_SIZE"]) * 1024 * scale.get("WRITE_SIZE", 1.0)
+        rec = {"kernel": ag[0], "source_hash": _source_hash(), "fetch_bytes": round(fetch),
+               "write_bytes": round(write), "scale": scale}
+        with open(TRAFFIC_FILE, "w") as f:
+            json.dump(rec, f, indent=1)
+            f.write("\n")
+        print(f"wrote {TRAFFIC_FILE}: {rec}")
+
+
+def stored_traffic():
+    """HBM bytes per launch of the AllGatherMatmul kernel from the stored
+    counters, or None if they are missing or the kernel changed since."""
+    try:
+        rec = json.load(open(TRAFFIC_FILE))
+    except (OSError, ValueError):
+        return None
+    if rec.get("source_hash") != _source_hash():
+        return None
+    return int(rec["fetch_bytes"]) + int(rec["write_bytes"])
+
+
 def main():
     args = parse()
+    if args.summarize:
+        summarize(args.summarize, args.write_traffic)
+        return
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on exactly one GPU; --gpus above 1 is not supported "
                                    "(the r ranks are simulated as r buffers on one device)"}))
@@ -262,8 +392,10 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
     names = [s for s in args.rows.split(",") if s]
+    if args.copy_calib:
+        names.append("copy_calib")
     for s in names:
-        if s not in ALL_ROWS:
+        if s not in ALL_ROWS + EXTRA_ROWS:
             raise SystemExit(f"unknown row {s}")
     t0 = time.time()
     rows = setup_rows(names, mc2, torch)
@@ -324,7 +456,8 @@ def main():
                    "rows_in_step": [r.name for r in rows], "seeds": "workload number (1..5)"},
         "roofline": {"bound": h["bound"], "achieved": h["achieved"], "peak": h["peak"],
                      "unit": "TFLOP/s" if h["unit"] == "TFLOP/s" else h["unit"], "frac": h["frac"],
-                     "traffic": None, "kernel": h["kernels"][0]},
+                     "traffic": stored_traffic() if head == "ag_bf16_tp" else None,
+                     "kernel": h["kernels"][0]},
         "rows": out_rows,
     }
     if not args.no_cpu_baseline:

@@ -60,12 +60,12 @@ mc2_status current_device(int* dev_out) {
 
 int dt(mc2_dtype d) { return static_cast<int>(d); }
 
-// Arrival flags: kMaxRanks blocks x kArrivalChunks chunks, then the count of
-// timed-out waits.
-constexpr int kArrivalChunks = 16;
-constexpr int kFallbackSlot = kMaxRanks * kArrivalChunks;
-constexpr size_t kFlagBytes = 4096;
-static_assert((kFallbackSlot + 1) * sizeof(unsigned) <= kFlagBytes, "flag buffer");
+// Arrival flags: up to kArrivalFlags (row chunk, slab) pieces, then the
+// count of timed-out waits.
+constexpr int64_t kArrivalSlabs = 16;
+constexpr int64_t kArrivalFlags = 65535;
+constexpr int kFallbackSlot = (int)kArrivalFlags;
+constexpr size_t kFlagBytes = (kArrivalFlags + 1) * sizeof(unsigned);
 
 // Creates the arrival-emulation resources of device `dev` once.  The flags
 // sit in uncached device memory so that the GEMM's polls read memory, not a
@@ -218,26 +218,36 @@ mc2_status mc2_allgather_matmul(const void* const* shards, int world_size, int64
     return MC2_OK;
   }
   // Arrival emulation.  Fork a copy stream off `stream`; on it a copy kernel
-  // moves shard i into gather_out block i in chunks of rows, local block
-  // first, each chunk followed by its ready flag (= this call's epoch).  The
-  // GEMM on `stream` reads A from gather_out, each workgroup once the chunks
-  // its tile covers have arrived.  `stream` then joins the copy stream, so
-  // work enqueued after this call sees the whole gather_out.
+  // fills gather_out piece by piece (row chunks of the GEMM's tile height or
+  // a multiple of it, times up to 16 slabs of K), local rank's rows first,
+  // each piece followed by its ready flag (= this call's epoch).  The GEMM on
+  // `stream` reads A from gather_out and issues the loads of each slab of K
+  // once its piece has arrived.  `stream` then joins the copy stream, so work
+  // enqueued after this call sees the whole gather_out.
   DeviceState* ds = nullptr;
   if ((s = arrival_setup(dev, &ds)) != MC2_OK) return s;
   unsigned epoch = ++ds->epoch;
   if (epoch == 0) epoch = ++ds->epoch;  // flags start at 0: never wait for 0
+  const int64_t m = a.m;
+  int64_t slabs = (k + 63) / 64 < kArrivalSlabs ? (k + 63) / 64 : kArrivalSlabs;
+  const int64_t slab_cols = ((k + slabs - 1) / slabs + 63) / 64 * 64;
+  slabs = (k + slab_cols - 1) / slab_cols;
+  int64_t rows_chunk = gemm16_tile_rows(m, n);
+  while (((m + rows_chunk - 1) / rows_chunk) * slabs > kArrivalFlags) rows_chunk *= 2;
+  const int64_t chunks = (m + rows_chunk - 1) / rows_chunk;
+  const int64_t first_chunk = (int64_t)rank_id * m_local / rows_chunk;
   ArrivalArgs c{};
   for (int i = 0; i < world_size; i++) c.shards[i] = shards[i];
   c.gather_out = gather_out;
   c.flags = ds->flags;
   c.block_rows = m_local;
-  c.row_bytes = k * 2;
-  c.chunks = (int)(m_local < kArrivalChunks ? m_local : kArrivalChunks);
-  c.chunk_rows = (m_local + c.chunks - 1) / c.chunks;
-  c.chunks = (int)((m_local + c.chunk_rows - 1) / c.chunk_rows);
+  c.k = k;
+  c.rows_chunk = rows_chunk;
+  c.slab_cols = slab_cols;
+  c.slabs = (int)slabs;
+  c.chunks = (int)chunks;
   c.r = world_size;
-  c.first = rank_id;
+  c.first_chunk = (int)first_chunk;
   c.epoch = epoch;
   hipError_t e = hipEventRecord(ds->fork, st);
   if (e == hipSuccess) e = hipStreamWaitEvent(ds->copy_stream, ds->fork, 0);
@@ -248,9 +258,10 @@ mc2_status mc2_allgather_matmul(const void* const* shards, int world_size, int64
   a.gather_out = gather_out;
   a.ready_flags = ds->flags;
   a.ready_value = epoch;
-  a.first_part = rank_id;
-  a.chunks = c.chunks;
-  a.chunk_rows = c.chunk_rows;
+  a.rows_chunk = rows_chunk;
+  a.slab_cols = slab_cols;
+  a.slabs = (int)slabs;
+  a.first_row_tile = (int)(first_chunk * rows_chunk / gemm16_tile_rows(m, n));
   a.status_flag = ds->flags + kFallbackSlot;
   e = launch_gemm16(a, st);
   if (e == hipSuccess) e = hipEventRecord(ds->join, ds->copy_stream);

@@ -2,13 +2,18 @@
 // page, "function": communication and matmul run as a pipeline).
 //
 // On one GPU the peers' shards are already in HBM, so their "arrival" is
-// modelled by a copy kernel on a side stream: shard i is copied into row
-// block i of gather_out in chunks of rows, and each chunk raises its own
-// ready flag once its bytes are visible to every XCD.  The GEMM's workgroups
-// poll the flags of the chunks their tile covers (gemm_mfma.hpp), so tiles
-// start as their rows land.  Workgroups are handed out local block first,
-// then the other blocks in rank order after it, as a ring AllGather delivers
-// them.
+// modelled by a copy kernel on a side stream that fills gather_out piece by
+// piece: the gathered rows are cut into row chunks (a multiple of the GEMM's
+// tile height) and K into slabs.  One workgroup copies one piece (row chunk
+// g, slab s) and then raises that piece's flag.  Workgroups are handed out
+// slab by slab, and within a slab from the local rank's rows on (as a ring
+// AllGather delivers them), so the GEMM's tiles can start on the first slab
+// of K while later slabs are still being copied.
+//
+// Visibility across XCDs: the copy's stores are device-scope atomic stores,
+// which write through the XCD's L2, so the release fence before the flag has
+// no dirty lines of the piece to write back (a fence that had to write back
+// a whole piece made the copy several times slower).
 #include "device.hpp"
 #include "kernels.hpp"
 
@@ -16,50 +21,84 @@ namespace mc2 {
 namespace {
 
 constexpr int kCopyThreads = 256;
+constexpr int kBatch = 16;  // 16-byte loads in flight per thread
 
 __global__ __launch_bounds__(kCopyThreads) void arrive_kernel(ArrivalArgs a) {
-  const int w = blockIdx.x;
-  const int blk = (a.first + w / a.chunks) % a.r, c = w % a.chunks;
-  const int64_t row0 = (int64_t)c * a.chunk_rows;
-  const int64_t rows = (row0 + a.chunk_rows <= a.block_rows ? a.chunk_rows : a.block_rows - row0);
-  const int64_t bytes = rows * a.row_bytes;
-  const uint8_t* src = static_cast<const uint8_t*>(a.shards[blk]) + row0 * a.row_bytes;
-  uint8_t* dst = static_cast<uint8_t*>(a.gather_out) + ((int64_t)blk * a.block_rows + row0) * a.row_bytes;
-  if (bytes > 0) {
-    if ((((uintptr_t)src | (uintptr_t)dst | (uintptr_t)bytes) & 15) == 0) {
-      const u32x4* s = reinterpret_cast<const u32x4*>(src);
-      u32x4* d = reinterpret_cast<u32x4*>(dst);
-      const int64_t n = bytes / 16;
-      int64_t i = threadIdx.x;
-      for (; i + 3 * kCopyThreads < n; i += 4 * kCopyThreads) {
-        const u32x4 v0 = s[i], v1 = s[i + kCopyThreads], v2 = s[i + 2 * kCopyThreads], v3 = s[i + 3 * kCopyThreads];
-        d[i] = v0;
-        d[i + kCopyThreads] = v1;
-        d[i + 2 * kCopyThreads] = v2;
-        d[i + 3 * kCopyThreads] = v3;
+  // piece w: slab w / chunks of row chunk (first_chunk + w % chunks) % chunks
+  const int w = (int)blockIdx.x;
+  const int sl = w / a.chunks, g = (a.first_chunk + w % a.chunks) % a.chunks;
+  const int64_t m = (int64_t)a.r * a.block_rows;
+  const int64_t row0 = (int64_t)g * a.rows_chunk;
+  const int64_t rows = row0 + a.rows_chunk <= m ? a.rows_chunk : m - row0;
+  const int64_t c0 = (int64_t)sl * a.slab_cols;
+  const int64_t cols = c0 + a.slab_cols <= a.k ? a.slab_cols : a.k - c0;
+  uint16_t* gout = static_cast<uint16_t*>(a.gather_out);
+  // one shard holds the whole chunk unless the chunk straddles a shard edge
+  const int64_t b0 = row0 / a.block_rows;
+  const bool one_shard = (row0 + rows - 1) / a.block_rows == b0;
+  if ((a.k % 8 == 0) && (a.slab_cols % 8 == 0)) {
+    // 16-byte pieces in row-major order; thread t takes pieces t, t + 256, ...
+    // and steps its (row, piece) position without dividing.  kBatch loads per
+    // thread are issued before their stores.
+    const int per_row = (int)(cols / 8), n = (int)rows * per_row;
+    const int dq = kCopyThreads / per_row, dc = kCopyThreads % per_row;
+    int r = (int)threadIdx.x / per_row, c = (int)threadIdx.x % per_row;
+    for (int i0 = (int)threadIdx.x; i0 < n; i0 += kBatch * kCopyThreads) {
+      u32x4 v[kBatch];
+      int64_t dst[kBatch];
+#pragma unroll
+      for (int j = 0; j < kBatch; j++) {
+        dst[j] = -1;
+        if (i0 + j * kCopyThreads < n) {
+          const int64_t R = row0 + r;
+          const int64_t bb = one_shard ? b0 : (int64_t)((uint32_t)R / (uint32_t)a.block_rows);
+          const int64_t lr = R - bb * a.block_rows, col = c0 + (int64_t)c * 8;
+          v[j] = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(a.shards[bb]) + lr * a.k + col);
+          dst[j] = R * a.k + col;
+        }
+        r += dq;
+        c += dc;
+        if (c >= per_row) {
+          c -= per_row;
+          r += 1;
+        }
       }
-      for (; i < n; i += kCopyThreads) d[i] = s[i];
-    } else {  // 16-bit elements, any row length
-      const uint16_t* s = reinterpret_cast<const uint16_t*>(src);
-      uint16_t* d = reinterpret_cast<uint16_t*>(dst);
-      for (int64_t i = threadIdx.x; i < bytes / 2; i += kCopyThreads) d[i] = s[i];
+#pragma unroll
+      for (int j = 0; j < kBatch; j++)
+        if (dst[j] >= 0) {
+          uint64_t* d = reinterpret_cast<uint64_t*>(gout + dst[j]);
+          __hip_atomic_store(d, (uint64_t)v[j][0] | ((uint64_t)v[j][1] << 32), __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT);
+          __hip_atomic_store(d + 1, (uint64_t)v[j][2] | ((uint64_t)v[j][3] << 32), __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT);
+        }
+    }
+  } else {  // 16-bit elements, any row length
+    const int64_t n = rows * cols;
+    for (int64_t i = threadIdx.x; i < n; i += kCopyThreads) {
+      const int64_t R = row0 + i / cols, c = c0 + i % cols;
+      const int64_t bb = R / a.block_rows, lr = R - bb * a.block_rows;
+      __hip_atomic_store(gout + R * a.k + c, static_cast<const uint16_t*>(a.shards[bb])[lr * a.k + c],
+                         __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   }
-  // Every wave makes its stores visible device-wide (the XCDs' L2s are not
-  // coherent with each other), then one thread raises the chunk's flag.
-  __atomic_thread_fence(__ATOMIC_RELEASE);
+  // every wavefront's stores are visible device-wide, then one thread raises the flag
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
   __syncthreads();
   if (threadIdx.x == 0)
-    __hip_atomic_store(a.flags + (int64_t)blk * a.chunks + c, a.epoch, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_SYSTEM);
+    __hip_atomic_store(a.flags + (int64_t)g * a.slabs + sl, a.epoch, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_SYSTEM);
 }
 
 }  // namespace
 
 hipError_t launch_arrival_copy(const ArrivalArgs& a, hipStream_t s) {
-  if (a.r < 1 || a.r > kMaxRanks || a.chunks < 1 || a.chunk_rows < 1 || a.block_rows < 1 || a.row_bytes < 2 ||
-      (int64_t)a.chunks * a.chunk_rows < a.block_rows || a.first < 0 || a.first >= a.r)
+  const int64_t m = (int64_t)a.r * a.block_rows;
+  if (a.r < 1 || a.r > kMaxRanks || a.block_rows < 1 || a.k < 1 || a.rows_chunk < 1 || a.slab_cols < 1 ||
+      a.slabs < 1 || a.chunks < 1 || (int64_t)a.chunks * a.rows_chunk < m ||
+      (int64_t)(a.chunks - 1) * a.rows_chunk >= m || (int64_t)a.slabs * a.slab_cols < a.k ||
+      (int64_t)(a.slabs - 1) * a.slab_cols >= a.k || a.first_chunk < 0 || a.first_chunk >= a.chunks)
     return hipErrorInvalidValue;
-  arrive_kernel<<<a.r * a.chunks, kCopyThreads, 0, s>>>(a);
+  arrive_kernel<<<(unsigned)((int64_t)a.chunks * a.slabs), kCopyThreads, 0, s>>>(a);
   return hipGetLastError();
 }
 

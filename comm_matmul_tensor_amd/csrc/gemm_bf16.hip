@@ -35,15 +35,15 @@ struct Ops16 {
   }
 };
 
-template <int BM, int BN, bool AK, bool BKM, bool VEC, int DT>
+// ARR: arrival emulation (A arrives in p.arrived piece by piece; gemm_mfma.hpp).
+template <int BM, int BN, bool AK, bool BKM, bool VEC, int DT, bool ARR>
 __global__ __launch_bounds__(kThreads, 1) void gemm16_kernel(Problem p, void* c) {
   constexpr int FM = BM / 32, FN = BN / 32;
   __shared__ __attribute__((aligned(1024))) uint8_t s0[lds_stage_array_bytes<BM, BN>()];
   __shared__ __attribute__((aligned(1024))) uint8_t s1[lds_stage_array_bytes<BM, BN>()];
   __shared__ __attribute__((aligned(1024))) uint8_t s2[lds_stage_array_bytes<BM, BN>()];
   int tm, tn;
-  const int first_tile = p.ready ? (int)(p.first_block * p.rows_per_part / BM) : 0;
-  tile_of_block(p.m, p.n, BM, BN, p.tile_order_cols, tm, tn, first_tile);
+  tile_of_block(p.m, p.n, BM, BN, p.tile_order_cols, p.tile_group, tm, tn, ARR ? p.first_row_tile : 0);
   const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
   const int tiles_n = (int)((p.n + BN - 1) / BN);
 
@@ -53,12 +53,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm16_kernel(Problem p, void* c)
 #pragma unroll
     for (int j = 0; j < FN; j++) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  if (AK && p.ready) {
-    const Problem q = arrival_problem(p, m0, BM);
-    run_mainloop<2, BM, BN, AK, BKM, VEC, Ops16<DT>>(q, m0, n0, tn, tiles_n, s0, s1, s2, acc);
-  } else {
-    run_mainloop<2, BM, BN, AK, BKM, VEC, Ops16<DT>>(p, m0, n0, tn, tiles_n, s0, s1, s2, acc);
-  }
+  run_mainloop<2, BM, BN, AK, BKM, VEC, ARR, Ops16<DT>>(p, m0, n0, tn, tiles_n, s0, s1, s2, acc);
 
   store_c16<BM, BN, VEC>(reinterpret_cast<uint16_t*>(s0), reinterpret_cast<uint16_t*>(s1), static_cast<uint16_t*>(c),
                          p.m, p.n, m0, n0, [&](int i, int j, int r, int, int) { return Ops16<DT>::cvt(acc[i][j][r]); });
@@ -70,15 +65,24 @@ hipError_t launch_cfg(Problem p, void* c, hipStream_t s) {
   // 16-byte vector access needs every row of every operand and of C to start 16-byte aligned
   const bool vec = (p.k % 8 == 0) && (AK || p.m % 8 == 0) && (p.n % 8 == 0);
   p.tile_order_cols = prefer_column_order(p.m, p.n, p.k, 2) ? 1 : 0;
-  if (vec) gemm16_kernel<BM, BN, AK, BKM, true, DT><<<(unsigned)tiles, kThreads, 0, s>>>(p, c);
-  else gemm16_kernel<BM, BN, AK, BKM, false, DT><<<(unsigned)tiles, kThreads, 0, s>>>(p, c);
+  p.tile_group = choose_tile_group(p.m, p.n, BM, BN, p.tile_order_cols);
+  if constexpr (AK) {
+    if (p.ready) {
+      if (vec) gemm16_kernel<BM, BN, AK, BKM, true, DT, true><<<(unsigned)tiles, kThreads, 0, s>>>(p, c);
+      else gemm16_kernel<BM, BN, AK, BKM, false, DT, true><<<(unsigned)tiles, kThreads, 0, s>>>(p, c);
+      return hipGetLastError();
+    }
+  }
+  if (vec) gemm16_kernel<BM, BN, AK, BKM, true, DT, false><<<(unsigned)tiles, kThreads, 0, s>>>(p, c);
+  else gemm16_kernel<BM, BN, AK, BKM, false, DT, false><<<(unsigned)tiles, kThreads, 0, s>>>(p, c);
   return hipGetLastError();
 }
 
+const TileChoice kTiles16[] = {{128, 224}, {224, 128}, {128, 128}};
+
 template <bool AK, bool BKM, int DT>
 hipError_t launch_layout(const Problem& p, void* c, hipStream_t s) {
-  static const TileChoice cands[] = {{128, 224}, {224, 128}, {128, 128}};
-  switch (pick_tile(p.m, p.n, cands, 3)) {
+  switch (pick_tile(p.m, p.n, kTiles16, 3)) {
     case 0: return launch_cfg<128, 224, AK, BKM, DT>(p, c, s);
     case 1: return launch_cfg<224, 128, AK, BKM, DT>(p, c, s);
     default: return launch_cfg<128, 128, AK, BKM, DT>(p, c, s);
@@ -100,9 +104,10 @@ hipError_t launch_dt(const GemmArgs& g, hipStream_t s) {
     p.ready_value = g.ready_value;
     p.fallbacks = g.status_flag;
     p.arrived = g.gather_out;
-    p.first_block = g.first_part;
-    p.chunks = g.chunks;
-    p.chunk_rows = g.chunk_rows;
+    p.rows_chunk = g.rows_chunk;
+    p.slab_cols = g.slab_cols;
+    p.slabs = g.slabs;
+    p.first_row_tile = g.first_row_tile;
     p.gather_out = nullptr;
   }
   if (g.a_kmajor && g.b_kmajor) return launch_layout<true, true, DT>(p, g.c, s);
@@ -113,13 +118,19 @@ hipError_t launch_dt(const GemmArgs& g, hipStream_t s) {
 
 }  // namespace
 
+int gemm16_tile_rows(int64_t m, int64_t n) { return kTiles16[pick_tile(m, n, kTiles16, 3)].bm; }
+
 hipError_t launch_gemm16(const GemmArgs& g, hipStream_t s) {
   if (g.m < 1 || g.n < 1 || g.k < 1 || g.num_parts < 1 || g.num_parts > kMaxRanks) return hipErrorInvalidValue;
   if (g.num_parts * g.rows_per_part != g.m) return hipErrorInvalidValue;
   if (g.gather_out && !g.a_kmajor) return hipErrorInvalidValue;
-  if (g.ready_flags && (!g.gather_out || !g.status_flag || g.first_part < 0 || g.first_part >= g.num_parts ||
-                        g.chunks < 1 || g.chunk_rows < 1 || g.chunks * g.chunk_rows < g.rows_per_part))
-    return hipErrorInvalidValue;
+  if (g.ready_flags) {
+    const int bm = gemm16_tile_rows(g.m, g.n);
+    if (!g.gather_out || !g.status_flag || !g.a_kmajor || g.rows_chunk < bm || g.rows_chunk % bm != 0 ||
+        g.slabs < 1 || g.slab_cols < 1 || g.slab_cols % 64 != 0 || (int64_t)g.slabs * g.slab_cols < g.k ||
+        g.first_row_tile < 0 || (int64_t)g.first_row_tile * bm >= g.m)
+      return hipErrorInvalidValue;
+  }
   if (g.dtype == DT_BF16) return launch_dt<DT_BF16>(g, s);
   if (g.dtype == DT_F16) return launch_dt<DT_F16>(g, s);
   return hipErrorInvalidValue;

@@ -33,7 +33,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_i8_kernel(Problem p, GemmI8A
   __shared__ __attribute__((aligned(1024))) uint8_t s1[lds_stage_array_bytes<BM, BN>()];
   __shared__ __attribute__((aligned(1024))) uint8_t s2[lds_stage_array_bytes<BM, BN>()];
   int tm, tn;
-  tile_of_block(p.m, p.n, BM, BN, p.tile_order_cols, tm, tn);
+  tile_of_block(p.m, p.n, BM, BN, p.tile_order_cols, p.tile_group, tm, tn);
   const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
   const int tiles_n = (int)((p.n + BN - 1) / BN);
 
@@ -43,7 +43,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_i8_kernel(Problem p, GemmI8A
 #pragma unroll
     for (int j = 0; j < FN; j++) acc[i][j] = i32x4{0, 0, 0, 0};
 
-  run_mainloop<1, BM, BN, true, false, VEC, OpsI8>(p, m0, n0, tn, tiles_n, s0, s1, s2, acc);
+  run_mainloop<1, BM, BN, true, false, VEC, false, OpsI8>(p, m0, n0, tn, tiles_n, s0, s1, s2, acc);
 
   const int wave = threadIdx.x / 64, lane = threadIdx.x % 64;
   const int wm = wave / 2, wn = wave % 2;
@@ -78,6 +78,7 @@ hipError_t launch_cfg(Problem p, const GemmI8Args& g, hipStream_t s) {
   const int64_t tiles = ((p.m + BM - 1) / BM) * ((p.n + BN - 1) / BN);
   const bool vec = (p.k % 16 == 0) && (p.n % 16 == 0);
   p.tile_order_cols = prefer_column_order(p.m, p.n, p.k, 1) ? 1 : 0;
+  p.tile_group = choose_tile_group(p.m, p.n, BM, BN, p.tile_order_cols);
   if (vec) gemm_i8_kernel<BM, BN, true, DT><<<(unsigned)tiles, kThreads, 0, s>>>(p, g);
   else gemm_i8_kernel<BM, BN, false, DT><<<(unsigned)tiles, kThreads, 0, s>>>(p, g);
   return hipGetLastError();

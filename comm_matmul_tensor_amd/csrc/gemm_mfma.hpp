@@ -74,65 +74,26 @@ struct Problem {
   void* gather_out;       // optional copy of the gathered A
   int64_t m, n, k;
   int tile_order_cols;
-  // Arrival emulation (ready == NULL: off).  Rows of row block i are read
-  // from `arrived` once the flags of their chunks equal ready_value (flag
-  // i * chunks + c: rows [c chunk_rows, (c+1) chunk_rows) of block i); a
-  // workgroup whose wait times out reads its rows from a_parts instead and
-  // counts itself in *fallbacks.
+  int tile_group;         // tile rows (columns with tile_order_cols) per group of the tile order
+  // Arrival emulation (ready == NULL: off).  A arrives in `arrived` (the
+  // gathered matrix) in pieces: rows [g rows_chunk, (g+1) rows_chunk) x
+  // columns [s slab_cols, (s+1) slab_cols) may be read once
+  // ready[g * slabs + s] == ready_value.  rows_chunk is a multiple of the
+  // tile height, so a tile waits on one flag per slab.  A workgroup whose
+  // wait times out reads the rest of its rows from a_parts (the shards)
+  // instead and counts itself in *fallbacks.
   const unsigned* ready;
   unsigned ready_value;
   unsigned* fallbacks;
   const void* arrived;
-  int first_block;        // the local block: its tiles are handed out first
-  int chunks;
-  int64_t chunk_rows;
+  int64_t rows_chunk;
+  int64_t slab_cols;
+  int slabs;
+  int first_row_tile;     // tile row of the local block's first rows: handed out first
 };
 
 // Longest wait for one row block, in ticks of the 100 MHz real-time counter.
 constexpr uint64_t kArrivalTimeoutTicks = 20000000ull;  // 200 ms
-
-// Waits until *flag == value (raised by the copy kernel once the chunk's
-// bytes are visible device-wide) or the time limit passes.  Returns whether
-// the chunk arrived.  The flag lives in uncached memory, so every poll reads
-// memory; the acquire fence orders the tile's loads after the poll.
-__device__ __forceinline__ bool wait_block(const unsigned* flag, unsigned value) {
-  const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
-  for (;;) {
-    if (__hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM) == value) {
-      __atomic_thread_fence(__ATOMIC_ACQUIRE);
-      return true;
-    }
-    if (__builtin_amdgcn_s_memrealtime() - t0 > kArrivalTimeoutTicks) return false;
-    __builtin_amdgcn_s_sleep(4);
-  }
-}
-
-// Arrival prologue of a workgroup whose tile covers rows [m0, m0 + bm): waits
-// for the row blocks of those rows and returns the Problem its main loop
-// reads (A from the arrived buffer, or from the shards after a time-out).
-__device__ __forceinline__ Problem arrival_problem(const Problem& p, int64_t m0, int bm) {
-  __shared__ int s_ok;
-  if (threadIdx.x == 0) {
-    const int64_t end = m0 + bm < p.m ? m0 + bm : p.m;
-    bool ok = true;
-    for (int64_t i = m0 / p.rows_per_part; ok && i <= (end - 1) / p.rows_per_part; i++) {
-      const int64_t base = i * p.rows_per_part;
-      const int64_t lo = (m0 > base ? m0 : base) - base;
-      const int64_t hi = (end < base + p.rows_per_part ? end : base + p.rows_per_part) - base;
-      for (int64_t c = lo / p.chunk_rows; ok && c <= (hi - 1) / p.chunk_rows; c++)
-        ok = wait_block(p.ready + i * p.chunks + c, p.ready_value);
-    }
-    if (!ok) __hip_atomic_fetch_add(p.fallbacks, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    s_ok = ok;
-  }
-  __syncthreads();
-  Problem q = p;
-  if (s_ok) {
-    for (int i = 0; i < kMaxRanks; i++) q.a_parts[i] = p.arrived;
-    q.rows_per_part = p.m;
-  }
-  return q;
-}
 
 // Row pointer of K-contiguous operand row `row` (row blocks of rows_per_part
 // rows live in separate buffers; resolved once per thread, outside the K loop).
@@ -145,6 +106,42 @@ __device__ __forceinline__ const uint8_t* kmajor_row(const void* const* parts, i
     part++;
   }
   return static_cast<const uint8_t*>(parts[part]) + local * ld_bytes;
+}
+
+// Waits until *flag == value (raised by the copy kernel once its piece of A
+// is visible device-wide) or the time limit passes; returns whether the
+// piece arrived.  The flag lives in uncached memory, so every poll reads
+// memory.  Every wavefront polls for itself (the 64 lanes' loads of one
+// address are one request).
+__device__ __forceinline__ bool wait_flag(const unsigned* flag, unsigned value) {
+  const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+  for (;;) {
+    if (__hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM) == value) return true;
+    if (__builtin_amdgcn_s_memrealtime() - t0 > kArrivalTimeoutTicks) return false;
+    __builtin_amdgcn_s_sleep(4);
+  }
+}
+
+// Arrival prologue of the checked path: waits for every slab of the tile's
+// row chunk and returns the Problem its main loop reads (A from the arrived
+// buffer, or from the shards after a time-out).
+__device__ __forceinline__ Problem arrival_problem(const Problem& p, int64_t m0) {
+  __shared__ int s_ok;
+  if (threadIdx.x == 0) {
+    const unsigned* f = p.ready + (m0 / p.rows_chunk) * p.slabs;
+    bool ok = true;
+    for (int sl = 0; ok && sl < p.slabs; sl++) ok = wait_flag(f + sl, p.ready_value);
+    if (!ok) __hip_atomic_fetch_add(p.fallbacks, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    s_ok = ok;
+  }
+  __syncthreads();
+  __atomic_thread_fence(__ATOMIC_ACQUIRE);
+  Problem q = p;
+  if (s_ok) {
+    for (int i = 0; i < kMaxRanks; i++) q.a_parts[i] = p.arrived;
+    q.rows_per_part = p.m;
+  }
+  return q;
 }
 
 // ---------------------------------------------------------------- MN-contiguous operand, transposed in registers
@@ -483,10 +480,19 @@ struct FragReader {
 //   read half 0 of step kt+1; MFMAs of half 1.
 // The barrier sits between two blocks of MFMAs, and every LDS read has a
 // block of MFMAs to hide behind.
-template <int E, int BM, int BN, bool AK, bool BKM, bool GATHER, typename Ops>
+//
+// Arrival (ARR, K-contiguous A only): A is read from p.arrived, and the DMA
+// of a step that starts a new slab of K is issued only once that slab of
+// the tile's row chunk has arrived.  Each wavefront polls the flag of the
+// slab two steps ahead just before issuing the DMA of the step after next,
+// so the poll completes under the wait every step already makes and a slab
+// that is on time costs no extra wait.  A wavefront whose wait times out
+// reads the rest of A from the shards.
+template <int E, int BM, int BN, bool AK, bool BKM, bool GATHER, bool ARR, typename Ops>
 __device__ __forceinline__ void mainloop_fast(const Problem& p, int64_t m0, int64_t n0, int gather_phase,
                                               int gather_every, uint8_t* L0, uint8_t* L1, uint8_t* L2,
                                               typename Ops::Acc (&acc)[BM / 32][BN / 32]) {
+  static_assert(!ARR || (AK && !GATHER), "arrival needs a K-contiguous A and no gather copy");
   constexpr int BK = kRowBytes / E;  // K elements per step
   constexpr int kATile = BM * kRowBytes;
   constexpr int WM = BM / 2, WN = BN / 2, FM = WM / 16, FN = WN / 16;
@@ -495,8 +501,14 @@ __device__ __forceinline__ void mainloop_fast(const Problem& p, int64_t m0, int6
   constexpr int ND = DA::kN + DB::kN;  // DMA instructions per thread and step
   DA da;
   DB db;
-  if constexpr (AK) da.init_k(p.a_parts, p.rows_per_part, p.k * E, m0, p.m);
-  else da.init_mn(p.a_parts[0], p.m * E, m0, p.m);
+  if constexpr (ARR) {
+    const void* arrived[1] = {p.arrived};
+    da.init_k(arrived, p.m, p.k * E, m0, p.m);
+  } else if constexpr (AK) {
+    da.init_k(p.a_parts, p.rows_per_part, p.k * E, m0, p.m);
+  } else {
+    da.init_mn(p.a_parts[0], p.m * E, m0, p.m);
+  }
   if constexpr (BKM) {
     const void* bparts[1] = {p.b};
     db.init_k(bparts, p.n, p.k * E, n0, p.n);
@@ -510,6 +522,22 @@ __device__ __forceinline__ void mainloop_fast(const Problem& p, int64_t m0, int6
   rb.init(wn * WN);
   const int nk = (int)(p.k / BK);
   int next_gather = gather_phase;
+
+  // arrival: the flags of this tile's row chunk, one per slab of K
+  const unsigned* flags = ARR ? p.ready + (m0 / p.rows_chunk) * p.slabs : nullptr;
+  const int sps = ARR ? (int)(p.slab_cols / BK) : 1;  // steps per slab
+  bool fell_back = false;
+  unsigned pv = 0;  // polled flag of the slab of the step after next
+  auto poll = [&](int kt) { return __hip_atomic_load(flags + kt / sps, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM); };
+  // Blocking wait for the slab of step kt; after a time-out A comes from the shards.
+  auto wait_step = [&](int kt) {
+    if (fell_back) return;
+    if (!wait_flag(flags + kt / sps, p.ready_value)) {
+      fell_back = true;
+      da.init_k(p.a_parts, p.rows_per_part, p.k * E, m0, p.m);
+      if (threadIdx.x % 64 == 0) __hip_atomic_fetch_add(p.fallbacks, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  };
 
   u32x4 fa0[FM], fb0[FN], fa1[FM], fb1[FN];
   auto dma = [&](uint8_t* L, int kt) {
@@ -531,12 +559,14 @@ __device__ __forceinline__ void mainloop_fast(const Problem& p, int64_t m0, int6
 #pragma unroll
     for (int q = 0; q < NM; q++) {
       acc[q / FN][q % FN] = Ops::mfma(fa[q / FN], fb[q % FN], acc[q / FN][q % FN]);
+      if constexpr (NDH > 0) {
 #pragma unroll
-      for (int d = 0; d < NDH; d++)
-        if ((d * NM) / NDH == q && dma_on) {
-          if (D0 + d < DA::kN) da.issue_one(L, offa, D0 + d);
-          else db.issue_one(L + kATile, offb, D0 + d - DA::kN);
-        }
+        for (int d = 0; d < NDH; d++)
+          if ((d * NM) / NDH == q && dma_on) {
+            if (D0 + d < DA::kN) da.issue_one(L, offa, D0 + d);
+            else db.issue_one(L + kATile, offb, D0 + d - DA::kN);
+          }
+      }
 #pragma unroll
       for (int f = 0; f < NF; f++)
         if ((f * NM) / NF == q && rd_on) {
@@ -558,6 +588,11 @@ __device__ __forceinline__ void mainloop_fast(const Problem& p, int64_t m0, int6
       copy_gather<E, BM>(cur, p.gather_out, p.m, p.k, m0, (int64_t)kt * BK);
       next_gather += gather_every;
     }
+    if constexpr (ARR) {
+      // the slab of step kt+2 (polled during the previous step) must have arrived
+      if (dma2 && (kt + 2) % sps == 0 && pv != p.ready_value) wait_step(kt + 2);
+      if (!fell_back && kt + 3 < nk && (kt + 3) % sps == 0) pv = poll(kt + 3);
+    }
     __builtin_amdgcn_sched_barrier(0);
     // half 0 of step kt; the DMA of step kt+2 (its stage was last read
     // before the previous barrier); reads of half 1 of step kt
@@ -573,6 +608,12 @@ __device__ __forceinline__ void mainloop_fast(const Problem& p, int64_t m0, int6
     __builtin_amdgcn_sched_barrier(0);
   };
 
+  if constexpr (ARR) {
+    wait_step(0);
+    __atomic_thread_fence(__ATOMIC_ACQUIRE);  // no stale lines of A from earlier calls
+    if (nk > 1 && 1 % sps == 0) wait_step(1);
+    if (!fell_back && nk > 2 && 2 % sps == 0) pv = poll(2);
+  }
   dma(L0, 0);
   if (nk > 1) {
     dma(L1, 1);
@@ -656,37 +697,55 @@ constexpr int stage_bytes() { return (BM + BN) * kRowBytes; }
 // Runs the main loop variant this workgroup needs.  gather: copy the gathered
 // A to p.gather_out, spread over the workgroups of the row of tiles (the
 // workgroup of column tile tn copies the steps kt with kt % tiles_n == tn).
-template <int E, int BM, int BN, bool AK, bool BKM, bool VEC, typename Ops>
+// ARR: arrival emulation (see mainloop_fast; the checked path waits for the
+// whole row chunk first).
+template <int E, int BM, int BN, bool AK, bool BKM, bool VEC, bool ARR, typename Ops>
 __device__ __forceinline__ void run_mainloop(const Problem& p, int64_t m0, int64_t n0, int tn, int tiles_n,
                                              uint8_t* L0, uint8_t* L1, uint8_t* L2,
                                              typename Ops::Acc (&acc)[BM / 32][BN / 32]) {
   constexpr int BK = kRowBytes / E;
-  const int gather_every = (AK && p.gather_out != nullptr) ? tiles_n : 0;
+  const int gather_every = (AK && !ARR && p.gather_out != nullptr) ? tiles_n : 0;
   if constexpr (VEC) {
     if (p.k % BK == 0) {
-      if (AK && gather_every > 0) mainloop_fast<E, BM, BN, AK, BKM, AK, Ops>(p, m0, n0, tn, gather_every, L0, L1, L2, acc);
-      else mainloop_fast<E, BM, BN, AK, BKM, false, Ops>(p, m0, n0, tn, gather_every, L0, L1, L2, acc);
+      if constexpr (ARR) mainloop_fast<E, BM, BN, AK, BKM, false, true, Ops>(p, m0, n0, tn, 0, L0, L1, L2, acc);
+      else if (AK && gather_every > 0)
+        mainloop_fast<E, BM, BN, AK, BKM, AK, false, Ops>(p, m0, n0, tn, gather_every, L0, L1, L2, acc);
+      else mainloop_fast<E, BM, BN, AK, BKM, false, false, Ops>(p, m0, n0, tn, gather_every, L0, L1, L2, acc);
       return;
     }
   }
-  mainloop_checked<E, BM, BN, AK, BKM, Ops>(p, m0, n0, tn, gather_every, L0, L1, acc);
+  if constexpr (ARR) {
+    const Problem q = arrival_problem(p, m0);
+    mainloop_checked<E, BM, BN, AK, BKM, Ops>(q, m0, n0, tn, 0, L0, L1, acc);
+  } else {
+    mainloop_checked<E, BM, BN, AK, BKM, Ops>(p, m0, n0, tn, gather_every, L0, L1, acc);
+  }
 }
 
-// Choose the XCD-aware tile of workgroup blockIdx.x.  first_row_tile rotates
-// the row tiles so that the tiles holding that row tile come first.
-__device__ __forceinline__ void tile_of_block(int64_t m, int64_t n, int bm, int bn, int cols_order, int& tm, int& tn,
-                                              int first_row_tile = 0) {
+// Choose the XCD-aware tile of workgroup blockIdx.x.  Workgroup b runs on XCD
+// b % 8, so b is first renumbered to lin such that each XCD owns a
+// contiguous 1/8 of the tiles.  lin then walks the tiles in groups of
+// kTileGroup tile rows, column by column inside a group (cols_order: groups
+// of tile columns, row by row), so the tiles an XCD runs at once form a
+// compact block and the band of the operand its group shares stays in that
+// XCD's L2 while the other operand streams past once (choose_tile_group
+// picks the group size).  first_row_tile rotates the row tiles so that tile
+// row comes first.
+__device__ __forceinline__ void tile_of_block(int64_t m, int64_t n, int bm, int bn, int cols_order, int group, int& tm,
+                                              int& tn, int first_row_tile = 0) {
   const int tiles_m = (int)((m + bm - 1) / bm), tiles_n = (int)((n + bn - 1) / bn);
   const int tiles = tiles_m * tiles_n;
   int lin = blockIdx.x;
   if (tiles % 8 == 0) lin = (blockIdx.x % 8) * (tiles / 8) + blockIdx.x / 8;
-  if (cols_order) {
-    tn = lin / tiles_m;
-    tm = lin % tiles_m;
-  } else {
-    tm = lin / tiles_n;
-    tn = lin % tiles_n;
-  }
+  // major: the dimension grouped (rows, or columns with cols_order); minor: the other
+  const int n_major = cols_order ? tiles_n : tiles_m, n_minor = cols_order ? tiles_m : tiles_n;
+  const int per_group = group * n_minor;
+  const int first = (lin / per_group) * group;
+  const int gsize = n_major - first < group ? n_major - first : group;
+  const int r = lin % per_group;
+  const int major = first + r % gsize, minor = r / gsize;
+  tm = cols_order ? minor : major;
+  tn = cols_order ? major : minor;
   tm = (tm + first_row_tile) % tiles_m;
 }
 
@@ -744,6 +803,28 @@ constexpr int lds_stage_array_bytes() {
 inline bool prefer_column_order(int64_t m, int64_t n, int64_t k, int e) {
   const double a = (double)m * (double)k * e, b = (double)n * (double)k * e;
   return 8.0 * a + b < a + 8.0 * b;
+}
+
+// Group size of the tile order: the 32 workgroups an XCD runs at once cover
+// G tile rows x 32/G tile columns (transposed with cols_order), whose A and
+// B bands its L2 must hold; pick the G with the smallest bands.
+inline int choose_tile_group(int64_t m, int64_t n, int bm, int bn, int cols_order) {
+  constexpr int kPerXcd = 32;
+  const int64_t tiles_m = (m + bm - 1) / bm, tiles_n = (n + bn - 1) / bn;
+  const int64_t major = cols_order ? tiles_n : tiles_m, minor = cols_order ? tiles_m : tiles_n;
+  const int64_t wmaj = cols_order ? bn : bm, wmin = cols_order ? bm : bn;
+  int best = 1;
+  int64_t best_cost = -1;
+  for (int64_t g = 1; g <= major && g <= kPerXcd; g++) {
+    const int64_t cols = (kPerXcd + g - 1) / g;
+    if (cols > minor && g < major) continue;
+    const int64_t cost = g * wmaj + (cols < minor ? cols : minor) * wmin;
+    if (best_cost < 0 || cost < best_cost) {
+      best_cost = cost;
+      best = (int)g;
+    }
+  }
+  return best;
 }
 
 // Pick a tile shape: maximise (useful MFMA work / issued) x (CU fill over the

@@ -37,32 +37,41 @@ struct GemmArgs {
   int64_t m, n, k;
   int dtype;  // DT_F16 or DT_BF16
   int tile_order_cols;  // set by the launcher: XCD tile order walks columns of tiles
-  // arrival emulation (ready_flags NULL when unused): rows of part i of A
-  // are read from gather_out once the flags of their chunks equal
-  // ready_value (flag i * chunks + c covers rows [c chunk_rows, (c+1)
-  // chunk_rows) of part i); the tiles of part first_part come first;
-  // *status_flag counts workgroups whose wait timed out (they read the part
-  // from a_parts instead)
+  // arrival emulation (ready_flags NULL when unused): A is read from
+  // gather_out; rows [g rows_chunk, (g+1) rows_chunk) x columns
+  // [s slab_cols, (s+1) slab_cols) may be read once
+  // ready_flags[g * slabs + s] == ready_value.  rows_chunk must be a
+  // multiple of gemm16_tile_rows(m, n) and slab_cols of 64.  Tile row
+  // first_row_tile is handed out first; *status_flag counts wavefronts
+  // whose wait timed out (they read A from a_parts instead).
   const unsigned* ready_flags;
   unsigned ready_value;
-  int first_part;
-  int chunks;
-  int64_t chunk_rows;
+  int64_t rows_chunk;
+  int64_t slab_cols;
+  int slabs;
+  int first_row_tile;
   unsigned* status_flag;
 };
 hipError_t launch_gemm16(const GemmArgs& a, hipStream_t s);
+// Tile height (rows of C per workgroup) launch_gemm16 uses for an (m, n) C.
+int gemm16_tile_rows(int64_t m, int64_t n);
 
-// ---- arrival emulation: copy of the shards into gather_out, chunk by chunk,
-// each chunk followed by its ready flag (flags[b * chunks + c] = epoch)
+// ---- arrival emulation: copy of the shards into gather_out piece by piece
+// (row chunk g, slab s of K), each piece followed by its ready flag
+// (flags[g * slabs + s] = epoch).  Row chunk g covers gathered rows
+// [g rows_chunk, (g+1) rows_chunk); one workgroup per piece, slab by slab,
+// row chunk first_chunk first within a slab.
 struct ArrivalArgs {
   const void* shards[kMaxRanks];
   void* gather_out;
   unsigned* flags;
   int64_t block_rows;  // rows per shard
-  int64_t row_bytes;   // bytes per row
-  int64_t chunk_rows;  // rows per chunk
-  int chunks;          // chunks per shard
-  int r, first;        // shard count; the block copied first
+  int64_t k;           // elements per row (16-bit elements)
+  int64_t rows_chunk;
+  int64_t slab_cols;
+  int slabs;
+  int chunks;          // row chunks in the gathered matrix
+  int r, first_chunk;
   unsigned epoch;
 };
 hipError_t launch_arrival_copy(const ArrivalArgs& a, hipStream_t s);

@@ -74,14 +74,16 @@ typedef enum {
   /* the GEMM reads each rank's rows straight from its shard and the
      workgroups of the first column tile also write gather_out */
   MC2_AG_FUSED_WRITE = 0,
-  /* arrival emulation: on a side stream a copy kernel moves shard i into
-     gather_out block i in up to 16 chunks of rows, local block (rank_id)
-     first, raising a ready flag per chunk; the GEMM reads A from gather_out
-     and each workgroup starts its K loop once the chunks its tile covers
-     have arrived.  The side stream is forked from and joined back into
-     `stream`.  A workgroup that waits longer than 200 ms for a chunk reads
-     its rows from the shards instead (the result is the same) and is
-     counted by mc2_allgather_arrival_fallbacks. */
+  /* arrival emulation: on a side stream a copy kernel fills gather_out
+     piece by piece -- row chunks of the GEMM's tile height times up to 16
+     slabs of K, the local rank's (rank_id) rows first -- raising a ready
+     flag per piece; the GEMM reads A from gather_out and issues the loads
+     of each slab of K only once its piece has arrived, so compute starts on
+     the first slab while later ones are still being copied.  The side
+     stream is forked from and joined back into `stream`.  A wavefront that
+     waits longer than 200 ms for a piece reads the rest of its rows from
+     the shards instead (the result is the same) and is counted by
+     mc2_allgather_arrival_fallbacks. */
   MC2_AG_ARRIVAL = 1
 } mc2_ag_mode;
 
@@ -115,9 +117,9 @@ mc2_status mc2_allgather_matmul(const void* const* shards, int world_size, int64
                                 int rank_id, void* stream);
 
 /*
- * Number of GEMM workgroups of MC2_AG_ARRIVAL calls on the current device
- * whose wait for a row block timed out since the last reset (each such
- * workgroup read its rows from the shards, so results are unaffected).
+ * Number of GEMM wavefronts of MC2_AG_ARRIVAL calls on the current device
+ * whose wait for a piece of gather_out timed out since the last reset (each
+ * read its rows from the shards instead, so results are unaffected).
  * Waits for the device to be idle; reset != 0 clears the count afterwards.
  * A nonzero count means the copies did not feed the GEMM in time, so that
  * call did not pipeline copies with compute.
