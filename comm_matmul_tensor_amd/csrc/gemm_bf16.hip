@@ -62,8 +62,14 @@ __global__ __launch_bounds__(kThreads, 1) void gemm16_kernel(Problem p, void* c)
 template <int BM, int BN, bool AK, bool BKM, int DT>
 hipError_t launch_cfg(Problem p, void* c, hipStream_t s) {
   const int64_t tiles = ((p.m + BM - 1) / BM) * ((p.n + BN - 1) / BN);
-  // 16-byte vector access needs every row of every operand and of C to start 16-byte aligned
-  const bool vec = (p.k % 8 == 0) && (AK || p.m % 8 == 0) && (p.n % 8 == 0);
+  // 16-byte vector access needs every row of every operand and of C to start
+  // 16-byte aligned; the buffer-load staging needs operands below 2 GiB and
+  // gathered row blocks of a multiple of 8 rows (otherwise: checked path)
+  const int64_t a_bytes = AK ? (p.ready ? p.m : p.rows_per_part) * p.k * 2 : p.k * p.m * 2;
+  const int parts = p.rows_per_part == p.m ? 1 : 2;
+  const bool vec = (p.k % 8 == 0) && (AK || p.m % 8 == 0) && (p.n % 8 == 0) &&
+                   dma_buffers_ok(a_bytes, p.k * p.n * 2, parts, p.rows_per_part) &&
+                   dma_buffers_ok(p.rows_per_part * p.k * 2, 0, parts, p.rows_per_part);
   p.tile_order_cols = prefer_column_order(p.m, p.n, p.k, 2) ? 1 : 0;
   p.tile_group = choose_tile_group(p.m, p.n, BM, BN, p.tile_order_cols);
   if constexpr (AK) {

@@ -76,7 +76,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_i8_kernel(Problem p, GemmI8A
 template <int BM, int BN, int DT>
 hipError_t launch_cfg(Problem p, const GemmI8Args& g, hipStream_t s) {
   const int64_t tiles = ((p.m + BM - 1) / BM) * ((p.n + BN - 1) / BN);
-  const bool vec = (p.k % 16 == 0) && (p.n % 16 == 0);
+  // 16-byte vector access and the buffer-load staging (operands below 2 GiB)
+  const bool vec = (p.k % 16 == 0) && (p.n % 16 == 0) && dma_buffers_ok(p.m * p.k, p.k * p.n, 1, p.m);
   p.tile_order_cols = prefer_column_order(p.m, p.n, p.k, 1) ? 1 : 0;
   p.tile_group = choose_tile_group(p.m, p.n, BM, BN, p.tile_order_cols);
   if (vec) gemm_i8_kernel<BM, BN, true, DT><<<(unsigned)tiles, kThreads, 0, s>>>(p, g);

@@ -362,51 +362,86 @@ __device__ __forceinline__ int swz_mn(int k, int c) { return k * (R * E) + ((c ^
 // One operand tile per step (R rows x 128 bytes of K = 8R slots of 16 bytes).
 // Thread t fills slots s = t + 256 i, i < R / 32, so instruction i of
 // wavefront w writes the 1 KB block 256 i + 64 w + lane, in lane order as
-// global_load_lds requires; the global address of each lane is chosen so
+// the LDS-destination loads require; the address of each lane is chosen so
 // that the block holds the swizzled layout.  Rows (K-major) or chunks
 // (MN-major) past the matrix edge are clamped to the last valid one: their
 // products land only in C elements the epilogue does not store.
+//
+// The loads are buffer loads into LDS (buffer_load_dwordx4 ... lds): each
+// instruction has a wave-uniform buffer resource (base and byte size of the
+// operand, or of the row block holding that instruction's 8 rows), a fixed
+// 32-bit per-lane offset and the step's offset as a scalar, so issuing one
+// takes no vector arithmetic.  A load past the resource's size returns zeros
+// instead of faulting.  Requirements, checked by the launcher: every
+// operand (or row block) below 2 GiB, and gathered row blocks a multiple of
+// 8 rows (the 8 rows of one instruction then never straddle two blocks).
+constexpr int kBufferFlags = 0x00020000;  // dword 3 of a raw buffer resource on gfx9
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, kBufferFlags);
+}
+
 template <int E, int R, bool KMAJ>
 struct DmaOperand {
   static constexpr int kN = R / 32;  // DMA instructions per thread and step
-  const uint8_t* src[kN];            // this lane's 16 bytes at step 0
-  int64_t step_bytes;                // global distance between consecutive steps
+  __amdgpu_buffer_rsrc_t rsrc[kN];   // instruction i's operand (wave-uniform)
+  uint32_t voff[kN];                 // this lane's byte offset at step 0
+  uint32_t step_bytes;               // distance between consecutive steps
+  int lds_wave;                      // 1024 x this wavefront's index (wave-uniform)
 
   // K-contiguous operand: row r of the tile is matrix row mn0 + r, found in
   // the row blocks `parts` (rows_per_part rows each, ld_bytes per row).
   __device__ __forceinline__ void init_k(const void* const* parts, int64_t rows_per_part, int64_t ld_bytes,
                                          int64_t mn0, int64_t mn_ext) {
+    const int w = __builtin_amdgcn_readfirstlane((int)(threadIdx.x / 64));
+    lds_wave = 1024 * w;
 #pragma unroll
     for (int i = 0; i < kN; i++) {
       const int s = threadIdx.x + kThreads * i, row = s / 8, c = (s % 8) ^ (row & 7);
       const int64_t r = mn0 + row < mn_ext ? mn0 + row : mn_ext - 1;
-      src[i] = kmajor_row(parts, rows_per_part, ld_bytes, r) + c * 16;
+      // the instruction's 8 rows (32 i + 8 w ...) lie in one row block
+      int64_t g0 = mn0 + 32 * i + 8 * w;
+      g0 = g0 < mn_ext ? g0 : mn_ext - 1;
+      const int64_t part = g0 / rows_per_part;
+      rsrc[i] = make_rsrc(parts[part], rows_per_part * ld_bytes);
+      voff[i] = (uint32_t)((r - part * rows_per_part) * ld_bytes + c * 16);
     }
     step_bytes = kRowBytes;
   }
-  // MN-contiguous operand stored (k, mn) with ld_bytes between k rows;
+  // MN-contiguous operand stored (k_ext, mn) with ld_bytes between k rows;
   // mn_ext is a multiple of the 16-byte chunk.
-  __device__ __forceinline__ void init_mn(const void* base, int64_t ld_bytes, int64_t mn0, int64_t mn_ext) {
+  __device__ __forceinline__ void init_mn(const void* base, int64_t ld_bytes, int64_t k_ext, int64_t mn0,
+                                          int64_t mn_ext) {
     constexpr int CH = 16 / E, kChunks = R * E / 16;
+    lds_wave = 1024 * __builtin_amdgcn_readfirstlane((int)(threadIdx.x / 64));
 #pragma unroll
     for (int i = 0; i < kN; i++) {
       const int s = threadIdx.x + kThreads * i, k = s / kChunks, c = (s % kChunks) ^ mn_swz<E, R>(k);
       int64_t col = mn0 + (int64_t)c * CH;
       if (col + CH > mn_ext) col = mn_ext - CH;
-      src[i] = static_cast<const uint8_t*>(base) + k * ld_bytes + col * E;
+      rsrc[i] = make_rsrc(base, k_ext * ld_bytes);
+      voff[i] = (uint32_t)(k * ld_bytes + col * E);
     }
-    step_bytes = (int64_t)(kRowBytes / E) * ld_bytes;
+    step_bytes = (uint32_t)((kRowBytes / E) * ld_bytes);
   }
   __device__ __forceinline__ void issue(uint8_t* tile, int64_t off) const {
 #pragma unroll
     for (int i = 0; i < kN; i++) issue_one(tile, off, i);
   }
-  // Instruction i alone.
+  // Instruction i alone; off = the step's byte offset.
   __device__ __forceinline__ void issue_one(uint8_t* tile, int64_t off, int i) const {
-    const int w = threadIdx.x / 64;
-    __builtin_amdgcn_global_load_lds((gptr_t)(src[i] + off), (lptr_t)(tile + 4096 * i + 1024 * w), 16, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc[i], (lptr_t)(tile + 4096 * i + lds_wave), 16, (int)voff[i], (int)off,
+                                             0, 0);
   }
 };
+
+// Whether the buffer-load staging covers this problem: every operand, or
+// gathered row block, below 2 GiB, and gathered row blocks of a multiple of
+// 8 rows.
+inline bool dma_buffers_ok(int64_t a_block_bytes, int64_t b_bytes, int num_parts, int64_t rows_per_part) {
+  const int64_t lim = (int64_t)1 << 31;
+  return a_block_bytes < lim && b_bytes < lim && (num_parts == 1 || rows_per_part % 8 == 0);
+}
 
 // ---------------------------------------------------------------- fragment reads
 // NF fragments of 16 rows (m or n) starting at tile row row0, for the K
@@ -507,13 +542,13 @@ __device__ __forceinline__ void mainloop_fast(const Problem& p, int64_t m0, int6
   } else if constexpr (AK) {
     da.init_k(p.a_parts, p.rows_per_part, p.k * E, m0, p.m);
   } else {
-    da.init_mn(p.a_parts[0], p.m * E, m0, p.m);
+    da.init_mn(p.a_parts[0], p.m * E, p.k, m0, p.m);
   }
   if constexpr (BKM) {
     const void* bparts[1] = {p.b};
     db.init_k(bparts, p.n, p.k * E, n0, p.n);
   } else {
-    db.init_mn(p.b, p.n * E, n0, p.n);
+    db.init_mn(p.b, p.n * E, p.k, n0, p.n);
   }
   const int wave = threadIdx.x / 64, wm = wave / 2, wn = wave % 2;
   FragReader<E, BM, AK, FM> ra;
