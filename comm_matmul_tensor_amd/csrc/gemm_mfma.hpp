@@ -590,6 +590,7 @@ __device__ __forceinline__ void mainloop_fast(const Problem& p, int64_t m0, int6
                   int kt_dma, bool rd_on, const uint8_t* rd, int kk, u32x4(&ra_out)[FM], u32x4(&rb_out)[FN]) {
     constexpr int D0 = decltype(D0_)::value, D1 = decltype(D1_)::value;
     constexpr int NM = FM * FN, NF = FM + FN, NDH = D1 - D0;
+    constexpr int kTail = NM >= 2 * NF ? NM - 2 * NF < 8 ? NM - 2 * NF : 8 : 0;
     const int64_t offa = (int64_t)kt_dma * da.step_bytes, offb = (int64_t)kt_dma * db.step_bytes;
 #pragma unroll
     for (int q = 0; q < NM; q++) {
@@ -602,11 +603,16 @@ __device__ __forceinline__ void mainloop_fast(const Problem& p, int64_t m0, int6
             else db.issue_one(L + kATile, offb, D0 + d - DA::kN);
           }
       }
+      // reads in the order the next half consumes them (its MFMAs run row i
+      // by row i: A fragment 0 with B fragments 0..FN-1, then A fragments
+      // 1..FM-1), spread over all but the last kTail slots so the last one
+      // lands before the barrier
 #pragma unroll
       for (int f = 0; f < NF; f++)
-        if ((f * NM) / NF == q && rd_on) {
-          if (f < FM) ra_out[f] = ra.read_one(rd, kk, f);
-          else rb_out[f - FM] = rb.read_one(rd + kATile, kk, f - FM);
+        if ((f * (NM - kTail)) / NF == q && rd_on) {
+          if (f == 0) ra_out[0] = ra.read_one(rd, kk, 0);
+          else if (f <= FN) rb_out[f - 1] = rb.read_one(rd + kATile, kk, f - 1);
+          else ra_out[f - FN] = ra.read_one(rd, kk, f - FN);
         }
       __builtin_amdgcn_sched_barrier(0);
     }
