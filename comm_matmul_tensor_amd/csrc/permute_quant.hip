@@ -23,8 +23,9 @@
 namespace mc2 {
 namespace {
 
-constexpr int kThreads = 512;
-constexpr int kMaxUnits = 5;  // 16-element units per thread: r*h <= 40960
+constexpr int kThreads = 512;   // general path
+constexpr int kVecThreads = 1024;
+constexpr int kMaxUnits = 3;    // 16-element units per thread of the vector path: r*h <= 49152
 
 template <int DT>
 __device__ __forceinline__ float dec16(uint32_t bits) {
@@ -58,112 +59,109 @@ __device__ __forceinline__ int quant1(float y, float s) {
 // with the division.
 
 // Vector path: h % 16 == 0, so every 16-element unit of P lies inside one
-// source row and is 32-byte aligned.  All of the token's loads are issued
-// first; y = P * smooth stays in registers between the two passes.
+// source row and is 32-byte aligned.  1024 threads per token, each owning
+// U units (U is the smallest count that covers the row, at most 3); all of
+// the token's loads are issued first and y = P * smooth stays in registers
+// between the two passes.
 //
 // Pass 2 per element, with inv = 1/s:  qa = y * inv;  c = med3(qa, -127, 127);
 // m = c + 1.5 * 2^23, which rounds c to an integer with ties to even and
 // leaves that integer's two's-complement low byte in the low byte of m's bit
-// pattern (|c| <= 127 < 2^22), so the int8 code is one byte of m.  If
-// |qa - rint(c)| >= 0.5 - 3e-5 the element is near a half-integer and the
-// wavefront recomputes its codes with the IEEE division (see quant_fast).
-template <int DT>
-__global__ __launch_bounds__(kThreads) void permute_quant_vec(QuantArgs a) {
-  __shared__ float red[kThreads / 64];
+// pattern (|c| <= 127 < 2^22), so the int8 code is one byte of m.  If any
+// |qa - rint(c)| of a unit reaches 0.5 - 3e-5, that element is near a
+// half-integer and the unit is recomputed with the IEEE division (see the
+// bound above).
+template <int DT, int U>
+__global__ __launch_bounds__(kVecThreads) void permute_quant_vec(QuantArgs a) {
+  __shared__ float red[kVecThreads / 64];
   const int64_t t = blockIdx.x;
   const int64_t T = a.bs / a.r;
   const int64_t cols = (int64_t)a.r * a.h;
   const int units = (int)(cols / 16);
+  const int hh = (int)a.h;
   const uint16_t* x1 = static_cast<const uint16_t*>(a.x1);
   const uint16_t* sm = static_cast<const uint16_t*>(a.smooth);
 
-  u32x4 raw[kMaxUnits][2], smr[kMaxUnits][2];
+  // unit u of P is 16 elements of source row j T + t, column c
+  u32x4 raw[U][2];
 #pragma unroll
-  for (int v = 0; v < kMaxUnits; v++) {
-    const int u = threadIdx.x + v * kThreads;
-    const int e = (u < units ? u : 0) * 16;  // column in P (r * h <= 40960)
-    const int hh = (int)a.h;
-    const int j = e / hh, c = e - j * hh;      // source rank block and column
-    const u32x4* src = reinterpret_cast<const u32x4*>(x1 + (((int64_t)j * T + t) * a.h + c));
+  for (int v = 0; v < U; v++) {
+    const int u = threadIdx.x + v * kVecThreads;
     if (u < units) {
+      const int e = u * 16, j = e / hh, c = e - j * hh;
+      const u32x4* src = reinterpret_cast<const u32x4*>(x1 + ((int64_t)j * T + t) * a.h + c);
       raw[v][0] = src[0];
       raw[v][1] = src[1];
     }
   }
-  if (sm) {
+  float y[U][16];
+  float amax = 0.0f;
 #pragma unroll
-    for (int v = 0; v < kMaxUnits; v++) {
-      const int u = threadIdx.x + v * kThreads;
-      if (u < units) {
-        const u32x4* sp = reinterpret_cast<const u32x4*>(sm + (int64_t)u * 16);
-        smr[v][0] = sp[0];
-        smr[v][1] = sp[1];
+  for (int v = 0; v < U; v++) {
+    const int u = threadIdx.x + v * kVecThreads;
+    if (u < units) {
+      u32x4 smr[2] = {{0u, 0u, 0u, 0u}, {0u, 0u, 0u, 0u}};
+      if (sm) {
+        const u32x4* sp = reinterpret_cast<const u32x4*>(sm + u * 16);
+        smr[0] = sp[0];
+        smr[1] = sp[1];
+      }
+#pragma unroll
+      for (int i = 0; i < 16; i++) {
+        const uint32_t xw = raw[v][i / 8][(i % 8) / 2] >> (16 * (i & 1));
+        float yy = dec16<DT>(xw);
+        if (sm) yy *= dec16<DT>(smr[i / 8][(i % 8) / 2] >> (16 * (i & 1)));
+        y[v][i] = yy;
+        amax = fmaxf(amax, __builtin_fabsf(yy));
       }
     }
   }
-  // y, element 2w+b of half hlf of unit v: y[v][hlf*8 + 2w + b]
-  float y[kMaxUnits][16];
-  float amax = 0.0f;
 #pragma unroll
-  for (int v = 0; v < kMaxUnits; v++) {
-    const int u = threadIdx.x + v * kThreads;
-    if (u < units) {
+  for (int off = 32; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off, 64));
+  if (threadIdx.x % 64 == 0) red[threadIdx.x / 64] = amax;
+  __syncthreads();
+  amax = red[0];
 #pragma unroll
-      for (int hlf = 0; hlf < 2; hlf++)
-#pragma unroll
-        for (int w = 0; w < 4; w++)
-#pragma unroll
-          for (int b = 0; b < 2; b++) {
-            float yy = dec16<DT>(raw[v][hlf][w] >> (16 * b));
-            if (sm) yy *= dec16<DT>(smr[v][hlf][w] >> (16 * b));
-            y[v][hlf * 8 + 2 * w + b] = yy;
-            amax = fmaxf(amax, __builtin_fabsf(yy));
-          }
-    }
-  }
-  amax = block_max(amax, red);
+  for (int w = 1; w < kVecThreads / 64; w++) amax = fmaxf(amax, red[w]);
   const float s = amax / 127.0f;
   if (threadIdx.x == 0) a.s1[t] = s;
-  // The error bound of quant_fast needs |y / s| <= 127 (1 + 2^-23), which holds
-  // when s is a normal number; rows with a subnormal scale use the division.
+  // The error bound of the fast path needs |y / s| <= 127 (1 + 2^-23), which
+  // holds when s is a normal number; rows with a subnormal scale use the division.
   const float inv = 1.0f / s;
   const bool fast = s >= 1.17549435e-38f;  // uniform over the workgroup
   constexpr float kMagic = 12582912.0f;    // 1.5 * 2^23
 
 #pragma unroll
-  for (int v = 0; v < kMaxUnits; v++) {
-    const int u = threadIdx.x + v * kThreads;
+  for (int v = 0; v < U; v++) {
+    const int u = threadIdx.x + v * kVecThreads;
     if (u < units) {
       const int64_t e = (int64_t)u * 16;
       u32x4 qv = {0u, 0u, 0u, 0u};
       if (amax > 0.0f) {
-        bool near = !fast;
+        float dmax = 0.0f;
         uint32_t mb[16];
 #pragma unroll
         for (int i = 0; i < 16; i++) {
           const float qa = y[v][i] * inv;
-          const float c = __builtin_amdgcn_fmed3f(qa, -127.0f, 127.0f);
-          const float m = c + kMagic;
-          near |= __builtin_fabsf(qa - (m - kMagic)) >= 0.49997f;
+          const float m = __builtin_amdgcn_fmed3f(qa, -127.0f, 127.0f) + kMagic;
+          dmax = fmaxf(dmax, __builtin_fabsf(qa - (m - kMagic)));
           mb[i] = __float_as_uint(m);
         }
-        if (near) {  // rare: redo this unit with the IEEE division
+        if (!fast || dmax >= 0.49997f) {  // rare: redo this unit with the IEEE division
 #pragma unroll
           for (int i = 0; i < 16; i++) mb[i] = (uint32_t)quant1(y[v][i], s);
         }
+        // low bytes of four codes -> one word
 #pragma unroll
         for (int w = 0; w < 4; w++)
-          qv[w] = (mb[4 * w] & 0xFFu) | ((mb[4 * w + 1] & 0xFFu) << 8) | ((mb[4 * w + 2] & 0xFFu) << 16) |
-                  (mb[4 * w + 3] << 24);
+          qv[w] = (__builtin_amdgcn_perm(mb[4 * w + 3], mb[4 * w + 2], 0x0c0c0400u) << 16) |
+                  __builtin_amdgcn_perm(mb[4 * w + 1], mb[4 * w], 0x0c0c0400u);
       }
       *reinterpret_cast<u32x4*>(a.q + t * cols + e) = qv;
-      if (a.permuted) {  // optional copy of P: reload the unit rather than keep it in registers
-        const int hh = (int)a.h;
-        const int j = (int)e / hh, c = (int)e - j * hh;
-        const u32x4* src = reinterpret_cast<const u32x4*>(x1 + (((int64_t)j * T + t) * a.h + c));
+      if (a.permuted) {  // optional copy of P, straight from the registers
         u32x4* dst = reinterpret_cast<u32x4*>(static_cast<uint16_t*>(a.permuted) + t * cols + e);
-        dst[0] = src[0];
-        dst[1] = src[1];
+        dst[0] = raw[v][0];
+        dst[1] = raw[v][1];
       }
     }
   }
@@ -200,18 +198,30 @@ __global__ __launch_bounds__(kThreads) void permute_quant_scalar(QuantArgs a) {
   }
 }
 
+template <int DT>
+void launch_vec(const QuantArgs& a, int units_per_thread, hipStream_t s) {
+  const unsigned grid = (unsigned)(a.bs / a.r);
+  switch (units_per_thread) {
+    case 1: permute_quant_vec<DT, 1><<<grid, kVecThreads, 0, s>>>(a); break;
+    case 2: permute_quant_vec<DT, 2><<<grid, kVecThreads, 0, s>>>(a); break;
+    default: permute_quant_vec<DT, kMaxUnits><<<grid, kVecThreads, 0, s>>>(a); break;
+  }
+}
+
 }  // namespace
 
 hipError_t launch_permute_quant(const QuantArgs& a, hipStream_t s) {
   const int64_t T = a.bs / a.r;
   const int64_t cols = (int64_t)a.r * a.h;
-  if (T < 1 || cols < 1 || cols > (int64_t)kMaxUnits * kThreads * 16) return hipErrorInvalidValue;
-  const bool vec = a.h % 16 == 0;
+  if (T < 1 || cols < 1) return hipErrorInvalidValue;
+  // vector path when rows split into whole 16-element units and fit 3 units per thread
+  const bool vec = a.h % 16 == 0 && cols <= (int64_t)kMaxUnits * kVecThreads * 16;
+  const int upt = (int)((cols / 16 + kVecThreads - 1) / kVecThreads);
   if (a.dtype == DT_BF16) {
-    if (vec) permute_quant_vec<DT_BF16><<<(unsigned)T, kThreads, 0, s>>>(a);
+    if (vec) launch_vec<DT_BF16>(a, upt, s);
     else permute_quant_scalar<DT_BF16><<<(unsigned)T, kThreads, 0, s>>>(a);
   } else if (a.dtype == DT_F16) {
-    if (vec) permute_quant_vec<DT_F16><<<(unsigned)T, kThreads, 0, s>>>(a);
+    if (vec) launch_vec<DT_F16>(a, upt, s);
     else permute_quant_scalar<DT_F16><<<(unsigned)T, kThreads, 0, s>>>(a);
   } else {
     return hipErrorInvalidValue;
