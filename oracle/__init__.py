@@ -58,6 +58,8 @@ def _load():
             "orc_int8_matmul": (I64, [P, P, I64, I64, I64, P]),
             "orc_dequant": (None, [P, P, P, P, I64, I64, INT, P]),
             "orc_alltoall_quant_matmul": (I64, [P, INT, I64, I64, INT, P, I64, P, P, P, P, P, P, P, P]),
+            "orc_permute_i8": (None, [P, INT, I64, I64, P]),
+            "orc_alltoall_quant_matmul_static": (I64, [P, INT, I64, I64, P, P, I64, P, P, INT, P, P, P]),
             "orc_quant_all_reduce": (INT, [P, P, INT, I64, I64, INT, INT, P, INT]),
             "orc_decode_array": (INT, [INT, I64, P, P]),
             "orc_encode_array": (INT, [INT, I64, P, P]),
@@ -219,6 +221,38 @@ def alltoall_quant_matmul(x1, r: int, x2, x2_scale, smooth=None, bias=None,
     if ovf:
         raise OverflowError(f"{ovf} int32 overflows")
     return {"out": out, "permuted": perm, "q": q, "s1": s1, "acc": acc}
+
+
+def permute_i8(x1: np.ndarray, r: int) -> np.ndarray:
+    """AlltoAll + permute of an int8 (bs, h) x1 into (bs / r, r h)."""
+    x1 = np.ascontiguousarray(x1, dtype=np.int8)
+    bs, h = x1.shape
+    out = np.empty((bs // r, r * h), dtype=np.int8)
+    _load().orc_permute_i8(_ptr(x1), r, bs, h, _ptr(out))
+    return out
+
+
+def alltoall_quant_matmul_static(x1, r: int, x1_scale, x2, x2_scale, bias=None,
+                                 dtype: str = "bf16") -> Dict[str, np.ndarray]:
+    """Full-quant AlltoAllQuantMatmul: x1 int8 (bs, h) with one fp32 scale per
+    permuted token (bs / r); out = (P @ x2) * x1_scale * x2_scale + bias."""
+    x1 = np.ascontiguousarray(x1, dtype=np.int8)
+    x1_scale = np.ascontiguousarray(x1_scale, dtype=np.float32)
+    x2 = np.ascontiguousarray(x2, dtype=np.int8)
+    x2_scale = np.ascontiguousarray(x2_scale, dtype=np.float32)
+    bs, h = x1.shape
+    n = x2.shape[1]
+    rows, cols = bs // r, r * h
+    out = np.empty((rows, n), dtype=_STORAGE[dtype])
+    perm = np.empty((rows, cols), dtype=np.int8)
+    acc = np.empty((rows, n), dtype=np.int32)
+    b = None if bias is None else np.ascontiguousarray(bias)
+    ovf = _load().orc_alltoall_quant_matmul_static(_ptr(x1), r, bs, h, _ptr(x1_scale), _ptr(x2), n,
+                                                   _ptr(x2_scale), _ptr(b), DT[dtype], _ptr(out), _ptr(perm),
+                                                   _ptr(acc))
+    if ovf:
+        raise OverflowError(f"{ovf} int32 overflows")
+    return {"out": out, "permuted": perm, "acc": acc}
 
 
 # ---------------------------------------------------------------- QuantAllReduce

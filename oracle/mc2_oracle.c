@@ -323,6 +323,40 @@ int64_t orc_alltoall_quant_matmul(const uint16_t* x1, int r, int64_t bs, int64_t
   return ovf;
 }
 
+/*
+ * Full-quantisation variant (aclnnAlltoAllQuantMatmul page, "function"
+ * formulas, full-quant case): x1 arrives already int8 with one scale per
+ * token of the permuted matrix, so
+ *   P   = AlltoAll + permute of x1 (int8 bytes, the same addressing as above)
+ *   acc = P @ x2                         (exact, int32)
+ *   out = acc * x1_scale * x2_scale + bias
+ * The page prints the matmul as "x1 @ x2"; since the permute is defined just
+ * before it and the shapes only match after it, the product is read as
+ * P @ x2.  Returns the int32 overflow count.
+ */
+void orc_permute_i8(const int8_t* x1, int r, int64_t bs, int64_t h, int8_t* p) {
+  int64_t t_count = bs / r;
+  for (int64_t t = 0; t < t_count; t++)
+    for (int j = 0; j < r; j++)
+      for (int64_t c = 0; c < h; c++) p[t * (r * h) + j * h + c] = x1[(j * t_count + t) * h + c];
+}
+
+int64_t orc_alltoall_quant_matmul_static(const int8_t* x1, int r, int64_t bs, int64_t h, const float* x1_scale,
+                                         const int8_t* x2, int64_t n, const float* x2_scale, const uint16_t* bias,
+                                         int dtype, uint16_t* out, int8_t* permuted, int32_t* acc_out) {
+  int64_t rows = bs / r, cols = (int64_t)r * h;
+  int8_t* p = (int8_t*)malloc((size_t)(rows * cols));
+  int32_t* acc = (int32_t*)malloc(sizeof(int32_t) * (size_t)(rows * n));
+  orc_permute_i8(x1, r, bs, h, p);
+  int64_t ovf = orc_int8_matmul(p, x2, rows, n, cols, acc);
+  orc_dequant(acc, x1_scale, x2_scale, bias, rows, n, dtype, out);
+  if (permuted) memcpy(permuted, p, (size_t)(rows * cols));
+  if (acc_out) memcpy(acc_out, acc, sizeof(int32_t) * (size_t)(rows * n));
+  free(p);
+  free(acc);
+  return ovf;
+}
+
 /* ------------------------------------------------------------------------ */
 /* [QAR] QuantAllReduce: output = sum over ranks of scale * x.               */
 /* ------------------------------------------------------------------------ */

@@ -275,6 +275,54 @@ def test_alltoall_chain_is_composition_of_steps():
     assert np.max(np.abs(got - ref)) <= 0.02 * np.sqrt(np.mean(ref ** 2)) + 0.01 * np.max(np.abs(ref))
 
 
+def test_permute_i8_is_the_library_transpose():
+    """The byte permute of the full-quant case: the library's reshape/transpose, inverse, r = 1 identity."""
+    rng = np.random.default_rng(17)
+    for r, bs, h in ((2, 6, 5), (4, 8, 16), (8, 16, 3), (1, 5, 7), (8, 8, 128)):
+        x = rng.integers(-128, 128, (bs, h)).astype(np.int8)
+        p = oracle.permute_i8(x, r)
+        assert np.array_equal(p, x.reshape(r, bs // r, h).transpose(1, 0, 2).reshape(bs // r, r * h))
+        assert np.array_equal(p.reshape(bs // r, r, h).transpose(1, 0, 2).reshape(bs, h), x)
+        if r == 1:
+            assert np.array_equal(p, x)
+
+
+def test_static_quant_equals_dynamic_on_its_own_codes():
+    """Full-quant mode fed with the dynamic path's own int8 codes (permuted back to the
+    pre-AlltoAll layout) and its per-token scales reproduces the dynamic output bit for bit:
+    both are permute -> exact int8 matmul -> the same dequant."""
+    r, bs, h, n = 4, 32, 64, 24
+    specs = mc2_inputs.configs.scaled("a16w8", r=r, bs=bs, h=h, n=n)
+    t = mc2_inputs.make(specs, seed=18)
+    dyn = oracle.alltoall_quant_matmul(t["x1"], r, t["x2"], t["x2_scale"], t["x1_smooth"], t["bias"])
+    x1_i8 = dyn["q"].reshape(bs // r, r, h).transpose(1, 0, 2).reshape(bs, h)  # inverse permute (library form)
+    st = oracle.alltoall_quant_matmul_static(x1_i8, r, dyn["s1"], t["x2"], t["x2_scale"], t["bias"])
+    assert np.array_equal(st["permuted"], dyn["q"])
+    assert np.array_equal(st["acc"], dyn["acc"])
+    assert np.array_equal(st["out"].view(np.uint16), dyn["out"].view(np.uint16))
+
+
+def test_static_quant_brute_force_tiny():
+    """Python triple loop over the full-quant formulas: acc exact in Python integers, the
+    dequant rounded once to bf16 from the exact rational value."""
+    rng = np.random.default_rng(19)
+    r, bs, h, n = 2, 4, 3, 5
+    x1 = rng.integers(-127, 128, (bs, h)).astype(np.int8)
+    x2 = rng.integers(-127, 128, (r * h, n)).astype(np.int8)
+    s1 = np.array([0.5, 0.0078125], dtype=np.float32)           # per permuted token
+    s2 = np.array([0.25, 1.0, 2.0, 0.125, 0.0625], dtype=np.float32)
+    bias = enc([1.0, -2.0, 0.5, 0.0, 3.0], "bf16")
+    st = oracle.alltoall_quant_matmul_static(x1, r, s1, x2, s2, bias)
+    T = bs // r
+    for t_ in range(T):
+        for c in range(n):
+            acc = sum(int(x1[j * T + t_, e]) * int(x2[j * h + e, c]) for j in range(r) for e in range(h))
+            assert st["acc"][t_, c] == acc
+            exact = Fraction(acc) * Fraction(float(s1[t_])) * Fraction(float(s2[c])) + \
+                Fraction(float(decode16(bias[c:c + 1], "bf16")[0]))
+            assert int(bits(st["out"])[t_, c]) == round_rne(exact, "bf16")
+
+
 # ----------------------------------------------------------------- QuantAllReduce
 def test_qar_worked_examples():
     w = gold("worked_examples.json")
