@@ -10,6 +10,8 @@ this order (names as in the JSON "rows"):
   colpar_dw    column-parallel backward dW = dY^T (1792, 8192) @ AG(X) (8192, 4096)
   a16w8        AlltoAllQuantMatmul A16W8: permute+quant of bf16 (8192, 4096) on 8 ranks,
                then int8 (1024, 32768) @ (32768, 7168) with per-token x per-channel dequant + bias
+  a8w8         AlltoAllQuantMatmul, full quantisation: int8 (8192, 4096) on 8 ranks with
+               per-token scales, the permute folded into the int8 GEMM's loads, same GEMM
   qar_int8     QuantAllReduce, 8 ranks x int8 (4, 2048, 7168) + fp32 group-128 scales -> fp32
   qar_mx       QuantAllReduce, 8 ranks x E4M3FN (4, 2048, 7168) + E8M0 mx scales -> bf16
 
@@ -40,7 +42,7 @@ PEAK_BF16 = 2500.0     # TFLOP/s, dense MFMA, MI355X
 PEAK_INT8 = 5000.0     # TOP/s, dense MFMA, MI355X
 PEAK_HBM = 8000.0      # GB/s, MI355X HBM3E
 
-ALL_ROWS = ["ag_bf16_tp", "ag_arrival", "colpar_dx", "colpar_dw", "a16w8", "qar_int8", "qar_mx"]
+ALL_ROWS = ["ag_bf16_tp", "ag_arrival", "colpar_dx", "colpar_dw", "a16w8", "a8w8", "qar_int8", "qar_mx"]
 EXTRA_ROWS = ["copy_calib"]
 COPY_CALIB_BYTES = 256 << 20
 
@@ -149,6 +151,20 @@ def setup_rows(names, mc2, torch):
         row.bytes = 2 * bs * h + 2 * cols + cols * n + 4 * n + 2 * n + 2 * rows_ * n
         row.check = lambda t=t, d=d, out=out: check_a16w8(t, d, out, mc2, torch)
         rows[row.name] = row
+    if "a8w8" in names:
+        seed, d, specs = mc2_inputs.CONFIGS["a8w8"]
+        t = mc2_inputs.make("a8w8")
+        r, bs, h, n = d["r"], d["bs"], d["h"], d["n"]
+        x1, s1, x2 = T(t["x1"], "i8"), T(t["x1_scale"], "f32"), T(t["x2"], "i8")
+        s2, bias = T(t["x2_scale"], "f32"), T(t["bias"], "bf16")
+        rows_, cols = bs // r, r * h
+        out = torch.empty((rows_, n), dtype=torch.bfloat16, device="cuda")
+        row = Row("a8w8", "TOP/s", "mfma", PEAK_INT8, 2.0 * rows_ * cols * n,
+                  [("gemm_i8", lambda x1=x1, r=r, s1=s1, x2=x2, s2=s2, bias=bias, out=out:
+                    mc2.mc2_alltoall_quant_matmul_static(x1, r, s1, x2, s2, bias, out=out))])
+        row.bytes = bs * h + 4 * rows_ + cols * n + 4 * n + 2 * n + 2 * rows_ * n
+        row.check = lambda t=t, d=d, out=out: check_a8w8(t, d, out)
+        rows[row.name] = row
     for name, xdt, sdt, odt in (("qar_int8", "i8", "f32", torch.float32), ("qar_mx", "e4m3fn", "e8m0", torch.bfloat16)):
         if name not in names:
             continue
@@ -229,6 +245,19 @@ def check_a16w8(t, d, out, mc2, torch):
     q, s1 = oracle.smooth_quant(np.ascontiguousarray(p[toks]), t["x1_smooth"])
     acc = oracle.int8_matmul(q, t["x2"])
     want = oracle.dequant(acc, s1, t["x2_scale"], t["bias"])
+    return _tol16(mc2_inputs.from_torch(out)[toks], want, "bf16")
+
+
+def check_a8w8(t, d, out):
+    import numpy as np
+
+    import mc2_inputs
+    import oracle
+    rng = np.random.default_rng(4)
+    toks = np.sort(rng.choice(d["bs"] // d["r"], 6, replace=False))
+    p = oracle.permute_i8(t["x1"], d["r"])
+    acc = oracle.int8_matmul(np.ascontiguousarray(p[toks]), t["x2"])
+    want = oracle.dequant(acc, t["x1_scale"][toks], t["x2_scale"], t["bias"])
     return _tol16(mc2_inputs.from_torch(out)[toks], want, "bf16")
 
 
@@ -351,7 +380,7 @@ def summarize(d, write_traffic):
                      ", ".join(f"{c} {v:.4f}" for c, v in scale.items()) + "\n")
     print("\n".join(lines))
     if write_traffic:
-        ag = [k for k in counters if k.startswith("gemm16_kernel<128, 224, true, false, true, 2>")]
+        ag = [k for k in counters if k.startswith("gemm16_kernel<128, 224, true, false, true, 2, false>")]
         if not ag or not all(c in counters[ag[0]] for c in ("FETCH_SIZE", "WRITE_SIZE")):
             raise SystemExit("no FETCH_SIZE / WRITE_SIZE for the AllGatherMatmul kernel in " + d)
         cs = counters[ag[0]]
@@ -450,10 +479,10 @@ def main():
         "metric": "TFLOPS/TOPS (% MFMA peak) for AG-GEMM & A16W8; GB/s for dequant-sum",
         "value": h["achieved"], "unit": h["unit"], "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": round(wall / args.steps * 1e3, 3), "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": "bf16" if head != "a16w8" else "int8", "data": "synthetic",
+        "vs_baseline": None, "dtype": "int8" if head in ("a16w8", "a8w8") else "bf16", "data": "synthetic",
         "config": {"workload": {"ag_bf16_tp": "AllGatherMatmul bf16 TP layer: 8 x (512, 4096) shards @ (4096, 1792)",
                                 }.get(head, head),
-                   "rows_in_step": [r.name for r in rows], "seeds": "workload number (1..5)"},
+                   "rows_in_step": [r.name for r in rows], "seeds": "workload number (1..6)"},
         "roofline": {"bound": h["bound"], "achieved": h["achieved"], "peak": h["peak"],
                      "unit": "TFLOP/s" if h["unit"] == "TFLOP/s" else h["unit"], "frac": h["frac"],
                      "traffic": stored_traffic() if head == "ag_bf16_tp" else None,

@@ -8,7 +8,7 @@ raises.
 
 Functions carry the C names:
   mc2_allgather_matmul, mc2_allgather_arrival_fallbacks, mc2_matmul_grad_input, mc2_matmul_grad_weight,
-  mc2_alltoall_quant_matmul_workspace_size, mc2_alltoall_quant_matmul,
+  mc2_alltoall_quant_matmul_workspace_size, mc2_alltoall_quant_matmul, mc2_alltoall_quant_matmul_static,
   mc2_quant_all_reduce, mc2_status_string, mc2_last_error.
 """
 from __future__ import annotations
@@ -56,6 +56,7 @@ _SIGS = {
                                   _P, ctypes.c_size_t, _P],
     "mc2_quant_all_reduce": [_P, _P, _INT, _I64, _I64, _INT, _INT, _P, _INT, _P],
     "mc2_allgather_arrival_fallbacks": [_INT, ctypes.POINTER(ctypes.c_uint)],
+    "mc2_alltoall_quant_matmul_static": [_P, _INT, _I64, _I64, _P, _P, _I64, _P, _P, _P, _INT, _P, _P, _P],
 }
 for _name, _args in _SIGS.items():
     _f = getattr(_lib, _name)
@@ -204,6 +205,30 @@ def mc2_alltoall_quant_matmul(x1: torch.Tensor, rank_size: int, x2: torch.Tensor
     return out
 
 
+def mc2_alltoall_quant_matmul_static(x1: torch.Tensor, rank_size: int, x1_scale: torch.Tensor, x2: torch.Tensor,
+                                     x2_scale: torch.Tensor, bias: Optional[torch.Tensor] = None, *,
+                                     out_dtype: torch.dtype = torch.bfloat16, out: Optional[torch.Tensor] = None,
+                                     permuted_out: Optional[torch.Tensor] = None,
+                                     acc_out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Full-quant AlltoAllQuantMatmul: x1 int8 (bs, h), x1_scale fp32 (bs / rank_size);
+    out = (P @ x2) * x1_scale * x2_scale + bias with P the permuted x1."""
+    bs, h = x1.shape
+    n = x2.shape[1]
+    rows = bs // rank_size
+    if out is None:
+        out = torch.empty((rows, n), dtype=out_dtype, device=x1.device)
+    if x1.dtype != torch.int8 or x2.dtype != torch.int8:
+        raise TypeError("x1 and x2 must be int8")
+    if x1_scale.numel() != rows or x2_scale.numel() != n:
+        raise ValueError("x1_scale must hold bs / rank_size scales and x2_scale n")
+    _check(_lib.mc2_alltoall_quant_matmul_static(_dev(x1, "x1"), rank_size, bs, h, _dev(x1_scale, "x1_scale"),
+                                                 _dev(x2, "x2"), n, _dev(x2_scale, "x2_scale"),
+                                                 _opt(bias, "bias"), _dev(out, "out"), _dt(out),
+                                                 _opt(permuted_out, "permuted_out"), _opt(acc_out, "acc_out"),
+                                                 _stream(stream)))
+    return out
+
+
 # ------------------------------------------------------------------ QuantAllReduce
 def mc2_quant_all_reduce(x: Sequence[torch.Tensor], scales: Sequence[torch.Tensor], *,
                          out_dtype: torch.dtype = torch.float32, out: Optional[torch.Tensor] = None,
@@ -232,6 +257,7 @@ def mc2_quant_all_reduce(x: Sequence[torch.Tensor], scales: Sequence[torch.Tenso
 
 __all__ = [
     "mc2_allgather_matmul", "mc2_allgather_arrival_fallbacks", "mc2_matmul_grad_input", "mc2_matmul_grad_weight",
-    "mc2_alltoall_quant_matmul_workspace_size", "mc2_alltoall_quant_matmul", "mc2_quant_all_reduce",
+    "mc2_alltoall_quant_matmul_workspace_size", "mc2_alltoall_quant_matmul", "mc2_alltoall_quant_matmul_static",
+    "mc2_quant_all_reduce",
     "mc2_status_string", "mc2_last_error", "Mc2Error", "LIB_PATH",
 ]

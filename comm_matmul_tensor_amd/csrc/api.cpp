@@ -357,4 +357,41 @@ mc2_status mc2_alltoall_quant_matmul(const void* x1, int rank_size, int64_t bs, 
   return MC2_OK;
 }
 
+mc2_status mc2_alltoall_quant_matmul_static(const int8_t* x1, int rank_size, int64_t bs, int64_t h,
+                                            const float* x1_scale, const int8_t* x2, int64_t n,
+                                            const float* x2_scale, const void* bias, void* out,
+                                            mc2_dtype out_dtype, int8_t* permuted_out, int32_t* acc_out,
+                                            void* stream) {
+  clear_error();
+  mc2_status s = check_alltoall_quant_matmul_static(x1, rank_size, bs, h, x1_scale, x2, n, x2_scale, bias, out,
+                                                    out_dtype, permuted_out, acc_out);
+  if (s != MC2_OK) return s;
+  int dev;
+  if ((s = current_device(&dev)) != MC2_OK) return s;
+  // The AlltoAll permute is the GEMM's addressing of A: row t of P is the r
+  // segments x1[(j T + t) h : + h], j = 0..r-1, so A = x1 with K split into
+  // r segments of h elements, T h bytes apart.
+  const int64_t rows = bs / rank_size, cols = (int64_t)rank_size * h;
+  GemmI8Args ga{};
+  ga.a = x1;
+  ga.a_ld = h;
+  ga.kseg = h;
+  ga.kseg_stride = rows * h;
+  ga.a_bytes = bs * h;
+  ga.permuted_out = permuted_out;
+  ga.b = x2;
+  ga.s1 = x1_scale;
+  ga.s2 = x2_scale;
+  ga.bias = bias;
+  ga.out = out;
+  ga.acc_out = acc_out;
+  ga.m = rows;
+  ga.n = n;
+  ga.k = cols;
+  ga.dtype = dt(out_dtype);
+  hipError_t e = launch_gemm_i8(ga, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "alltoall_quant_matmul_static launch");
+  return MC2_OK;
+}
+
 }  // extern "C"

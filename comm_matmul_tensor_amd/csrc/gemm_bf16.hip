@@ -105,6 +105,10 @@ hipError_t launch_dt(const GemmArgs& g, hipStream_t s) {
   p.m = g.m;
   p.n = g.n;
   p.k = g.k;
+  p.a_ld = g.k * 2;  // plain A: one K segment
+  p.kseg = g.k;
+  p.kseg_stride = 0;
+  p.a_part_bytes = g.rows_per_part * g.k * 2;
   if (g.ready_flags) {  // arrival emulation: A arrives in gather_out, which the kernel only reads
     p.ready = g.ready_flags;
     p.ready_value = g.ready_value;

@@ -76,8 +76,10 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_i8_kernel(Problem p, GemmI8A
 template <int BM, int BN, int DT>
 hipError_t launch_cfg(Problem p, const GemmI8Args& g, hipStream_t s) {
   const int64_t tiles = ((p.m + BM - 1) / BM) * ((p.n + BN - 1) / BN);
-  // 16-byte vector access and the buffer-load staging (operands below 2 GiB)
-  const bool vec = (p.k % 16 == 0) && (p.n % 16 == 0) && dma_buffers_ok(p.m * p.k, p.k * p.n, 1, p.m);
+  // 16-byte vector access, the buffer-load staging (operands below 2 GiB)
+  // and, for a segmented A, segments of whole K steps (128 bytes)
+  const bool vec = (p.k % 16 == 0) && (p.n % 16 == 0) && (p.kseg == p.k || p.kseg % 128 == 0) &&
+                   (p.a_ld % 16 == 0) && dma_buffers_ok(p.a_part_bytes, p.k * p.n, 1, p.m);
   p.tile_order_cols = prefer_column_order(p.m, p.n, p.k, 1) ? 1 : 0;
   p.tile_group = choose_tile_group(p.m, p.n, BM, BN, p.tile_order_cols);
   if (vec) gemm_i8_kernel<BM, BN, true, DT><<<(unsigned)tiles, kThreads, 0, s>>>(p, g);
@@ -94,6 +96,18 @@ hipError_t launch_dt(const GemmI8Args& g, hipStream_t s) {
   p.m = g.m;
   p.n = g.n;
   p.k = g.k;
+  if (g.kseg > 0 && g.kseg < g.k) {  // A's K split into segments stored apart
+    p.a_ld = g.a_ld;
+    p.kseg = g.kseg;
+    p.kseg_stride = g.kseg_stride;
+    p.a_part_bytes = g.a_bytes;
+  } else {
+    p.a_ld = g.k;
+    p.kseg = g.k;
+    p.kseg_stride = 0;
+    p.a_part_bytes = g.m * g.k;
+  }
+  p.gather_out = g.permuted_out;
   static const TileChoice cands[] = {{128, 224}, {224, 128}, {128, 128}};
   switch (pick_tile(p.m, p.n, cands, 3)) {
     case 0: return launch_cfg<128, 224, DT>(p, g, s);

@@ -73,6 +73,12 @@ struct Problem {
   const void* b;
   void* gather_out;       // optional copy of the gathered A
   int64_t m, n, k;
+  // K-contiguous A, general form: element (row, kk) of A lies at
+  //   a_parts[block of row] + (kk / kseg) kseg_stride + (row in block) a_ld + (kk % kseg) E
+  // (kseg = k, kseg_stride = 0 for a plain matrix; kseg < k addresses an A
+  // whose K is split into segments stored apart, as the AlltoAll permute
+  // does).  a_part_bytes: bytes of one row block's buffer.
+  int64_t a_ld, kseg, kseg_stride, a_part_bytes;
   int tile_order_cols;
   int tile_group;         // tile rows (columns with tile_order_cols) per group of the tile order
   // Arrival emulation (ready == NULL: off).  A arrives in `arrived` (the
@@ -243,6 +249,8 @@ struct RegLoaderK {
   __device__ __forceinline__ static int row_of(int i) { return (threadIdx.x + i * kThreads) / 8; }
   __device__ __forceinline__ static int chunk_of(int i) { return (threadIdx.x + i * kThreads) % 8; }
 
+  int64_t kseg = 0, kseg_stride = 0;  // K segments (kseg = 0: one segment)
+
   __device__ __forceinline__ void init(const void* const* parts, int64_t rows_per_part, int64_t ld_bytes,
                                        int64_t mn_ext_, int64_t k_ext_, int64_t mn0_) {
     k_ext = k_ext_;
@@ -261,6 +269,16 @@ struct RegLoaderK {
       r[i] = u32x4{0u, 0u, 0u, 0u};
       if (mn0 + row_of(i) >= mn_ext) continue;
       const int64_t gk = k0 + CH * chunk_of(i);
+      if (kseg > 0 && kseg < k_ext) {  // segmented K: element by element
+        T e[CH];
+#pragma unroll
+        for (int x = 0; x < CH; x++) {
+          const int64_t g = gk + x, sg = g / kseg;
+          e[x] = g < k_ext ? *(reinterpret_cast<const T*>(row_ptr[i] + sg * kseg_stride) + (g - sg * kseg)) : (T)0;
+        }
+        r[i] = __builtin_bit_cast(u32x4, e);
+        continue;
+      }
       const T* p = reinterpret_cast<const T*>(row_ptr[i]) + gk;
       if (gk + CH <= k_ext && (k_ext % CH) == 0) {
         r[i] = *reinterpret_cast<const u32x4*>(p);
@@ -391,8 +409,9 @@ struct DmaOperand {
 
   // K-contiguous operand: row r of the tile is matrix row mn0 + r, found in
   // the row blocks `parts` (rows_per_part rows each, ld_bytes per row).
+  // part_bytes: bytes of each row block's buffer (the resource size).
   __device__ __forceinline__ void init_k(const void* const* parts, int64_t rows_per_part, int64_t ld_bytes,
-                                         int64_t mn0, int64_t mn_ext) {
+                                         int64_t mn0, int64_t mn_ext, int64_t part_bytes) {
     const int w = __builtin_amdgcn_readfirstlane((int)(threadIdx.x / 64));
     lds_wave = 1024 * w;
 #pragma unroll
@@ -403,7 +422,7 @@ struct DmaOperand {
       int64_t g0 = mn0 + 32 * i + 8 * w;
       g0 = g0 < mn_ext ? g0 : mn_ext - 1;
       const int64_t part = g0 / rows_per_part;
-      rsrc[i] = make_rsrc(parts[part], rows_per_part * ld_bytes);
+      rsrc[i] = make_rsrc(parts[part], part_bytes);
       voff[i] = (uint32_t)((r - part * rows_per_part) * ld_bytes + c * 16);
     }
     step_bytes = kRowBytes;
@@ -538,15 +557,15 @@ __device__ __forceinline__ void mainloop_fast(const Problem& p, int64_t m0, int6
   DB db;
   if constexpr (ARR) {
     const void* arrived[1] = {p.arrived};
-    da.init_k(arrived, p.m, p.k * E, m0, p.m);
+    da.init_k(arrived, p.m, p.k * E, m0, p.m, p.m * p.k * E);
   } else if constexpr (AK) {
-    da.init_k(p.a_parts, p.rows_per_part, p.k * E, m0, p.m);
+    da.init_k(p.a_parts, p.rows_per_part, p.a_ld, m0, p.m, p.a_part_bytes);
   } else {
     da.init_mn(p.a_parts[0], p.m * E, p.k, m0, p.m);
   }
   if constexpr (BKM) {
     const void* bparts[1] = {p.b};
-    db.init_k(bparts, p.n, p.k * E, n0, p.n);
+    db.init_k(bparts, p.n, p.k * E, n0, p.n, p.n * p.k * E);
   } else {
     db.init_mn(p.b, p.n * E, p.k, n0, p.n);
   }
@@ -569,15 +588,31 @@ __device__ __forceinline__ void mainloop_fast(const Problem& p, int64_t m0, int6
     if (fell_back) return;
     if (!wait_flag(flags + kt / sps, p.ready_value)) {
       fell_back = true;
-      da.init_k(p.a_parts, p.rows_per_part, p.k * E, m0, p.m);
+      da.init_k(p.a_parts, p.rows_per_part, p.a_ld, m0, p.m, p.a_part_bytes);
       if (threadIdx.x % 64 == 0) __hip_atomic_fetch_add(p.fallbacks, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  };
+
+  // A's offset of the next step to be loaded: steps go through K segment by
+  // segment (one segment, kseg = k, for a plain or an M-contiguous A)
+  const int seg_steps = (int)(p.kseg / BK);
+  int64_t a_next = 0, seg_base = 0;
+  int seg_left = seg_steps;
+  auto advance_a = [&]() {
+    if (--seg_left == 0) {
+      seg_base += p.kseg_stride;
+      a_next = seg_base;
+      seg_left = seg_steps;
+    } else {
+      a_next += da.step_bytes;
     }
   };
 
   u32x4 fa0[FM], fb0[FN], fa1[FM], fb1[FN];
   auto dma = [&](uint8_t* L, int kt) {
-    da.issue(L, kt * da.step_bytes);
+    da.issue(L, a_next);
     db.issue(L + kATile, kt * db.step_bytes);
+    advance_a();
   };
   // One K half: the FM x FN MFMAs on (fa, fb), with DMA instructions
   // [d0, d1) of step kt_dma (when dma_on) and the FM + FN fragment reads of
@@ -591,7 +626,7 @@ __device__ __forceinline__ void mainloop_fast(const Problem& p, int64_t m0, int6
     constexpr int D0 = decltype(D0_)::value, D1 = decltype(D1_)::value;
     constexpr int NM = FM * FN, NF = FM + FN, NDH = D1 - D0;
     constexpr int kTail = NM >= 2 * NF ? NM - 2 * NF < 8 ? NM - 2 * NF : 8 : 0;
-    const int64_t offa = (int64_t)kt_dma * da.step_bytes, offb = (int64_t)kt_dma * db.step_bytes;
+    const int64_t offa = a_next, offb = (int64_t)kt_dma * db.step_bytes;
 #pragma unroll
     for (int q = 0; q < NM; q++) {
       acc[q / FN][q % FN] = Ops::mfma(fa[q / FN], fb[q % FN], acc[q / FN][q % FN]);
@@ -638,6 +673,7 @@ __device__ __forceinline__ void mainloop_fast(const Problem& p, int64_t m0, int6
     // half 0 of step kt; the DMA of step kt+2 (its stage was last read
     // before the previous barrier); reads of half 1 of step kt
     half(fa0, fb0, C0(), CD(), dma2, nn, kt + 2, true, cur, 1, fa1, fb1);
+    if (dma2) advance_a();
     // the DMA of step kt+1 (issued during step kt-1) has landed; only this
     // step's may still fly
     if (dma2) wait_vmcnt<ND>();
@@ -693,8 +729,13 @@ __device__ __forceinline__ void mainloop_checked(const Problem& p, int64_t m0, i
   constexpr int NB = BKM ? BN / 32 : 16 / E;
   LA la;
   LB lb;
-  if constexpr (AK) la.init(p.a_parts, p.rows_per_part, p.k * E, p.m, p.k, m0);
-  else la.init(p.a_parts[0], p.m, m0);
+  if constexpr (AK) {
+    la.init(p.a_parts, p.rows_per_part, p.a_ld, p.m, p.k, m0);
+    la.kseg = p.kseg;
+    la.kseg_stride = p.kseg_stride;
+  } else {
+    la.init(p.a_parts[0], p.m, m0);
+  }
   const void* bparts[1] = {p.b};
   if constexpr (BKM) lb.init(bparts, p.n, p.k * E, p.n, p.k, n0);
   else lb.init(p.b, p.n, n0);
@@ -747,7 +788,7 @@ __device__ __forceinline__ void run_mainloop(const Problem& p, int64_t m0, int64
   constexpr int BK = kRowBytes / E;
   const int gather_every = (AK && !ARR && p.gather_out != nullptr) ? tiles_n : 0;
   if constexpr (VEC) {
-    if (p.k % BK == 0) {
+    if (p.k % BK == 0 && p.kseg % BK == 0) {  // whole steps, each inside one K segment
       if constexpr (ARR) mainloop_fast<E, BM, BN, AK, BKM, false, true, Ops>(p, m0, n0, tn, 0, L0, L1, L2, acc);
       else if (AK && gather_every > 0)
         mainloop_fast<E, BM, BN, AK, BKM, AK, false, Ops>(p, m0, n0, tn, gather_every, L0, L1, L2, acc);

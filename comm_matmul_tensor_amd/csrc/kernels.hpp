@@ -91,7 +91,11 @@ hipError_t launch_permute_quant(const QuantArgs& a, hipStream_t s);
 
 // ---- K3: int8 GEMM with the fused dequant epilogue
 struct GemmI8Args {
-  const int8_t* a;       // (m, k) row-major
+  // A (m, k): element (row, kk) at a + (kk / kseg) kseg_stride + row a_ld + kk % kseg
+  // (kseg = 0: a plain row-major (m, k) matrix)
+  const int8_t* a;
+  int64_t a_ld, kseg, kseg_stride, a_bytes;
+  void* permuted_out;    // optional (m, k) copy of A as the GEMM reads it
   const int8_t* b;       // (k, n) row-major
   const float* s1;       // (m)
   const float* s2;       // (n)

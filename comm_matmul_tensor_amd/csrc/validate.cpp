@@ -123,6 +123,25 @@ mc2_status check_alltoall_quant_matmul(const void* x1, int rank_size, int64_t bs
   return MC2_OK;
 }
 
+mc2_status check_alltoall_quant_matmul_static(const void* x1, int rank_size, int64_t bs, int64_t h,
+                                              const void* x1_scale, const void* x2, int64_t n,
+                                              const void* x2_scale, const void* bias, const void* out,
+                                              mc2_dtype out_dtype, const void* permuted_out,
+                                              const void* acc_out) {
+  // x1, x2, x2Scale and output must not be NULL ("constraints"); the
+  // full-quant formulas also need x1's per-token scale
+  if (!x1 || !x1_scale || !x2 || !x2_scale || !out)
+    return fail(MC2_ERR_NULL, "alltoall_quant_matmul_static: x1, x1_scale, x2, x2_scale and out are required");
+  mc2_status s = check_alltoall_sizes(rank_size, bs, h, n);
+  if (s != MC2_OK) return s;
+  if (!is_half(out_dtype))
+    return fail(MC2_ERR_DTYPE, "alltoall_quant_matmul_static: out must be F16 or BF16");
+  const void* ptrs[] = {x1, x1_scale, x2, x2_scale, bias, out, permuted_out, acc_out};
+  for (const void* p : ptrs)
+    if (p && !aligned16(p)) return fail(MC2_ERR_ALIGN, "alltoall_quant_matmul_static: tensor not 16-byte aligned");
+  return MC2_OK;
+}
+
 mc2_status check_quant_all_reduce(const void* const* x, const void* const* scales, int world_size,
                                   int64_t rows, int64_t h, mc2_dtype x_dtype,
                                   mc2_dtype scale_dtype, const void* out, mc2_dtype out_dtype) {

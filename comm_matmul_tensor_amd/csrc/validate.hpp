@@ -30,6 +30,11 @@ mc2_status check_alltoall_quant_matmul(const void* x1, int rank_size, int64_t bs
                                        const void* q_out, const void* x1_scale_out,
                                        const void* acc_out, const void* workspace,
                                        size_t workspace_bytes, size_t workspace_needed);
+mc2_status check_alltoall_quant_matmul_static(const void* x1, int rank_size, int64_t bs, int64_t h,
+                                              const void* x1_scale, const void* x2, int64_t n,
+                                              const void* x2_scale, const void* bias, const void* out,
+                                              mc2_dtype out_dtype, const void* permuted_out,
+                                              const void* acc_out);
 mc2_status check_quant_all_reduce(const void* const* x, const void* const* scales, int world_size,
                                   int64_t rows, int64_t h, mc2_dtype x_dtype,
                                   mc2_dtype scale_dtype, const void* out, mc2_dtype out_dtype);

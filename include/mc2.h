@@ -187,6 +187,33 @@ mc2_status mc2_alltoall_quant_matmul(const void* x1, int rank_size, int64_t bs, 
                                      void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * AlltoAllQuantMatmul, full quantisation (x1 mode 3, per-token; x2 mode 2,
+ * per-channel) -- aclnnAlltoAllQuantMatmul page, "function" formulas, the
+ * full-quant case: x1 arrives already int8, with one scale per token.
+ *   P      = AlltoAll(x1.view(rank_size, bs / rank_size, h)).permute(1, 0, 2)
+ *            .view(bs / rank_size, rank_size h)           (int8 bytes)
+ *   acc    = P @ x2                                        exact int32
+ *   out    = acc * x1_scale * x2_scale + bias              fp32, rounded once
+ * The page prints the product as "x1 @ x2"; it is read as P @ x2 (the
+ * permute is defined just before it and only P has matching shapes).
+ * x1_scale holds one fp32 scale per token of P.  The permute is the GEMM's
+ * load addressing: nothing is materialised and no workspace is needed.
+ *
+ * x1          (bs, h) int8; sizes as for mc2_alltoall_quant_matmul
+ * x1_scale    (bs / rank_size) fp32
+ * x2          (rank_size h, n) int8, row-major, contiguous
+ * x2_scale    (n) fp32 per-channel scale
+ * bias        (n) of out_dtype, or NULL for a zero bias
+ * out         (bs / rank_size, n) of out_dtype (MC2_BF16 or MC2_F16)
+ * permuted_out, acc_out: optional (NULL) copies of P (int8) and acc (int32)
+ */
+mc2_status mc2_alltoall_quant_matmul_static(const int8_t* x1, int rank_size, int64_t bs, int64_t h,
+                                            const float* x1_scale, const int8_t* x2, int64_t n,
+                                            const float* x2_scale, const void* bias, void* out,
+                                            mc2_dtype out_dtype, int8_t* permuted_out, int32_t* acc_out,
+                                            void* stream);
+
+/*
  * QuantAllReduce -- QuantAllReduce README ("function" formula, parameter
  * table, constraints):
  *   out = sum over ranks i of dequant(x[i])   with dequant = x * its scale

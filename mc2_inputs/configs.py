@@ -21,6 +21,11 @@ shapes:
 5 ``qar_mx``      QuantAllReduce over 8 ranks, x FLOAT8_E4M3FN from N(0, 1)
                   with saturation, E8M0 scales (4, 2048, 112, 2) with
                   exponents U{-8..0}.
+6 ``a8w8``        AlltoAllQuantMatmul, full quantisation: x1 int8 (8192, 4096)
+                  in U{-127..127} seen as (8, 1024, 4096), one fp32 scale per
+                  permuted token (1024) in U(0.02, 0.04) (absmax / 127 of a
+                  unit-normal row of 32768 values is about 0.034), x2 int8
+                  (32768, 7168), x2 scale and bias as in ``a16w8``.
 """
 from __future__ import annotations
 
@@ -50,6 +55,16 @@ def _a16w8(r, bs, h, n):
     return {
         "x1": TensorSpec(0, (bs, h), "normal", 0.0, 1.0, "bf16"),
         "x1_smooth": TensorSpec(1, (r * h,), "uniform", 0.5, 2.0, "bf16"),
+        "x2": TensorSpec(2, (r * h, n), "int", -127, 127, "i8"),
+        "x2_scale": TensorSpec(3, (n,), "uniform", 1e-3, 1e-2, "f32"),
+        "bias": TensorSpec(4, (n,), "normal", 0.0, 1.0, "bf16"),
+    }
+
+
+def _a8w8(r, bs, h, n):
+    return {
+        "x1": TensorSpec(0, (bs, h), "int", -127, 127, "i8"),
+        "x1_scale": TensorSpec(1, (bs // r,), "uniform", 0.02, 0.04, "f32"),
         "x2": TensorSpec(2, (r * h, n), "int", -127, 127, "i8"),
         "x2_scale": TensorSpec(3, (n,), "uniform", 1e-3, 1e-2, "f32"),
         "bias": TensorSpec(4, (n,), "normal", 0.0, 1.0, "bf16"),
@@ -90,6 +105,7 @@ CONFIGS: Dict[str, tuple] = {
     "colpar_bwd": (4, {"m": 8192, "n_local": 1792, "k": 4096}, _bwd(8192, 1792, 4096)),
     "qar_int8": (5, {"r": 8, "shape": (4, 2048, 7168)}, _qar_int8(8, (4, 2048, 7168))),
     "qar_mx": (5, {"r": 8, "shape": (4, 2048, 7168)}, _qar_mx(8, (4, 2048, 7168))),
+    "a8w8": (6, {"r": 8, "bs": 8192, "h": 4096, "n": 7168}, _a8w8(8, 8192, 4096, 7168)),
 }
 
 
@@ -100,6 +116,8 @@ def scaled(kind: str, **dims):
                    dims.get("x2_std", 1.0))
     if kind == "a16w8":
         return _a16w8(dims["r"], dims["bs"], dims["h"], dims["n"])
+    if kind == "a8w8":
+        return _a8w8(dims["r"], dims["bs"], dims["h"], dims["n"])
     if kind == "bwd":
         return _bwd(dims["m"], dims["n_local"], dims["k"])
     if kind == "qar_int8":

@@ -31,7 +31,7 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     names = _declared()
-    assert len(names) == 9, names
+    assert len(names) == 10, names
     for n in names:
         assert hasattr(lib, n), n
 
@@ -118,6 +118,29 @@ def test_alltoall_validation(lib):
     assert f(*bad) == 5                                    # workspace too small
     bad = list(args); bad[4] = 0
     assert f(*bad) == 3                                    # fp32 activations
+
+
+def test_alltoall_static_validation(lib):
+    f = lib.mc2_alltoall_quant_matmul_static
+    f.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p,
+                  ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                  ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+    args = [A, 8, 64, 256, B, C, 32, B, None, A, 2, None, None, None]
+    for i in (0, 4, 5, 7, 9):                              # x1, x1_scale, x2, x2_scale, out
+        bad = list(args); bad[i] = None
+        assert f(*bad) == 1
+    bad = list(args); bad[1] = 3
+    assert f(*bad) == 2                                    # rank_size 3
+    bad = list(args); bad[2] = 60
+    assert f(*bad) == 2                                    # bs not divisible by rank_size
+    bad = list(args); bad[3] = 4376
+    assert f(*bad) == 2                                    # rank_size*h above 35000
+    bad = list(args); bad[6] = 0
+    assert f(*bad) == 2                                    # empty
+    bad = list(args); bad[10] = 0
+    assert f(*bad) == 3                                    # fp32 out
+    bad = list(args); bad[11] = ctypes.c_void_p(0x10008)
+    assert f(*bad) == 8                                    # permuted_out misaligned
 
 
 def test_quant_all_reduce_validation(lib):
