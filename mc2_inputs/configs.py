@@ -26,6 +26,14 @@ shapes:
                   permuted token (1024) in U(0.02, 0.04) (absmax / 127 of a
                   unit-normal row of 32768 values is about 0.034), x2 int8
                   (32768, 7168), x2 scale and bias as in ``a16w8``.
+7 ``rs_fwd``      MatmulReduceScatter, row-parallel forward of the same TP layer,
+                  one rank of 8: x bf16 (4096, 1792), w bf16 (4096, 1792) in
+                  nn.Linear (out, in) layout with std 0.02 (x2 = w^T), and the
+                  7 partial blocks (512, 4096) the other ranks send, bf16 with
+                  the partials' std 0.02 sqrt(1792) = 0.85 (recv0 unused: rank 0).
+8 ``rs_dx``       MatmulReduceScatter completing the column-parallel dX: dY bf16
+                  (8192, 1792), W bf16 (1792, 4096) with std 0.02, blocks
+                  (1024, 4096) with std 0.85 (rank 0).
 """
 from __future__ import annotations
 
@@ -71,6 +79,16 @@ def _a8w8(r, bs, h, n):
     }
 
 
+def _rs(r, m, k, n, x2_trans, w_std=0.02):
+    specs = {
+        "x": TensorSpec(0, (m, k), "normal", 0.0, 1.0, "bf16"),
+        "x2": TensorSpec(1, (n, k) if x2_trans else (k, n), "normal", 0.0, w_std, "bf16"),
+    }
+    for j in range(r):
+        specs[f"recv{j}"] = TensorSpec(2 + j, (m // r, n), "normal", 0.0, w_std * float(np.sqrt(k)), "bf16")
+    return specs
+
+
 def _bwd(m, n_local, k):
     return {
         "dy": TensorSpec(0, (m, n_local), "normal", 0.0, 1.0, "bf16"),
@@ -106,6 +124,10 @@ CONFIGS: Dict[str, tuple] = {
     "qar_int8": (5, {"r": 8, "shape": (4, 2048, 7168)}, _qar_int8(8, (4, 2048, 7168))),
     "qar_mx": (5, {"r": 8, "shape": (4, 2048, 7168)}, _qar_mx(8, (4, 2048, 7168))),
     "a8w8": (6, {"r": 8, "bs": 8192, "h": 4096, "n": 7168}, _a8w8(8, 8192, 4096, 7168)),
+    "rs_fwd": (7, {"r": 8, "rank": 0, "m": 4096, "k": 1792, "n": 4096, "x2_trans": True},
+               _rs(8, 4096, 1792, 4096, True)),
+    "rs_dx": (8, {"r": 8, "rank": 0, "m": 8192, "k": 1792, "n": 4096, "x2_trans": False},
+              _rs(8, 8192, 1792, 4096, False)),
 }
 
 
@@ -118,6 +140,8 @@ def scaled(kind: str, **dims):
         return _a16w8(dims["r"], dims["bs"], dims["h"], dims["n"])
     if kind == "a8w8":
         return _a8w8(dims["r"], dims["bs"], dims["h"], dims["n"])
+    if kind == "rs":
+        return _rs(dims["r"], dims["m"], dims["k"], dims["n"], dims["x2_trans"], dims.get("w_std", 0.02))
     if kind == "bwd":
         return _bwd(dims["m"], dims["n_local"], dims["k"])
     if kind == "qar_int8":

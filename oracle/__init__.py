@@ -53,6 +53,7 @@ def _load():
             "orc_allgather": (None, [P, INT, I64, I64, P]),
             "orc_matmul": (None, [P, INT, P, INT, I64, I64, I64, INT, P]),
             "orc_allgather_matmul": (None, [P, INT, I64, I64, P, I64, INT, INT, P, P]),
+            "orc_matmul_reduce_scatter": (None, [P, P, INT, INT, INT, I64, I64, I64, P, INT, P, P]),
             "orc_permute": (None, [P, INT, I64, I64, P]),
             "orc_smooth_quant": (None, [P, I64, I64, P, INT, P, P]),
             "orc_int8_matmul": (I64, [P, P, I64, I64, I64, P]),
@@ -159,6 +160,29 @@ def matmul_grad_weight(dy: np.ndarray, ag_x: np.ndarray, dtype: str = "bf16") ->
 
 
 # ---------------------------------------------------------------- AlltoAllQuantMatmul
+def matmul_reduce_scatter(x: np.ndarray, x2: np.ndarray, recv: Sequence[Optional[np.ndarray]], rank: int,
+                          dtype: str, x2_trans: bool = False) -> Dict[str, np.ndarray]:
+    """One rank's share of Y = ReduceScatter_m(x @ x2): "partial" = round(x @ x2) (m, n)
+    and "out" = round(sum over ranks j in order of block `rank` of rank j's partial),
+    (m / r, n); recv[j] is rank j's block for this rank (recv[rank] unused)."""
+    x = np.ascontiguousarray(x)
+    x2 = np.ascontiguousarray(x2)
+    r = len(recv)
+    m, k = x.shape
+    n = x2.shape[0] if x2_trans else x2.shape[1]
+    assert (x2.shape[1] if x2_trans else x2.shape[0]) == k and m % r == 0
+    rows = m // r
+    dummy = np.zeros((rows, n), dtype=_STORAGE[dtype])
+    blocks = [dummy if (j == rank or recv[j] is None) else np.ascontiguousarray(recv[j]) for j in range(r)]
+    for b in blocks:
+        assert b.shape == (rows, n)
+    partial = np.empty((m, n), dtype=_STORAGE[dtype])
+    out = np.empty((rows, n), dtype=_STORAGE[dtype])
+    _load().orc_matmul_reduce_scatter(_ptr(x), _ptr(x2), int(x2_trans), r, rank, m, k, n, _ptr_array(blocks),
+                                      DT[dtype], _ptr(partial), _ptr(out))
+    return {"partial": partial, "out": out}
+
+
 def permute(x1: np.ndarray, r: int) -> np.ndarray:
     x1 = np.ascontiguousarray(x1)
     bs, h = x1.shape

@@ -17,7 +17,8 @@
  *        permutedOut * x1Scale) -> int8 matmul -> x x1_scale x x2_scale -> + bias.
  *  [MC2] hyper_parallel tensor_parallel/mc2.py (coverage listing): module
  *        docstring and AllGatherMatmulFunction.backward -- dX = dY @ W
- *        (reduce-scattered across ranks), dW = dY^T @ AllGather(X).
+ *        (reduce-scattered across ranks), dW = dY^T @ AllGather(X);
+ *        MatmulReduceScatterFunction.forward -- Y = ReduceScatter_m(X @ W^T).
  *  [QAR] QuantAllReduce README (ops-transformer mc2/quant_all_reduce):
  *        "function" formula output = Reduce(AllGather(scales) * AllGather(x))
  *        with sum, parameter table (scale shapes (bs, H/128) fp32 or
@@ -199,6 +200,39 @@ void orc_allgather_matmul(const uint16_t* const* shards, int r, int64_t m_local,
   orc_matmul(g, 0, x2, x2_trans, r * m_local, n, k, dtype, out);
   if (gather_out) memcpy(gather_out, g, sizeof(uint16_t) * (size_t)(r * m_local * k));
   free(g);
+}
+
+/* ------------------------------------------------------------------------ */
+/* [MC2] MatmulReduceScatter, the share of one rank.                         */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * Y = ReduceScatter_m(x @ x2) as rank `rank` of r sees it (the row-parallel
+ * forward passes x2 = W^T; the backward dX = ReduceScatter_m(dY @ W)):
+ *   partial = round(x @ x2), (m, n): this rank's matmul output, in the
+ *             input dtype like any matmul output;
+ *   out     = round(P_0 + P_1 + ... + P_{r-1}), (m / r, n), where P_j is
+ *             block `rank` (rows [rank m/r, (rank+1) m/r)) of rank j's
+ *             partial: recv[j] for j != rank (what rank j sent) and this
+ *             rank's own partial for j == rank.  The sum runs in rank order
+ *             in fp64 and is rounded once to the dtype.
+ * recv[rank] is not read.  x2_trans: x2 stored (n, k) row-major.
+ */
+void orc_matmul_reduce_scatter(const uint16_t* x, const uint16_t* x2, int x2_trans, int r, int rank,
+                               int64_t m, int64_t k, int64_t n, const uint16_t* const* recv, int dtype,
+                               uint16_t* partial, uint16_t* out) {
+  orc_matmul(x, 0, x2, x2_trans, m, n, k, dtype, partial);
+  const int64_t rows = m / r;
+#pragma omp parallel for schedule(static)
+  for (int64_t t = 0; t < rows; t++)
+    for (int64_t c = 0; c < n; c++) {
+      double sum = 0.0;
+      for (int j = 0; j < r; j++) {
+        const uint16_t v = j == rank ? partial[(rank * rows + t) * n + c] : recv[j][t * n + c];
+        sum += dec16(dtype, v);
+      }
+      out[t * n + c] = enc16(dtype, sum);
+    }
 }
 
 /* ------------------------------------------------------------------------ */

@@ -127,6 +127,77 @@ def test_ag_against_float64_library_matmul():
         assert abs(int(bits(out)[i, j]) - int(want[i, j])) == 1 and near_tie(Fraction(ref[i, j]), "bf16", 1e-9)
 
 
+# ----------------------------------------------------------------- MatmulReduceScatter
+def _rs_system(xs, x2s, dtype, x2_trans=False):
+    """Every rank's share, each fed the blocks the other ranks' partials hold for it."""
+    r = len(xs)
+    rows = xs[0].shape[0] // r
+    shares = [oracle.matmul_reduce_scatter(xs[i], x2s[i], [None] * r, i, dtype, x2_trans) for i in range(r)]
+    outs = []
+    for i in range(r):
+        recv = [None if j == i else np.ascontiguousarray(shares[j]["partial"][i * rows:(i + 1) * rows])
+                for j in range(r)]
+        outs.append(oracle.matmul_reduce_scatter(xs[i], x2s[i], recv, i, dtype, x2_trans)["out"])
+    return [s_["partial"] for s_ in shares], outs
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("x2_trans", [False, True])
+def test_rs_exact_integer_system_is_the_unsharded_product(dtype, x2_trans):
+    """Row-parallel layer with small-integer operands: every partial and every sum is an
+    exact integer, so the ranks' outputs stacked in rank order are X @ W with X = [x_0 | ... |
+    x_{r-1}] (K split across the ranks) and W = [w_0; ...; w_{r-1}], here in int64."""
+    rng = np.random.default_rng(21)
+    r, m, k, n = 4, 12, 32, 5
+    xi = [rng.integers(-1, 2, (m, k)) for _ in range(r)]
+    wi = [rng.integers(-1, 2, (k, n)) for _ in range(r)]
+    xs = [enc(a, dtype) for a in xi]
+    x2s = [enc(w.T if x2_trans else w, dtype) for w in wi]
+    partials, outs = _rs_system(xs, x2s, dtype, x2_trans)
+    for a, w, p in zip(xi, wi, partials):
+        assert np.array_equal(bits(p), bits(enc(a @ w, dtype)))
+    full = np.hstack(xi).astype(np.int64) @ np.vstack(wi).astype(np.int64)
+    assert np.array_equal(bits(np.concatenate(outs)), bits(enc(full, dtype)))
+
+
+@pytest.mark.parametrize("r,rank,dtype,x2_trans", [(2, 1, "bf16", False), (4, 2, "bf16", True), (4, 0, "f16", False),
+                                                   (1, 0, "bf16", False)])
+def test_rs_matches_exact_rational_brute_force(r, rank, dtype, x2_trans):
+    """partial = RNE of the exact product; out = RNE of the exact sum of the decoded blocks."""
+    m, k, n = 2 * r, 6, 3
+    x = mc2_inputs.fill(40 + r, 0, "normal", 0.0, 1.0, dtype, (m, k))
+    x2 = mc2_inputs.fill(40 + r, 1, "normal", 0.0, 1.0, dtype, (n, k) if x2_trans else (k, n))
+    recv = [None if j == rank else mc2_inputs.fill(40 + r, 2 + j, "normal", 0.0, 4.0, dtype, (2, n))
+            for j in range(r)]
+    res = oracle.matmul_reduce_scatter(x, x2, recv, rank, dtype, x2_trans)
+    b = decode16(x2, dtype)
+    exact = exact_matmul(decode16(x, dtype), b.T if x2_trans else b)
+    for i in range(m):
+        for j in range(n):
+            if not near_tie(exact[i][j], dtype):
+                assert int(bits(res["partial"])[i, j]) == round_rne(exact[i][j], dtype), (i, j)
+    for t in range(2):
+        for c in range(n):
+            terms = [Fraction(float(decode16(res["partial"], dtype)[rank * 2 + t, c])) if j == rank else
+                     Fraction(float(decode16(recv[j], dtype)[t, c])) for j in range(r)]
+            assert int(bits(res["out"])[t, c]) == round_rne(sum(terms), dtype), (t, c)
+
+
+def test_rs_is_the_adjoint_of_allgather():
+    """The pages call the two operators duals: for exact data, sum_i <RS(P)_i, Z_i> equals
+    <P_0 + ... + P_{r-1}, AllGather(Z)>, with the gather taken from the AllGather oracle."""
+    rng = np.random.default_rng(22)
+    r, m, k, n = 4, 8, 16, 6
+    xs = [enc(rng.integers(-1, 2, (m, k)), "bf16") for _ in range(r)]
+    x2s = [enc(rng.integers(-1, 2, (k, n)), "bf16") for _ in range(r)]
+    partials, outs = _rs_system(xs, x2s, "bf16")
+    zs = [enc(rng.integers(-3, 4, (m // r, n)), "bf16") for _ in range(r)]
+    lhs = sum(float(np.sum(decode16(o, "bf16") * decode16(z, "bf16"))) for o, z in zip(outs, zs))
+    g = oracle.allgather(zs)
+    rhs = float(np.sum(sum(decode16(p, "bf16") for p in partials) * decode16(g, "bf16")))
+    assert lhs == rhs
+
+
 # ----------------------------------------------------------------- column-parallel backward
 def test_bwd_worked_example():
     g = gold("worked_examples.json")["column_parallel_backward"]
