@@ -8,6 +8,10 @@ this order (names as in the JSON "rows"):
                shards in gather_out chunk by chunk and the GEMM waits per chunk
   colpar_dx    column-parallel backward dX = dY (8192, 1792) @ W (1792, 4096)
   colpar_dw    column-parallel backward dW = dY^T (1792, 8192) @ AG(X) (8192, 4096)
+  rs_fwd       MatmulReduceScatter, rank 0 of 8: row-parallel forward partial x (4096, 1792) @
+               w^T (w (4096, 1792)), its own (512, 4096) block reduced with 7 received blocks
+  rs_dx        MatmulReduceScatter completing dX: dY (8192, 1792) @ W (1792, 4096), own
+               (1024, 4096) block reduced with 7 received blocks
   a16w8        AlltoAllQuantMatmul A16W8: permute+quant of bf16 (8192, 4096) on 8 ranks,
                then int8 (1024, 32768) @ (32768, 7168) with per-token x per-channel dequant + bias
   a8w8         AlltoAllQuantMatmul, full quantisation: int8 (8192, 4096) on 8 ranks with
@@ -42,7 +46,8 @@ PEAK_BF16 = 2500.0     # TFLOP/s, dense MFMA, MI355X
 PEAK_INT8 = 5000.0     # TOP/s, dense MFMA, MI355X
 PEAK_HBM = 8000.0      # GB/s, MI355X HBM3E
 
-ALL_ROWS = ["ag_bf16_tp", "ag_arrival", "colpar_dx", "colpar_dw", "a16w8", "a8w8", "qar_int8", "qar_mx"]
+ALL_ROWS = ["ag_bf16_tp", "ag_arrival", "colpar_dx", "colpar_dw", "rs_fwd", "rs_dx", "a16w8", "a8w8", "qar_int8",
+            "qar_mx"]
 EXTRA_ROWS = ["copy_calib"]
 COPY_CALIB_BYTES = 256 << 20
 
@@ -136,6 +141,23 @@ def setup_rows(names, mc2, torch):
             row.bytes = 2 * (m * nl + m * k + nl * k)
             row.check = lambda t=t, dw=dw: check_bwd(t, dw, "dw")
             rows[row.name] = row
+    for name in ("rs_fwd", "rs_dx"):
+        if name not in names:
+            continue
+        seed, d, specs = mc2_inputs.CONFIGS[name]
+        t = mc2_inputs.make(name)
+        r, rank, m, k, n, tr = d["r"], d["rank"], d["m"], d["k"], d["n"], d["x2_trans"]
+        x, x2 = T(t["x"], "bf16"), T(t["x2"], "bf16")
+        recv = [None if j == rank else T(t[f"recv{j}"], "bf16") for j in range(r)]
+        out = torch.empty((m // r, n), dtype=torch.bfloat16, device="cuda")
+        part = torch.empty((m, n), dtype=torch.bfloat16, device="cuda")
+        row = Row(name, "TFLOP/s", "mfma", PEAK_BF16, 2.0 * m * k * n,
+                  [("gemm_bf16_rs", lambda x=x, x2=x2, recv=recv, rank=rank, tr=tr, out=out, part=part:
+                    mc2.mc2_matmul_reduce_scatter(x, x2, recv, rank, x2_trans=tr, out=out, partial_out=part))])
+        rows_ = m // r
+        row.bytes = 2 * (m * k + k * n + (m - rows_) * n + (r - 1) * rows_ * n + rows_ * n)
+        row.check = lambda t=t, d=d, out=out, part=part: check_rs(t, d, out, part)
+        rows[row.name] = row
     if "a16w8" in names:
         seed, d, specs = mc2_inputs.CONFIGS["a16w8"]
         t = mc2_inputs.make("a16w8")
@@ -231,6 +253,25 @@ def check_bwd(t, res, which):
         rows = np.sort(rng.choice(t["dy"].shape[1], 24, replace=False))
         want = oracle.matmul(np.ascontiguousarray(t["dy"][:, rows]), t["ag_x"], "bf16", a_trans=True)
     return _tol16(got[rows], want, "bf16")
+
+
+def check_rs(t, d, out, part):
+    import numpy as np
+
+    import mc2_inputs
+    import oracle
+    r, rank, m, k, tr = d["r"], d["rank"], d["m"], d["k"], d["x2_trans"]
+    rows = m // r
+    rng = np.random.default_rng(6)
+    others = np.sort(rng.choice(np.arange(rows * (rank + 1), m), 6, replace=False))
+    want = oracle.matmul(np.ascontiguousarray(t["x"][others]), t["x2"], "bf16", b_trans=tr)
+    ok = _tol16(mc2_inputs.from_torch(part)[others], want, "bf16")
+    ts = np.sort(rng.choice(rows, 4, replace=False))
+    xsub = np.zeros((r * 4, k), dtype=t["x"].dtype)
+    xsub[rank * 4:(rank + 1) * 4] = t["x"][rank * rows + ts]
+    rsub = [None if j == rank else np.ascontiguousarray(t[f"recv{j}"][ts]) for j in range(r)]
+    ref = oracle.matmul_reduce_scatter(xsub, t["x2"], rsub, rank, "bf16", tr)
+    return bool(ok and _tol16(mc2_inputs.from_torch(out)[ts], ref["out"], "bf16"))
 
 
 def check_a16w8(t, d, out, mc2, torch):
@@ -482,7 +523,7 @@ def main():
         "vs_baseline": None, "dtype": "int8" if head in ("a16w8", "a8w8") else "bf16", "data": "synthetic",
         "config": {"workload": {"ag_bf16_tp": "AllGatherMatmul bf16 TP layer: 8 x (512, 4096) shards @ (4096, 1792)",
                                 }.get(head, head),
-                   "rows_in_step": [r.name for r in rows], "seeds": "workload number (1..6)"},
+                   "rows_in_step": [r.name for r in rows], "seeds": "workload number (1..8)"},
         "roofline": {"bound": h["bound"], "achieved": h["achieved"], "peak": h["peak"],
                      "unit": "TFLOP/s" if h["unit"] == "TFLOP/s" else h["unit"], "frac": h["frac"],
                      "traffic": stored_traffic() if head == "ag_bf16_tp" else None,

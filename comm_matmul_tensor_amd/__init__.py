@@ -8,6 +8,7 @@ raises.
 
 Functions carry the C names:
   mc2_allgather_matmul, mc2_allgather_arrival_fallbacks, mc2_matmul_grad_input, mc2_matmul_grad_weight,
+  mc2_matmul_reduce_scatter,
   mc2_alltoall_quant_matmul_workspace_size, mc2_alltoall_quant_matmul, mc2_alltoall_quant_matmul_static,
   mc2_quant_all_reduce, mc2_status_string, mc2_last_error.
 """
@@ -56,6 +57,7 @@ _SIGS = {
                                   _P, ctypes.c_size_t, _P],
     "mc2_quant_all_reduce": [_P, _P, _INT, _I64, _I64, _INT, _INT, _P, _INT, _P],
     "mc2_allgather_arrival_fallbacks": [_INT, ctypes.POINTER(ctypes.c_uint)],
+    "mc2_matmul_reduce_scatter": [_P, _P, _INT, _INT, _I64, _I64, _I64, _INT, _INT, _P, _P, _P, _P],
     "mc2_alltoall_quant_matmul_static": [_P, _INT, _I64, _I64, _P, _P, _I64, _P, _P, _P, _INT, _P, _P, _P],
 }
 for _name, _args in _SIGS.items():
@@ -164,6 +166,34 @@ def mc2_matmul_grad_input(dy: torch.Tensor, w: torch.Tensor, *, out: Optional[to
     return out
 
 
+def mc2_matmul_reduce_scatter(x: torch.Tensor, x2: torch.Tensor, recv: Sequence[Optional[torch.Tensor]],
+                              rank_id: int, *, x2_trans: bool = False, out: Optional[torch.Tensor] = None,
+                              partial_out: Optional[torch.Tensor] = None,
+                              stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Rank rank_id's share of ReduceScatter_m(x @ x2): returns (out, partial_out).
+    recv[j] (j != rank_id) is the (m / len(recv), n) block rank j sends; x2 is (k, n), or
+    (n, k) with x2_trans (the row-parallel forward passes the nn.Linear weight that way)."""
+    ws = len(recv)
+    m, k = x.shape
+    n = x2.shape[0] if x2_trans else x2.shape[1]
+    if (x2.shape[1] if x2_trans else x2.shape[0]) != k:
+        raise ValueError("x2 does not match x's contraction size")
+    if ws < 1 or m % ws != 0:
+        raise ValueError("m must be divisible by the number of ranks")
+    for j, b in enumerate(recv):
+        if j != rank_id and (b is None or tuple(b.shape) != (m // ws, n) or b.dtype != x.dtype):
+            raise ValueError(f"recv[{j}] must be a ({m // ws}, {n}) tensor of x's dtype")
+    if out is None:
+        out = torch.empty((m // ws, n), dtype=x.dtype, device=x.device)
+    if partial_out is None:
+        partial_out = torch.empty((m, n), dtype=x.dtype, device=x.device)
+    ptrs = (ctypes.c_void_p * ws)(*[None if j == rank_id else _dev(b, f"recv[{j}]") for j, b in enumerate(recv)])
+    _check(_lib.mc2_matmul_reduce_scatter(_dev(x, "x"), _dev(x2, "x2"), ws, rank_id, m, k, n, int(bool(x2_trans)),
+                                          _dt(x), ptrs, _dev(out, "out"), _dev(partial_out, "partial_out"),
+                                          _stream(stream)))
+    return out, partial_out
+
+
 def mc2_matmul_grad_weight(dy: torch.Tensor, ag_x: torch.Tensor, *, out: Optional[torch.Tensor] = None,
                            stream=None) -> torch.Tensor:
     """dW = dY^T @ AllGather_m(X)."""
@@ -257,6 +287,7 @@ def mc2_quant_all_reduce(x: Sequence[torch.Tensor], scales: Sequence[torch.Tenso
 
 __all__ = [
     "mc2_allgather_matmul", "mc2_allgather_arrival_fallbacks", "mc2_matmul_grad_input", "mc2_matmul_grad_weight",
+    "mc2_matmul_reduce_scatter",
     "mc2_alltoall_quant_matmul_workspace_size", "mc2_alltoall_quant_matmul", "mc2_alltoall_quant_matmul_static",
     "mc2_quant_all_reduce",
     "mc2_status_string", "mc2_last_error", "Mc2Error", "LIB_PATH",

@@ -164,6 +164,37 @@ mc2_status mc2_matmul_grad_input(const void* dy, const void* w, int64_t m, int64
   return MC2_OK;
 }
 
+mc2_status mc2_matmul_reduce_scatter(const void* x, const void* x2, int world_size, int rank_id, int64_t m,
+                                     int64_t k, int64_t n, int x2_trans, mc2_dtype dtype, const void* const* recv,
+                                     void* out, void* partial_out, void* stream) {
+  clear_error();
+  mc2_status s = check_matmul_reduce_scatter(x, x2, world_size, rank_id, m, k, n, dtype, recv, out, partial_out);
+  if (s != MC2_OK) return s;
+  int dev;
+  if ((s = current_device(&dev)) != MC2_OK) return s;
+  GemmArgs a{};
+  a.a_parts[0] = x;  // A = x (m, k), K-contiguous
+  a.num_parts = 1;
+  a.rows_per_part = m;
+  a.a_kmajor = 1;
+  a.b = x2;          // (k, n) row-major, or (n, k) row-major with x2_trans
+  a.b_kmajor = x2_trans ? 1 : 0;
+  a.c = partial_out;
+  a.m = m;
+  a.n = n;
+  a.k = k;
+  a.dtype = dt(dtype);
+  a.rs_out = out;
+  for (int j = 0; j < world_size; j++) a.rs_recv[j] = j == rank_id ? nullptr : recv[j];
+  a.rs_ranks = world_size;
+  a.rs_rank = rank_id;
+  a.rs_rows = m / world_size;
+  a.rs_row0 = (int64_t)rank_id * a.rs_rows;
+  hipError_t e = launch_gemm16(a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "matmul_reduce_scatter launch");
+  return MC2_OK;
+}
+
 mc2_status mc2_matmul_grad_weight(const void* dy, const void* ag_x, int64_t m, int64_t n_local,
                                   int64_t k, mc2_dtype dtype, void* dw, void* stream) {
   clear_error();

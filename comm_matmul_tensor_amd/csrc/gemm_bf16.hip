@@ -14,6 +14,17 @@
 //    work spreads evenly): one write per element and no extra global read.
 //  - Epilogue: fp32 -> bf16 / fp16 with round-to-nearest-even, staged through
 //    LDS and stored as 16-byte row chunks.
+//  - MatmulReduceScatter (hyper_parallel mc2.py, module docstring and
+//    MatmulReduceScatterFunction.forward, Y = ReduceScatter_m(X @ W^T)): C is
+//    this rank's partial.  The tiles of its own row block are handed out
+//    last and store their rounded rows into the block output; the other rows
+//    of C are the blocks it sends.  A streaming pass then sums the block
+//    output with the blocks the other ranks sent, in rank order in fp32, and
+//    rounds once.  Reducing inside the GEMM epilogue instead made every own
+//    tile read seven scattered 256-byte row pieces per row at the same time,
+//    well below streaming bandwidth; the separate pass reads whole rows.
+#include <algorithm>
+
 #include "gemm_mfma.hpp"
 
 namespace mc2 {
@@ -33,7 +44,98 @@ struct Ops16 {
   static __device__ __forceinline__ uint16_t cvt(float f) {
     return DT == DT_BF16 ? f32_to_bf16_bits(f) : f32_to_f16_bits(f);
   }
+  static __device__ __forceinline__ float dec(uint32_t bits) {
+    return DT == DT_BF16 ? bf16_bits_to_f32(bits & 0xFFFFu) : f16_bits_to_f32(bits & 0xFFFFu);
+  }
 };
+
+// Reduce-scatter store of a staged tile (Problem::rs_out): the rows of the
+// own block go to rs_out (row t of the block to rs_out row t), the others
+// to C.  The rank-ordered sum with the received blocks follows in
+// rs_reduce_kernel.
+template <int BM, int BN, bool VEC>
+__device__ __forceinline__ void store_rs_tile(const uint16_t* h0, const uint16_t* h1, uint16_t* C, const Problem& p,
+                                              int64_t m0, int64_t n0) {
+  constexpr int kRowChunks = BN / 8;
+  const int64_t n = p.n;
+  for (int c = threadIdx.x; c < BM * kRowChunks; c += kThreads) {
+    const int row = c / kRowChunks, col = (c % kRowChunks) * 8;
+    const int64_t grow = m0 + row, gcol = n0 + col;
+    if (grow >= p.m) continue;
+    const uint16_t* src = staged_chunk<BM, BN>(h0, h1, row, col);
+    const int64_t t = grow - p.rs_row0;
+    uint16_t* dst = (t >= 0 && t < p.rs_rows) ? static_cast<uint16_t*>(p.rs_out) + t * n : C + grow * n;
+    if (VEC && gcol + 8 <= n) {
+      *reinterpret_cast<u32x4*>(dst + gcol) = *reinterpret_cast<const u32x4*>(src);
+    } else {
+      for (int e = 0; e < 8; e++)
+        if (gcol + e < n) dst[gcol + e] = src[e];
+    }
+  }
+}
+
+// The reduction of the own block, in place in rs_out: element e becomes
+// round(B_0 + B_1 + ... + B_{ranks-1}) summed in fp32 in rank order, B_j =
+// rs_recv[j][e] and B_rank = the rounded partial the GEMM left in rs_out.
+// A streaming pass over whole rows (HBM-bound): 8 elements per thread and
+// step, every block's load issued before the sum.
+struct RsReduceArgs {
+  uint16_t* out;
+  const uint16_t* recv[kMaxRanks];  // own and unused slots: out
+  int ranks;
+  int64_t elems;
+};
+
+template <int DT, bool VEC>
+__global__ __launch_bounds__(256) void rs_reduce_kernel(RsReduceArgs a) {
+  using O = Ops16<DT>;
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  if constexpr (VEC) {
+    const int64_t chunks = a.elems / 8;
+    for (int64_t c = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; c < chunks; c += stride) {
+      u32x4 v[kMaxRanks];
+#pragma unroll
+      for (int j = 0; j < kMaxRanks; j++) v[j] = reinterpret_cast<const u32x4*>(a.recv[j])[c];
+      float sum[8];
+#pragma unroll
+      for (int j = 0; j < kMaxRanks; j++) {
+        const bool used = j < a.ranks;
+#pragma unroll
+        for (int e = 0; e < 8; e++) {
+          const float f = O::dec(v[j][e / 2] >> (16 * (e & 1)));
+          sum[e] = j == 0 ? f : (used ? sum[e] + f : sum[e]);
+        }
+      }
+      u32x4 o;
+#pragma unroll
+      for (int w = 0; w < 4; w++) o[w] = (uint32_t)O::cvt(sum[2 * w]) | ((uint32_t)O::cvt(sum[2 * w + 1]) << 16);
+      reinterpret_cast<u32x4*>(a.out)[c] = o;
+    }
+  } else {
+    for (int64_t e = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; e < a.elems; e += stride) {
+      float sum = 0.0f;
+      for (int j = 0; j < a.ranks; j++) sum = j == 0 ? O::dec(a.recv[j][e]) : sum + O::dec(a.recv[j][e]);
+      a.out[e] = O::cvt(sum);
+    }
+  }
+}
+
+template <int DT>
+hipError_t launch_rs_reduce(const GemmArgs& g, hipStream_t s) {
+  RsReduceArgs a{};
+  a.out = static_cast<uint16_t*>(g.rs_out);
+  for (int j = 0; j < kMaxRanks; j++)
+    a.recv[j] = (j < g.rs_ranks && j != g.rs_rank) ? static_cast<const uint16_t*>(g.rs_recv[j]) : a.out;
+  a.ranks = g.rs_ranks;
+  a.elems = g.rs_rows * g.n;
+  // 16-byte chunks when every row of every block starts 16-byte aligned
+  const bool vec = g.n % 8 == 0;
+  const int64_t work = vec ? a.elems / 8 : a.elems;
+  const int64_t blocks = std::min<int64_t>((work + 255) / 256, 256 * 16);
+  if (vec) rs_reduce_kernel<DT, true><<<(unsigned)blocks, 256, 0, s>>>(a);
+  else rs_reduce_kernel<DT, false><<<(unsigned)blocks, 256, 0, s>>>(a);
+  return hipGetLastError();
+}
 
 // ARR: arrival emulation (A arrives in p.arrived piece by piece; gemm_mfma.hpp).
 template <int BM, int BN, bool AK, bool BKM, bool VEC, int DT, bool ARR>
@@ -43,7 +145,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm16_kernel(Problem p, void* c)
   __shared__ __attribute__((aligned(1024))) uint8_t s1[lds_stage_array_bytes<BM, BN>()];
   __shared__ __attribute__((aligned(1024))) uint8_t s2[lds_stage_array_bytes<BM, BN>()];
   int tm, tn;
-  tile_of_block(p.m, p.n, BM, BN, p.tile_order_cols, p.tile_group, tm, tn, ARR ? p.first_row_tile : 0);
+  tile_of_block(p.m, p.n, BM, BN, p.tile_order_cols, p.tile_group, tm, tn, p.first_row_tile);
   const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
   const int tiles_n = (int)((p.n + BN - 1) / BN);
 
@@ -55,8 +157,11 @@ __global__ __launch_bounds__(kThreads, 1) void gemm16_kernel(Problem p, void* c)
 
   run_mainloop<2, BM, BN, AK, BKM, VEC, ARR, Ops16<DT>>(p, m0, n0, tn, tiles_n, s0, s1, s2, acc);
 
-  store_c16<BM, BN, VEC>(reinterpret_cast<uint16_t*>(s0), reinterpret_cast<uint16_t*>(s1), static_cast<uint16_t*>(c),
-                         p.m, p.n, m0, n0, [&](int i, int j, int r, int, int) { return Ops16<DT>::cvt(acc[i][j][r]); });
+  uint16_t* h0 = reinterpret_cast<uint16_t*>(s0);
+  uint16_t* h1 = reinterpret_cast<uint16_t*>(s1);
+  stage_c16<BM, BN>(h0, h1, [&](int i, int j, int r, int, int) { return Ops16<DT>::cvt(acc[i][j][r]); });
+  if (p.rs_out) store_rs_tile<BM, BN, VEC>(h0, h1, static_cast<uint16_t*>(c), p, m0, n0);
+  else store_c16_tile<BM, BN, VEC>(h0, h1, static_cast<uint16_t*>(c), p.m, p.n, m0, n0);
 }
 
 template <int BM, int BN, bool AK, bool BKM, int DT>
@@ -72,6 +177,10 @@ hipError_t launch_cfg(Problem p, void* c, hipStream_t s) {
                    dma_buffers_ok(p.rows_per_part * p.k * 2, 0, parts, p.rows_per_part);
   p.tile_order_cols = prefer_column_order(p.m, p.n, p.k, 2) ? 1 : 0;
   p.tile_group = choose_tile_group(p.m, p.n, BM, BN, p.tile_order_cols);
+  if (p.rs_out) {  // own block last: start at the tile row after it
+    const int64_t tiles_m = (p.m + BM - 1) / BM;
+    p.first_row_tile = (int)(((p.rs_row0 + p.rs_rows) / BM) % tiles_m);
+  }
   if constexpr (AK) {
     if (p.ready) {
       if (vec) gemm16_kernel<BM, BN, AK, BKM, true, DT, true><<<(unsigned)tiles, kThreads, 0, s>>>(p, c);
@@ -109,6 +218,11 @@ hipError_t launch_dt(const GemmArgs& g, hipStream_t s) {
   p.kseg = g.k;
   p.kseg_stride = 0;
   p.a_part_bytes = g.rows_per_part * g.k * 2;
+  if (g.rs_out) {
+    p.rs_out = g.rs_out;
+    p.rs_row0 = g.rs_row0;
+    p.rs_rows = g.rs_rows;
+  }
   if (g.ready_flags) {  // arrival emulation: A arrives in gather_out, which the kernel only reads
     p.ready = g.ready_flags;
     p.ready_value = g.ready_value;
@@ -141,9 +255,17 @@ hipError_t launch_gemm16(const GemmArgs& g, hipStream_t s) {
         g.first_row_tile < 0 || (int64_t)g.first_row_tile * bm >= g.m)
       return hipErrorInvalidValue;
   }
-  if (g.dtype == DT_BF16) return launch_dt<DT_BF16>(g, s);
-  if (g.dtype == DT_F16) return launch_dt<DT_F16>(g, s);
-  return hipErrorInvalidValue;
+  if (g.rs_out) {
+    if (g.ready_flags || g.gather_out || g.rs_ranks < 1 || g.rs_ranks > kMaxRanks || g.rs_rank < 0 ||
+        g.rs_rank >= g.rs_ranks || g.rs_row0 < 0 || g.rs_rows < 1 || g.rs_row0 + g.rs_rows > g.m)
+      return hipErrorInvalidValue;
+    for (int j = 0; j < g.rs_ranks; j++)
+      if (j != g.rs_rank && !g.rs_recv[j]) return hipErrorInvalidValue;
+  }
+  if (g.dtype != DT_BF16 && g.dtype != DT_F16) return hipErrorInvalidValue;
+  hipError_t e = g.dtype == DT_BF16 ? launch_dt<DT_BF16>(g, s) : launch_dt<DT_F16>(g, s);
+  if (e != hipSuccess || !g.rs_out) return e;
+  return g.dtype == DT_BF16 ? launch_rs_reduce<DT_BF16>(g, s) : launch_rs_reduce<DT_F16>(g, s);
 }
 
 }  // namespace mc2

@@ -81,6 +81,11 @@ struct Problem {
   int64_t a_ld, kseg, kseg_stride, a_part_bytes;
   int tile_order_cols;
   int tile_group;         // tile rows (columns with tile_order_cols) per group of the tile order
+  // Reduce-scatter routing (rs_out == NULL: off): rows [rs_row0, rs_row0 +
+  // rs_rows) of C, this rank's block, are stored to rs_out (row t of the
+  // block to row t) instead of C.
+  void* rs_out;
+  int64_t rs_row0, rs_rows;
   // Arrival emulation (ready == NULL: off).  A arrives in `arrived` (the
   // gathered matrix) in pieces: rows [g rows_chunk, (g+1) rows_chunk) x
   // columns [s slab_cols, (s+1) slab_cols) may be read once
@@ -95,7 +100,7 @@ struct Problem {
   int64_t rows_chunk;
   int64_t slab_cols;
   int slabs;
-  int first_row_tile;     // tile row of the local block's first rows: handed out first
+  int first_row_tile;     // tile row handed out first (also without arrival; 0 by default)
 };
 
 // Longest wait for one row block, in ticks of the 100 MHz real-time counter.
@@ -832,13 +837,11 @@ __device__ __forceinline__ void tile_of_block(int64_t m, int64_t n, int bm, int 
 }
 
 // Writes a wavefront's rounded 16-bit C fragments to an LDS copy of the C tile
-// (rows [0, BM/2) in h0, rows [BM/2, BM) in h1), then the whole workgroup
-// stores the tile with 16-byte row-contiguous stores.  cvt(i, j, r, row, col)
-// returns the 16-bit output of element r of fragment (i, j) at tile
-// coordinates (row, col).
-template <int BM, int BN, bool VEC, typename Cvt>
-__device__ __forceinline__ void store_c16(uint16_t* h0, uint16_t* h1, uint16_t* C, int64_t m, int64_t n, int64_t m0,
-                                          int64_t n0, Cvt cvt) {
+// (rows [0, BM/2) in h0, rows [BM/2, BM) in h1) and waits for the whole
+// workgroup.  cvt(i, j, r, row, col) returns the 16-bit output of element r
+// of fragment (i, j) at tile coordinates (row, col).
+template <int BM, int BN, typename Cvt>
+__device__ __forceinline__ void stage_c16(uint16_t* h0, uint16_t* h1, Cvt cvt) {
   constexpr int WM = BM / 2, WN = BN / 2;
   constexpr int FM = WM / 16, FN = WN / 16;
   constexpr int kPitch = BN + 8;
@@ -857,12 +860,25 @@ __device__ __forceinline__ void store_c16(uint16_t* h0, uint16_t* h1, uint16_t* 
       }
     }
   __syncthreads();
+}
+
+// Row chunk c of the staged tile: 8 elements of tile row `row` from column `col`.
+template <int BM, int BN>
+__device__ __forceinline__ const uint16_t* staged_chunk(const uint16_t* h0, const uint16_t* h1, int row, int col) {
+  constexpr int WM = BM / 2, kPitch = BN + 8;
+  return (row < WM ? h0 + row * kPitch : h1 + (row - WM) * kPitch) + col;
+}
+
+// Stores the staged tile with 16-byte row-contiguous stores.
+template <int BM, int BN, bool VEC>
+__device__ __forceinline__ void store_c16_tile(const uint16_t* h0, const uint16_t* h1, uint16_t* C, int64_t m,
+                                               int64_t n, int64_t m0, int64_t n0) {
   constexpr int kRowChunks = BN / 8;
   for (int c = threadIdx.x; c < BM * kRowChunks; c += kThreads) {
     const int row = c / kRowChunks, col = (c % kRowChunks) * 8;
     const int64_t grow = m0 + row, gcol = n0 + col;
     if (grow >= m) continue;
-    const uint16_t* src = (row < WM ? h0 + row * kPitch : h1 + (row - WM) * kPitch) + col;
+    const uint16_t* src = staged_chunk<BM, BN>(h0, h1, row, col);
     if (VEC && gcol + 8 <= n) {
       *reinterpret_cast<u32x4*>(C + grow * n + gcol) = *reinterpret_cast<const u32x4*>(src);
     } else {
@@ -870,6 +886,13 @@ __device__ __forceinline__ void store_c16(uint16_t* h0, uint16_t* h1, uint16_t* 
         if (gcol + j < n) C[grow * n + gcol + j] = src[j];
     }
   }
+}
+
+template <int BM, int BN, bool VEC, typename Cvt>
+__device__ __forceinline__ void store_c16(uint16_t* h0, uint16_t* h1, uint16_t* C, int64_t m, int64_t n, int64_t m0,
+                                          int64_t n0, Cvt cvt) {
+  stage_c16<BM, BN>(h0, h1, cvt);
+  store_c16_tile<BM, BN, VEC>(h0, h1, C, m, n, m0, n0);
 }
 
 // LDS bytes of one stage array: an operand stage, or half of the 16-bit C tile.

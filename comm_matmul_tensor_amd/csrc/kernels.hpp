@@ -51,6 +51,14 @@ struct GemmArgs {
   int slabs;
   int first_row_tile;
   unsigned* status_flag;
+  // reduce-scatter epilogue (rs_out NULL when unused): rows [rs_row0,
+  // rs_row0 + rs_rows) of C are not stored; rs_out row t = round(sum over
+  // ranks j < rs_ranks in order of (j == rs_rank ? C row rs_row0 + t :
+  // rs_recv[j] row t)), the sum in fp32.  rs_recv[j] and rs_out have n columns.
+  void* rs_out;
+  const void* rs_recv[kMaxRanks];
+  int rs_ranks, rs_rank;
+  int64_t rs_row0, rs_rows;
 };
 hipError_t launch_gemm16(const GemmArgs& a, hipStream_t s);
 // Tile height (rows of C per workgroup) launch_gemm16 uses for an (m, n) C.

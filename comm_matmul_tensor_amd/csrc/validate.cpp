@@ -72,6 +72,33 @@ mc2_status check_grad_input(const void* dy, const void* w, int64_t m, int64_t n_
   return MC2_OK;
 }
 
+mc2_status check_matmul_reduce_scatter(const void* x, const void* x2, int world_size, int rank_id, int64_t m,
+                                       int64_t k, int64_t n, mc2_dtype dtype, const void* const* recv,
+                                       const void* out, const void* partial_out) {
+  if (!x || !x2 || !recv || !out || !partial_out)
+    return fail(MC2_ERR_NULL, "matmul_reduce_scatter: x, x2, recv, out and partial_out are required");
+  if (!valid_world(world_size))
+    return fail(MC2_ERR_SHAPE, "matmul_reduce_scatter: world_size must be 2, 4 or 8, got " + str(world_size));
+  if (rank_id < 0 || rank_id >= world_size)
+    return fail(MC2_ERR_SHAPE, "matmul_reduce_scatter: rank_id out of range");
+  for (int j = 0; j < world_size; j++)
+    if (j != rank_id && !recv[j]) return fail(MC2_ERR_NULL, "matmul_reduce_scatter: recv " + str(j) + " is NULL");
+  // the fused kernel's contraction dimension lies in [256, 65535) (hyper_parallel
+  // mc2.py module docstring); the output rows are scattered over the ranks
+  if (k < 256 || k >= 65535)
+    return fail(MC2_ERR_SHAPE, "matmul_reduce_scatter: k must lie in [256, 65535), got " + str(k));
+  if (m < 1 || n < 1) return fail(MC2_ERR_SHAPE, "matmul_reduce_scatter: empty m or n");
+  if (m % world_size != 0) return fail(MC2_ERR_SHAPE, "matmul_reduce_scatter: m must be divisible by world_size");
+  if (m > INT32_MAX || n > INT32_MAX) return fail(MC2_ERR_SHAPE, "matmul_reduce_scatter: m or n above INT32_MAX");
+  if (!is_half(dtype)) return fail(MC2_ERR_DTYPE, "matmul_reduce_scatter: dtype must be F16 or BF16");
+  if (!aligned16(x) || !aligned16(x2) || !aligned16(out) || !aligned16(partial_out))
+    return fail(MC2_ERR_ALIGN, "matmul_reduce_scatter: tensor not 16-byte aligned");
+  for (int j = 0; j < world_size; j++)
+    if (j != rank_id && !aligned16(recv[j]))
+      return fail(MC2_ERR_ALIGN, "matmul_reduce_scatter: recv block not 16-byte aligned");
+  return MC2_OK;
+}
+
 mc2_status check_grad_weight(const void* dy, const void* ag_x, int64_t m, int64_t n_local,
                              int64_t k, mc2_dtype dtype, const void* dw) {
   if (!dy || !ag_x || !dw) return fail(MC2_ERR_NULL, "matmul_grad_weight: dy, ag_x and dw are required");

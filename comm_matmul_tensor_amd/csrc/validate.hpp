@@ -20,6 +20,9 @@ mc2_status check_allgather_matmul(const void* const* shards, int world_size, int
                                   const void* out, const void* gather_out, int mode, int rank_id);
 mc2_status check_grad_input(const void* dy, const void* w, int64_t m, int64_t n_local, int64_t k,
                             mc2_dtype dtype, const void* dx);
+mc2_status check_matmul_reduce_scatter(const void* x, const void* x2, int world_size, int rank_id, int64_t m,
+                                       int64_t k, int64_t n, mc2_dtype dtype, const void* const* recv,
+                                       const void* out, const void* partial_out);
 mc2_status check_grad_weight(const void* dy, const void* ag_x, int64_t m, int64_t n_local,
                              int64_t k, mc2_dtype dtype, const void* dw);
 mc2_status check_alltoall_sizes(int rank_size, int64_t bs, int64_t h, int64_t n);

@@ -139,6 +139,39 @@ mc2_status mc2_matmul_grad_input(const void* dy, const void* w, int64_t m, int64
                                  int64_t k, mc2_dtype dtype, void* dx_partial, void* stream);
 
 /*
+ * MatmulReduceScatter, the share of rank rank_id of world_size --
+ * hyper_parallel mc2.py, module docstring and MatmulReduceScatterFunction:
+ * the row-parallel forward Y = ReduceScatter_m(X @ W^T) (x2 = W^T, pass W
+ * with x2_trans = 1), and AllGatherMatmulFunction.backward's
+ * dX = ReduceScatter_m(dY @ W) (x2 = W, x2_trans = 0).  This rank computes
+ * its partial x @ x2 and reduces its own row block with the blocks the other
+ * ranks send it:
+ *   partial_out (m, n) = round(x (m, k) @ x2), fp32 accumulation; the rows
+ *       of other ranks' blocks are written (they are what this rank sends),
+ *       the rows [rank_id m/ws, (rank_id+1) m/ws) of its own block are not;
+ *   out (m / ws, n) = round(B_0 + B_1 + ... + B_{ws-1}), summed in fp32 in
+ *       rank order, B_j = recv[j] for j != rank_id and the rounded own-block
+ *       rows of x @ x2 for j == rank_id.
+ * Reading of the pages: each rank's partial is a matmul output, so it is
+ * rounded to `dtype` before the reduction; the pages fix no order or
+ * precision for the sum, so it runs in fp32 in rank order and is rounded
+ * once.  The tiles of the own block run last, so on several GPUs the
+ * received blocks have the whole GEMM to arrive; the sum is a second pass
+ * on `stream` after the GEMM, in place in `out`.
+ *
+ * x         (m, k) row-major; k is the contraction size of the fused kernel,
+ *           in [256, 65535); m divisible by world_size
+ * x2        (k, n) row-major, or with x2_trans (n, k) row-major
+ * recv      world_size pointers: recv[j], j != rank_id, is a (m / ws, n)
+ *           row-major block of `dtype`; recv[rank_id] is not read (may be NULL)
+ * out, partial_out  as above, of `dtype` (F16 or BF16)
+ * All pointers are caller-owned device memory, 16-byte aligned.
+ */
+mc2_status mc2_matmul_reduce_scatter(const void* x, const void* x2, int world_size, int rank_id, int64_t m,
+                                     int64_t k, int64_t n, int x2_trans, mc2_dtype dtype, const void* const* recv,
+                                     void* out, void* partial_out, void* stream);
+
+/*
  * Column-parallel backward, weight gradient -- hyper_parallel mc2.py,
  * AllGatherMatmulFunction.backward: dW = dY^T @ AllGather_m(X), where
  * AllGather_m(X) is the gather_out saved by the forward.

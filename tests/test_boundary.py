@@ -31,7 +31,7 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     names = _declared()
-    assert len(names) == 10, names
+    assert len(names) == 11, names
     for n in names:
         assert hasattr(lib, n), n
 
@@ -141,6 +141,34 @@ def test_alltoall_static_validation(lib):
     assert f(*bad) == 3                                    # fp32 out
     bad = list(args); bad[11] = ctypes.c_void_p(0x10008)
     assert f(*bad) == 8                                    # permuted_out misaligned
+
+
+def test_matmul_reduce_scatter_validation(lib):
+    f = lib.mc2_matmul_reduce_scatter
+    f.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int64, ctypes.c_int64,
+                  ctypes.c_int64, ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                  ctypes.c_void_p]
+    recv = _ptrs(A, None, B, C)                            # rank 1's own slot NULL
+    args = [A, B, 4, 1, 64, 256, 32, 0, 2, recv, C, A, None]
+    for i in (0, 1, 9, 10, 11):                            # x, x2, recv, out, partial_out
+        bad = list(args); bad[i] = None
+        assert f(*bad) == 1
+    bad = list(args); bad[9] = _ptrs(A, B, None, C)
+    assert f(*bad) == 1                                    # a peer's block NULL
+    bad = list(args); bad[2] = 3
+    assert f(*bad) == 2                                    # world size 3
+    bad = list(args); bad[3] = 4
+    assert f(*bad) == 2                                    # rank out of range
+    bad = list(args); bad[4] = 62
+    assert f(*bad) == 2                                    # m not divisible by world size
+    bad = list(args); bad[5] = 255
+    assert f(*bad) == 2                                    # contraction below 256
+    bad = list(args); bad[5] = 65535
+    assert f(*bad) == 2
+    bad = list(args); bad[8] = 0
+    assert f(*bad) == 3                                    # fp32
+    bad = list(args); bad[10] = ctypes.c_void_p(0x30002)
+    assert f(*bad) == 8                                    # out misaligned
 
 
 def test_quant_all_reduce_validation(lib):
