@@ -18,6 +18,7 @@ this order (names as in the JSON "rows"):
                per-token scales, the permute folded into the int8 GEMM's loads, same GEMM
   qar_int8     QuantAllReduce, 8 ranks x int8 (4, 2048, 7168) + fp32 group-128 scales -> fp32
   qar_mx       QuantAllReduce, 8 ranks x E4M3FN (4, 2048, 7168) + E8M0 mx scales -> bf16
+  qrs_int8     QuantReduceScatter, rank 3's share of the qar_int8 workload: 1024 of 8192 rows -> fp32
 
 Inputs are generated on the host, copied to HBM before timing, and stay
 resident.  --copy-calib adds a plain 256 MiB device copy to every step (the
@@ -47,7 +48,7 @@ PEAK_INT8 = 5000.0     # TOP/s, dense MFMA, MI355X
 PEAK_HBM = 8000.0      # GB/s, MI355X HBM3E
 
 ALL_ROWS = ["ag_bf16_tp", "ag_arrival", "colpar_dx", "colpar_dw", "rs_fwd", "rs_dx", "a16w8", "a8w8", "qar_int8",
-            "qar_mx"]
+            "qar_mx", "qrs_int8"]
 EXTRA_ROWS = ["copy_calib"]
 COPY_CALIB_BYTES = 256 << 20
 
@@ -204,6 +205,23 @@ def setup_rows(names, mc2, torch):
         row.bytes = nbytes
         row.check = (lambda t=t, d=d, out=out, xdt=xdt, sdt=sdt: check_qar(t, d, out, xdt, sdt))
         rows[name] = row
+    if "qrs_int8" in names:
+        seed, d, specs = mc2_inputs.CONFIGS["qar_int8"]
+        t = mc2_inputs.make("qar_int8")
+        r, rank = d["r"], 3
+        xs = [T(t[f"x{i}"], "i8") for i in range(r)]
+        sc = [T(t[f"scale{i}"], "f32") for i in range(r)]
+        h = d["shape"][-1]
+        nrows = int(np.prod(d["shape"][:-1]))
+        out = torch.empty((nrows // r, h), dtype=torch.float32, device="cuda")
+        elems = nrows // r * h
+        nbytes = r * (elems + 4 * elems // 128) + 4 * elems
+        row = Row("qrs_int8", "GB/s", "hbm", PEAK_HBM, float(nbytes),
+                  [("dequant_sum", lambda xs=xs, sc=sc, out=out, rank=rank:
+                    mc2.mc2_quant_reduce_scatter(xs, sc, rank, out_dtype=torch.float32, out=out))])
+        row.bytes = nbytes
+        row.check = lambda t=t, d=d, out=out, rank=rank: check_qrs(t, d, out, rank)
+        rows[row.name] = row
     if "copy_calib" in names:
         src = torch.empty(COPY_CALIB_BYTES, dtype=torch.uint8, device="cuda").fill_(1)
         dst = torch.empty_like(src)
@@ -319,6 +337,24 @@ def check_qar(t, d, out, xdt, sdt):
     got = mc2_inputs.from_torch(out).reshape(rows, h)[sel]
     view = np.uint32 if want.dtype == np.float32 else np.uint16
     return bool(np.array_equal(got.view(view), want.view(view)))
+
+
+def check_qrs(t, d, out, rank):
+    import numpy as np
+
+    import mc2_inputs
+    import oracle
+    r = d["r"]
+    h = d["shape"][-1]
+    rows = int(np.prod(d["shape"][:-1]))
+    blk = rows // r
+    rng = np.random.default_rng(7)
+    sel = np.sort(rng.choice(blk, 16, replace=False))
+    xs = [np.ascontiguousarray(t[f"x{i}"].reshape(rows, h)[rank * blk + sel]) for i in range(r)]
+    sc = [np.ascontiguousarray(t[f"scale{i}"].reshape(rows, h // 128)[rank * blk + sel]) for i in range(r)]
+    want = oracle.quant_all_reduce(xs, sc, "i8", "f32", "f32")
+    got = mc2_inputs.from_torch(out)[sel]
+    return bool(np.array_equal(got.view(np.uint32), want.view(np.uint32)))
 
 
 # ---------------------------------------------------------------- CPU baseline (the oracle)

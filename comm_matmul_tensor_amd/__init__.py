@@ -10,7 +10,7 @@ Functions carry the C names:
   mc2_allgather_matmul, mc2_allgather_arrival_fallbacks, mc2_matmul_grad_input, mc2_matmul_grad_weight,
   mc2_matmul_reduce_scatter,
   mc2_alltoall_quant_matmul_workspace_size, mc2_alltoall_quant_matmul, mc2_alltoall_quant_matmul_static,
-  mc2_quant_all_reduce, mc2_status_string, mc2_last_error.
+  mc2_quant_all_reduce, mc2_quant_reduce_scatter, mc2_status_string, mc2_last_error.
 """
 from __future__ import annotations
 
@@ -56,6 +56,7 @@ _SIGS = {
     "mc2_alltoall_quant_matmul": [_P, _INT, _I64, _I64, _INT, _P, _I64, _P, _P, _P, _P, _P, _P, _P, _P,
                                   _P, ctypes.c_size_t, _P],
     "mc2_quant_all_reduce": [_P, _P, _INT, _I64, _I64, _INT, _INT, _P, _INT, _P],
+    "mc2_quant_reduce_scatter": [_P, _P, _INT, _INT, _I64, _I64, _INT, _INT, _P, _INT, _P],
     "mc2_allgather_arrival_fallbacks": [_INT, ctypes.POINTER(ctypes.c_uint)],
     "mc2_matmul_reduce_scatter": [_P, _P, _INT, _INT, _I64, _I64, _I64, _INT, _INT, _P, _P, _P, _P],
     "mc2_alltoall_quant_matmul_static": [_P, _INT, _I64, _I64, _P, _P, _I64, _P, _P, _P, _INT, _P, _P, _P],
@@ -285,10 +286,38 @@ def mc2_quant_all_reduce(x: Sequence[torch.Tensor], scales: Sequence[torch.Tenso
     return out
 
 
+def mc2_quant_reduce_scatter(x: Sequence[torch.Tensor], scales: Sequence[torch.Tensor], rank_id: int, *,
+                             out_dtype: torch.dtype = torch.float32, out: Optional[torch.Tensor] = None,
+                             stream=None) -> torch.Tensor:
+    """Rows [rank_id rows / r, (rank_id + 1) rows / r) of mc2_quant_all_reduce's sum, as a
+    (rows / r, h) tensor (rows = the product of x's leading dimensions)."""
+    r = len(x)
+    shape = tuple(x[0].shape)
+    h = shape[-1]
+    rows = 1
+    for s in shape[:-1]:
+        rows *= s
+    if rows % r != 0:
+        raise ValueError("rows must be divisible by the number of ranks")
+    if out is None:
+        out = torch.empty((rows // r, h), dtype=out_dtype, device=x[0].device)
+    if out.numel() != rows // r * h:
+        raise ValueError(f"out holds {out.numel()} elements, expected {rows // r * h}")
+    per_scale = 128 if _dt(scales[0]) == MC2_F32 else 32
+    for i in range(r):
+        if tuple(x[i].shape) != shape or x[i].dtype != x[0].dtype or scales[i].dtype != scales[0].dtype:
+            raise ValueError(f"rank {i} tensors differ from rank 0")
+        if scales[i].numel() * per_scale != rows * h:
+            raise ValueError(f"scales[{i}] holds {scales[i].numel()} scales, expected {rows * h // per_scale}")
+    _check(_lib.mc2_quant_reduce_scatter(_ptrs(x, "x"), _ptrs(scales, "scales"), r, rank_id, rows, h, _dt(x[0]),
+                                         _dt(scales[0]), _dev(out, "out"), _dt(out), _stream(stream)))
+    return out
+
+
 __all__ = [
     "mc2_allgather_matmul", "mc2_allgather_arrival_fallbacks", "mc2_matmul_grad_input", "mc2_matmul_grad_weight",
     "mc2_matmul_reduce_scatter",
     "mc2_alltoall_quant_matmul_workspace_size", "mc2_alltoall_quant_matmul", "mc2_alltoall_quant_matmul_static",
-    "mc2_quant_all_reduce",
+    "mc2_quant_all_reduce", "mc2_quant_reduce_scatter",
     "mc2_status_string", "mc2_last_error", "Mc2Error", "LIB_PATH",
 ]

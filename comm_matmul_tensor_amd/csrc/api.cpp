@@ -140,6 +140,35 @@ mc2_status mc2_quant_all_reduce(const void* const* x, const void* const* scales,
   return MC2_OK;
 }
 
+mc2_status mc2_quant_reduce_scatter(const void* const* x, const void* const* scales, int world_size, int rank_id,
+                                    int64_t rows, int64_t h, mc2_dtype x_dtype, mc2_dtype scale_dtype, void* out,
+                                    mc2_dtype out_dtype, void* stream) {
+  clear_error();
+  mc2_status s = check_quant_reduce_scatter(x, scales, world_size, rank_id, rows, h, x_dtype, scale_dtype, out,
+                                            out_dtype);
+  if (s != MC2_OK) return s;
+  int dev;
+  if ((s = current_device(&dev)) != MC2_OK) return s;
+  // this rank's rows of the sum: the same pass over its row block of every input
+  const int64_t block = rows / world_size, row0 = (int64_t)rank_id * block;
+  const int64_t scale_row_bytes = scale_dtype == MC2_F32 ? (h / 128) * 4 : h / 32;
+  QarArgs a{};
+  for (int i = 0; i < world_size; i++) {
+    a.x[i] = static_cast<const uint8_t*>(x[i]) + row0 * h;
+    a.scales[i] = static_cast<const uint8_t*>(scales[i]) + row0 * scale_row_bytes;
+  }
+  a.out = out;
+  a.total = block * h;
+  a.h = h;
+  a.r = world_size;
+  a.x_dtype = dt(x_dtype);
+  a.scale_dtype = dt(scale_dtype);
+  a.out_dtype = dt(out_dtype);
+  hipError_t e = launch_dequant_sum(a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "quant_reduce_scatter launch");
+  return MC2_OK;
+}
+
 mc2_status mc2_matmul_grad_input(const void* dy, const void* w, int64_t m, int64_t n_local,
                                  int64_t k, mc2_dtype dtype, void* dx_partial, void* stream) {
   clear_error();

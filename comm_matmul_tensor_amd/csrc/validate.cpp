@@ -169,37 +169,56 @@ mc2_status check_alltoall_quant_matmul_static(const void* x1, int rank_size, int
   return MC2_OK;
 }
 
-mc2_status check_quant_all_reduce(const void* const* x, const void* const* scales, int world_size,
-                                  int64_t rows, int64_t h, mc2_dtype x_dtype,
-                                  mc2_dtype scale_dtype, const void* out, mc2_dtype out_dtype) {
-  if (!x || !scales || !out) return fail(MC2_ERR_NULL, "quant_all_reduce: x, scales and out are required");
+static mc2_status check_quant_reduce(const char* op, const void* const* x, const void* const* scales, int world_size,
+                                     int64_t rows, int64_t h, mc2_dtype x_dtype, mc2_dtype scale_dtype,
+                                     const void* out, mc2_dtype out_dtype) {
+  const std::string o = std::string(op) + ": ";
+  if (!x || !scales || !out) return fail(MC2_ERR_NULL, o + "x, scales and out are required");
   if (!valid_world(world_size))
-    return fail(MC2_ERR_SHAPE, "quant_all_reduce: world_size must be 2, 4 or 8, got " + str(world_size));
+    return fail(MC2_ERR_SHAPE, o + "world_size must be 2, 4 or 8, got " + str(world_size));
   for (int i = 0; i < world_size; i++)
-    if (!x[i] || !scales[i]) return fail(MC2_ERR_NULL, "quant_all_reduce: x or scales of rank " + str(i) + " is NULL");
+    if (!x[i] || !scales[i]) return fail(MC2_ERR_NULL, o + "x or scales of rank " + str(i) + " is NULL");
   // no empty tensors; H in [1024, 8192] and 128-aligned ("constraints")
-  if (rows < 1) return fail(MC2_ERR_SHAPE, "quant_all_reduce: empty tensor");
+  if (rows < 1) return fail(MC2_ERR_SHAPE, o + "empty tensor");
   if (h < 1024 || h > 8192 || h % 128 != 0)
-    return fail(MC2_ERR_SHAPE, "quant_all_reduce: h must be a multiple of 128 in [1024, 8192], got " + str(h));
+    return fail(MC2_ERR_SHAPE, o + "h must be a multiple of 128 in [1024, 8192], got " + str(h));
   // E8M0 scales go with E4M3FN / E5M2 x (mx); FLOAT scales with INT8,
   // E4M3FN or E5M2 x (pertoken-pergroup, group 128).  HIFLOAT8 is not
   // supported: the pages name it but never define it.
   if (scale_dtype == MC2_E8M0) {
     if (x_dtype != MC2_F8E4M3FN && x_dtype != MC2_F8E5M2)
-      return fail(MC2_ERR_DTYPE, "quant_all_reduce: E8M0 scales need E4M3FN or E5M2 x");
+      return fail(MC2_ERR_DTYPE, o + "E8M0 scales need E4M3FN or E5M2 x");
   } else if (scale_dtype == MC2_F32) {
     if (x_dtype != MC2_I8 && x_dtype != MC2_F8E4M3FN && x_dtype != MC2_F8E5M2)
-      return fail(MC2_ERR_DTYPE, "quant_all_reduce: FLOAT scales need INT8, E4M3FN or E5M2 x");
+      return fail(MC2_ERR_DTYPE, o + "FLOAT scales need INT8, E4M3FN or E5M2 x");
   } else {
-    return fail(MC2_ERR_DTYPE, "quant_all_reduce: scales must be F32 or E8M0");
+    return fail(MC2_ERR_DTYPE, o + "scales must be F32 or E8M0");
   }
   // output FLOAT, FLOAT16 or BFLOAT16 (parameter table)
   if (out_dtype != MC2_F32 && out_dtype != MC2_F16 && out_dtype != MC2_BF16)
-    return fail(MC2_ERR_DTYPE, "quant_all_reduce: out must be F32, F16 or BF16");
+    return fail(MC2_ERR_DTYPE, o + "out must be F32, F16 or BF16");
   for (int i = 0; i < world_size; i++)
     if (!aligned16(x[i]) || !aligned16(scales[i]))
-      return fail(MC2_ERR_ALIGN, "quant_all_reduce: tensor not 16-byte aligned");
-  if (!aligned16(out)) return fail(MC2_ERR_ALIGN, "quant_all_reduce: out not 16-byte aligned");
+      return fail(MC2_ERR_ALIGN, o + "tensor not 16-byte aligned");
+  if (!aligned16(out)) return fail(MC2_ERR_ALIGN, o + "out not 16-byte aligned");
+  return MC2_OK;
+}
+
+mc2_status check_quant_all_reduce(const void* const* x, const void* const* scales, int world_size,
+                                  int64_t rows, int64_t h, mc2_dtype x_dtype,
+                                  mc2_dtype scale_dtype, const void* out, mc2_dtype out_dtype) {
+  return check_quant_reduce("quant_all_reduce", x, scales, world_size, rows, h, x_dtype, scale_dtype, out, out_dtype);
+}
+
+mc2_status check_quant_reduce_scatter(const void* const* x, const void* const* scales, int world_size, int rank_id,
+                                      int64_t rows, int64_t h, mc2_dtype x_dtype, mc2_dtype scale_dtype,
+                                      const void* out, mc2_dtype out_dtype) {
+  mc2_status s = check_quant_reduce("quant_reduce_scatter", x, scales, world_size, rows, h, x_dtype, scale_dtype,
+                                    out, out_dtype);
+  if (s != MC2_OK) return s;
+  if (rank_id < 0 || rank_id >= world_size) return fail(MC2_ERR_SHAPE, "quant_reduce_scatter: rank_id out of range");
+  if (rows % world_size != 0)
+    return fail(MC2_ERR_SHAPE, "quant_reduce_scatter: rows must be divisible by world_size");
   return MC2_OK;
 }
 

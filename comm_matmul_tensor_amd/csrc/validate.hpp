@@ -38,6 +38,9 @@ mc2_status check_alltoall_quant_matmul_static(const void* x1, int rank_size, int
                                               const void* x2_scale, const void* bias, const void* out,
                                               mc2_dtype out_dtype, const void* permuted_out,
                                               const void* acc_out);
+mc2_status check_quant_reduce_scatter(const void* const* x, const void* const* scales, int world_size, int rank_id,
+                                      int64_t rows, int64_t h, mc2_dtype x_dtype, mc2_dtype scale_dtype,
+                                      const void* out, mc2_dtype out_dtype);
 mc2_status check_quant_all_reduce(const void* const* x, const void* const* scales, int world_size,
                                   int64_t rows, int64_t h, mc2_dtype x_dtype,
                                   mc2_dtype scale_dtype, const void* out, mc2_dtype out_dtype);

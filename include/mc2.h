@@ -269,6 +269,20 @@ mc2_status mc2_quant_all_reduce(const void* const* x, const void* const* scales,
                                 mc2_dtype scale_dtype, void* out, mc2_dtype out_dtype,
                                 void* stream);
 
+/*
+ * QuantReduceScatter, the share of rank rank_id -- named beside
+ * QuantAllReduce in the QuantAllReduce README's constraints (the two may run
+ * back to back in one communication domain); read as the reduce-scatter
+ * form of the same formula: this rank keeps rows [rank_id rows/ws,
+ * (rank_id+1) rows/ws) of output = Reduce(AllGather(scales) *
+ * AllGather(x)), summed over ranks in order exactly as mc2_quant_all_reduce.
+ * Arguments as for mc2_quant_all_reduce; rows must be divisible by
+ * world_size and out is (rows / world_size, h) of out_dtype.
+ */
+mc2_status mc2_quant_reduce_scatter(const void* const* x, const void* const* scales, int world_size, int rank_id,
+                                    int64_t rows, int64_t h, mc2_dtype x_dtype, mc2_dtype scale_dtype, void* out,
+                                    mc2_dtype out_dtype, void* stream);
+
 /* Static text for a status code. */
 const char* mc2_status_string(mc2_status s);
 

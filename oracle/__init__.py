@@ -62,6 +62,7 @@ def _load():
             "orc_permute_i8": (None, [P, INT, I64, I64, P]),
             "orc_alltoall_quant_matmul_static": (I64, [P, INT, I64, I64, P, P, I64, P, P, INT, P, P, P]),
             "orc_quant_all_reduce": (INT, [P, P, INT, I64, I64, INT, INT, P, INT]),
+            "orc_quant_reduce_scatter": (INT, [P, P, INT, INT, I64, I64, INT, INT, P, INT]),
             "orc_decode_array": (INT, [INT, I64, P, P]),
             "orc_encode_array": (INT, [INT, I64, P, P]),
             "orc_num_threads": (INT, []),
@@ -292,4 +293,20 @@ def quant_all_reduce(xs: Sequence[np.ndarray], scales: Sequence[np.ndarray], x_d
                                       DT[x_dtype], DT[scale_dtype], _ptr(out), DT[out_dtype])
     if rc != 0:
         raise ValueError("unsupported dtype combination")
+    return out
+
+
+def quant_reduce_scatter(xs: Sequence[np.ndarray], scales: Sequence[np.ndarray], rank: int, x_dtype: str,
+                         scale_dtype: str, out_dtype: str) -> np.ndarray:
+    """Rows [rank rows / r, (rank + 1) rows / r) of the QuantAllReduce sum, as (rows / r, h)."""
+    xs = [np.ascontiguousarray(x) for x in xs]
+    scales = [np.ascontiguousarray(s) for s in scales]
+    shape = xs[0].shape
+    h = shape[-1]
+    rows = int(np.prod(shape[:-1]))
+    out = np.empty((rows // len(xs), h), dtype=_STORAGE[out_dtype])
+    rc = _load().orc_quant_reduce_scatter(_ptr_array(xs), _ptr_array(scales), len(xs), rank, rows, h,
+                                          DT[x_dtype], DT[scale_dtype], _ptr(out), DT[out_dtype])
+    if rc != 0:
+        raise ValueError("unsupported dtype combination or rows not divisible by the ranks")
     return out

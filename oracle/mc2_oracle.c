@@ -437,6 +437,26 @@ int orc_quant_all_reduce(const void* const* x, const void* const* scales, int r,
   return 0;
 }
 
+/*
+ * QuantReduceScatter, the share of rank `rank` of r (named beside
+ * QuantAllReduce in its README's constraints; read as the reduce-scatter
+ * form): rows [rank rows/r, (rank+1) rows/r) of the QuantAllReduce output,
+ * with the same per-element sum.  out is (rows / r, h).
+ */
+int orc_quant_reduce_scatter(const void* const* x, const void* const* scales, int r, int rank, int64_t rows,
+                             int64_t h, int x_dtype, int scale_dtype, void* out, int out_dtype) {
+  const int64_t block = rows / r, row0 = (int64_t)rank * block;
+  const int64_t scale_row_bytes = scale_dtype == O_F32 ? (h / 128) * 4 : h / 32;
+  const void* xb[8];
+  const void* sb[8];
+  if (r < 1 || r > 8 || rows % r != 0) return -1;
+  for (int i = 0; i < r; i++) {
+    xb[i] = (const uint8_t*)x[i] + row0 * h;
+    sb[i] = (const uint8_t*)scales[i] + row0 * scale_row_bytes;
+  }
+  return orc_quant_all_reduce(xb, sb, r, block, h, x_dtype, scale_dtype, out, out_dtype);
+}
+
 /* ------------------------------------------------------------------------ */
 /* Array forms of the format routines (for the format tests).               */
 /* ------------------------------------------------------------------------ */

@@ -31,7 +31,7 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     names = _declared()
-    assert len(names) == 11, names
+    assert len(names) == 12, names
     for n in names:
         assert hasattr(lib, n), n
 
@@ -185,6 +185,20 @@ def test_quant_all_reduce_validation(lib):
     assert f(xs, ss, 2, 8, 1024, E4M3, I32, C, F32, None) == 3    # bad scale dtype
     assert f(xs, ss, 2, 8, 1024, E5M2, E8M0, C, I32, None) == 3   # bad out dtype
     assert f(xs, _ptrs(B, None), 2, 8, 1024, I8, F32, C, F32, None) == 1
+
+
+def test_quant_reduce_scatter_validation(lib):
+    f = lib.mc2_quant_reduce_scatter
+    f.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int64, ctypes.c_int64,
+                  ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p]
+    xs, ss = _ptrs(A, A), _ptrs(B, B)
+    I8, F32, BF16 = 3, 0, 2
+    assert f(xs, ss, 2, 2, 8, 1024, I8, F32, C, F32, None) == 2     # rank out of range
+    assert f(xs, ss, 2, 0, 7, 1024, I8, F32, C, F32, None) == 2     # rows not divisible by world size
+    assert f(xs, ss, 2, 0, 8, 1000, I8, F32, C, F32, None) == 2     # h not 128-aligned
+    assert f(xs, ss, 2, -1, 8, 1024, I8, F32, C, BF16, None) == 2
+    assert f(xs, _ptrs(B, None), 2, 0, 8, 1024, I8, F32, C, F32, None) == 1
+    assert f(xs, ss, 2, 0, 8, 1024, I8, 7, C, F32, None) == 3       # E8M0 scales with int8 x
 
 
 @pytest.mark.skipif(__import__("torch").cuda.is_available(), reason="checks the no-device path")

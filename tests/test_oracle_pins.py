@@ -439,6 +439,32 @@ def test_qar_unit_scales_integer_sum(r):
     assert np.array_equal(out, enc(np.sum(xi, axis=0).astype(np.float64), "bf16"))
 
 
+@pytest.mark.parametrize("r", [2, 4, 8])
+def test_qrs_blocks_against_library_sum(r):
+    """QuantReduceScatter: rank k's output is rows [k rows/r, (k+1) rows/r) of the rank sum.
+    Scales are powers of two that differ per row and group, so every product and the fp64
+    sum are exact and a wrong row block or scale offset changes the result."""
+    rng = np.random.default_rng(60 + r)
+    rows, h = 2 * r, 1024
+    xs = [rng.integers(-127, 128, (rows, h)).astype(np.int8) for _ in range(r)]
+    sc = [np.ldexp(1.0, rng.integers(-12, -2, (rows, h // 128))).astype(np.float32) for _ in range(r)]
+    full = sum(x.astype(np.float64) * np.repeat(s_.astype(np.float64), 128, axis=1) for x, s_ in zip(xs, sc))
+    for k in range(r):
+        out = oracle.quant_reduce_scatter(xs, sc, k, "i8", "f32", "f32")
+        assert np.array_equal(out, full[2 * k:2 * k + 2].astype(np.float32))
+    # mx: E4M3FN codes of small integers, E8M0 exponents per row and 32-element block
+    vals = np.arange(-8, 9)
+    codes = {v: int(np.where(oracle.decode("e4m3fn", np.arange(256, dtype=np.uint8)) == v)[0][0]) for v in vals}
+    xi = [rng.integers(-8, 9, (rows, h)) for _ in range(r)]
+    xc = [np.vectorize(codes.get)(x).astype(np.uint8) for x in xi]
+    ex = [rng.integers(120, 128, (rows, h // 64, 2)).astype(np.uint8) for _ in range(r)]
+    full = sum(x.astype(np.float64) * np.repeat(np.ldexp(1.0, e.reshape(rows, h // 32).astype(int) - 127), 32, axis=1)
+               for x, e in zip(xi, ex))
+    for k in range(r):
+        out = oracle.quant_reduce_scatter(xc, ex, k, "e4m3fn", "e8m0", "f32")
+        assert np.array_equal(out, full[2 * k:2 * k + 2].astype(np.float32))
+
+
 def test_qar_group_mapping_against_library_repeat():
     """Scales that differ per group reveal the element -> scale mapping."""
     rng = np.random.default_rng(10)
