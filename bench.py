@@ -439,15 +439,18 @@ def summarize(d, write_traffic):
         vals = [v for k in copy_names for v in counters[k].get(c, []) if v * 1024 > COPY_CALIB_BYTES / 2]
         if vals:
             scale[c] = COPY_CALIB_BYTES / (1024.0 * sum(vals) / len(vals))
+    mfma_names = ("MfmaUtil", "SQ_INSTS_VALU_MFMA_MOPS_BF16", "SQ_INSTS_VALU_MFMA_MOPS_I8")
     if counters:
-        names = sorted({c for k in counters for c in counters[k]})
+        names = sorted({c for k in counters for c in counters[k] if c not in mfma_names})
         lines.append("Counters, average per dispatch (FETCH_SIZE / WRITE_SIZE in KiB as read, and in MB after "
                      "scaling by the 256 MiB copy):\n")
         lines.append("| kernel | dispatches | " + " | ".join(names) + " | fetch MB (scaled) | write MB (scaled) |")
         lines.append("|---|---|" + "---|" * len(names) + "---|---|")
         for k, cs in sorted(counters.items()):
+            if not any(c in cs for c in names):
+                continue
             avg = {c: sum(v) / len(v) for c, v in cs.items()}
-            n = max(len(v) for v in cs.values())
+            n = max(len(v) for c, v in cs.items() if c in names)
             fm = avg.get("FETCH_SIZE", 0) * 1024 * scale.get("FETCH_SIZE", 1.0) / 1e6
             wm = avg.get("WRITE_SIZE", 0) * 1024 * scale.get("WRITE_SIZE", 1.0) / 1e6
             lines.append(f"| {k} | {n} | " + " | ".join(f"{avg.get(c, 0):.0f}" for c in names) +
@@ -455,6 +458,20 @@ def summarize(d, write_traffic):
         lines.append("")
         lines.append("Copy-kernel scale factors (known bytes / counted bytes): " +
                      ", ".join(f"{c} {v:.4f}" for c, v in scale.items()) + "\n")
+    mf = {k: cs for k, cs in counters.items() if "MfmaUtil" in cs}
+    if mf:
+        lines.append("MFMA counters, average per dispatch (MfmaUtil: MFMA-busy cycles over the dispatch's active "
+                     "cycles x SIMDs, in %; MFMA ops: the MOPS counters x 512):\n")
+        lines.append("| kernel | dispatches | MfmaUtil % | bf16 MFMA GFLOP | int8 MFMA GOP |")
+        lines.append("|---|---|---|---|---|")
+        for k, cs in sorted(mf.items()):
+            avg = {c: sum(v) / len(v) for c, v in cs.items()}
+            if avg.get("MfmaUtil", 0) < 0.05:
+                continue
+            lines.append(f"| {k} | {len(cs['MfmaUtil'])} | {avg['MfmaUtil']:.1f} | "
+                         f"{avg.get('SQ_INSTS_VALU_MFMA_MOPS_BF16', 0) * 512 / 1e9:.2f} | "
+                         f"{avg.get('SQ_INSTS_VALU_MFMA_MOPS_I8', 0) * 512 / 1e9:.2f} |")
+        lines.append("")
     print("\n".join(lines))
     if write_traffic:
         ag = [k for k in counters if k.startswith("gemm16_kernel<128, 224, true, false, true, 2, false>")]
