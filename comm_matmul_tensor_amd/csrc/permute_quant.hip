@@ -72,7 +72,7 @@ __device__ __forceinline__ int quant1(float y, float s) {
 // half-integer and the unit is recomputed with the IEEE division (see the
 // bound above).
 template <int DT, int U>
-__global__ __launch_bounds__(kVecThreads) void permute_quant_vec(QuantArgs a) {
+__global__ __launch_bounds__(kVecThreads, 2) void permute_quant_vec(QuantArgs a) {
   __shared__ float red[kVecThreads / 64];
   const int64_t t = blockIdx.x;
   const int64_t T = a.bs / a.r;
@@ -92,6 +92,17 @@ __global__ __launch_bounds__(kVecThreads) void permute_quant_vec(QuantArgs a) {
       const u32x4* src = reinterpret_cast<const u32x4*>(x1 + ((int64_t)j * T + t) * a.h + c);
       raw[v][0] = src[0];
       raw[v][1] = src[1];
+    }
+  }
+  if (a.permuted) {  // optional copy of P, straight from the registers (they die here)
+#pragma unroll
+    for (int v = 0; v < U; v++) {
+      const int u = threadIdx.x + v * kVecThreads;
+      if (u < units) {
+        u32x4* dst = reinterpret_cast<u32x4*>(static_cast<uint16_t*>(a.permuted) + t * cols + (int64_t)u * 16);
+        dst[0] = raw[v][0];
+        dst[1] = raw[v][1];
+      }
     }
   }
   float y[U][16];
@@ -158,11 +169,6 @@ __global__ __launch_bounds__(kVecThreads) void permute_quant_vec(QuantArgs a) {
                   __builtin_amdgcn_perm(mb[4 * w + 1], mb[4 * w], 0x0c0c0400u);
       }
       *reinterpret_cast<u32x4*>(a.q + t * cols + e) = qv;
-      if (a.permuted) {  // optional copy of P, straight from the registers
-        u32x4* dst = reinterpret_cast<u32x4*>(static_cast<uint16_t*>(a.permuted) + t * cols + e);
-        dst[0] = raw[v][0];
-        dst[1] = raw[v][1];
-      }
     }
   }
 }
