@@ -96,6 +96,18 @@ def test_a16w8_zero_rows_and_ties(mc2):
     assert_close16(mc2_inputs.from_torch(out), ref["out"], "bf16", "out")
 
 
+@pytest.mark.parametrize("h", [4374, 4368])
+def test_a16w8_largest_rank_h(mc2, h):
+    """r*H at the top of the allowed range: 34992 (H not a multiple of 16, element path)
+    and 34944 (vector path with three 16-element units per thread)."""
+    print(f"a16w8 r=8 h={h}", flush=True)
+    got, ref = _run(mc2, 8, 16, h, 48, seed=h)
+    assert_bits_equal(got["q"], ref["q"], "q")
+    assert_bits_equal(got["s1"], ref["s1"], "x1_scale")
+    assert_bits_equal(got["acc"], ref["acc"], "acc")
+    assert_close16(got["out"], ref["out"], "bf16", "out")
+
+
 def test_a16w8_full_config(mc2):
     """bf16 (8192, 4096) on 8 ranks -> (1024, 32768) @ int8 (32768, 7168): every permuted
     value, code and scale; accumulators and outputs on sampled tokens."""

@@ -95,6 +95,17 @@ def test_a8w8_extreme_codes(mc2):
     assert_close16(mc2_inputs.from_torch(out), ref["out"], "bf16", "out", REL, RMS_REL)
 
 
+@pytest.mark.parametrize("h", [4368, 4352])
+def test_a8w8_largest_rank_h(mc2, h):
+    """r*H near the top of the allowed range: segments of 4368 bytes (not whole 128-byte
+    steps: checked loader) and of 4352 = 34 * 128 (direct-to-LDS path)."""
+    print(f"a8w8 r=8 h={h}", flush=True)
+    got, ref = _run(mc2, 8, 64, h, 96, seed=h)
+    assert_bits_equal(got["permuted"], ref["permuted"], "permuted")
+    assert_bits_equal(got["acc"], ref["acc"], "acc")
+    assert_close16(got["out"], ref["out"], "bf16", "out", REL, RMS_REL)
+
+
 def test_a8w8_full_config(mc2):
     """int8 (8192, 4096) on 8 ranks -> (1024, 32768) @ int8 (32768, 7168): every permuted
     byte; accumulators and outputs on sampled tokens; two runs bit-identical."""

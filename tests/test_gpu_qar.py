@@ -114,7 +114,7 @@ def _run_rs(mc2, specs, seed, x_dtype, s_dtype, out_dtype, r, rank):
 
 
 @pytest.mark.parametrize("r,shape,rank", [(2, (2, 1024), 1), (4, (4, 3, 1152), 2), (8, (2, 8, 8192), 7),
-                                          (8, (16, 2048), 0)])
+                                          (8, (16, 2048), 0), (8, (8, 1024), 6)])
 @pytest.mark.parametrize("out_dtype", ["f32", "bf16"])
 def test_qrs_int8_pergroup(mc2, r, shape, rank, out_dtype):
     print(f"qrs int8 r={r} shape={shape} rank={rank} out={out_dtype}", flush=True)

@@ -119,6 +119,17 @@ def test_rs_exact_integer_system(mc2, dtype, x2_trans):
     assert_bits_equal(got, want, "stacked outputs vs unsharded product")
 
 
+def test_rs_largest_contraction(mc2):
+    """k = 65534, the largest contraction the fused kernel accepts."""
+    r, m, k, n, rank = 2, 32, 65534, 24, 1
+    xs, x2s = _system(r, m, k, n, False, "bf16", seed=91)
+    recv = _recv_for(rank, xs, x2s, "bf16", False)
+    ref = oracle.matmul_reduce_scatter(xs[rank], x2s[rank], recv, rank, "bf16", False)
+    out, part = _gpu(mc2, xs[rank], x2s[rank], recv, rank, False, "bf16")
+    _check_partial(part, ref["partial"], rank, r, "bf16")
+    assert_close16(out, ref["out"], "bf16", "out")
+
+
 def test_rs_repeated_calls_and_ranks(mc2):
     """Same operands, every rank id in turn, twice: each call writes only its own block."""
     r, m, k, n = 4, 512, 256, 128
