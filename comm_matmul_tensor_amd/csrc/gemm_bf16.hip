@@ -193,13 +193,15 @@ hipError_t launch_cfg(Problem p, void* c, hipStream_t s) {
   return hipGetLastError();
 }
 
-const TileChoice kTiles16[] = {{128, 224}, {224, 128}, {128, 128}};
+const TileChoice kTiles16[] = {{128, 224}, {224, 128}, {128, 256}, {128, 128}};
+constexpr int kNumTiles16 = sizeof(kTiles16) / sizeof(kTiles16[0]);
 
 template <bool AK, bool BKM, int DT>
 hipError_t launch_layout(const Problem& p, void* c, hipStream_t s) {
-  switch (pick_tile(p.m, p.n, kTiles16, 3)) {
+  switch (pick_tile(p.m, p.n, kTiles16, kNumTiles16)) {
     case 0: return launch_cfg<128, 224, AK, BKM, DT>(p, c, s);
     case 1: return launch_cfg<224, 128, AK, BKM, DT>(p, c, s);
+    case 2: return launch_cfg<128, 256, AK, BKM, DT>(p, c, s);
     default: return launch_cfg<128, 128, AK, BKM, DT>(p, c, s);
   }
 }
@@ -242,7 +244,7 @@ hipError_t launch_dt(const GemmArgs& g, hipStream_t s) {
 
 }  // namespace
 
-int gemm16_tile_rows(int64_t m, int64_t n) { return kTiles16[pick_tile(m, n, kTiles16, 3)].bm; }
+int gemm16_tile_rows(int64_t m, int64_t n) { return kTiles16[pick_tile(m, n, kTiles16, kNumTiles16)].bm; }
 
 hipError_t launch_gemm16(const GemmArgs& g, hipStream_t s) {
   if (g.m < 1 || g.n < 1 || g.k < 1 || g.num_parts < 1 || g.num_parts > kMaxRanks) return hipErrorInvalidValue;

@@ -372,7 +372,11 @@ __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(
 // conflicts.
 template <int E, int R>
 __device__ __forceinline__ int mn_swz(int k) {
-  static_assert((E == 2 || E == 1) && (R == 224 || R == 128), "no swizzle for this tile");
+  static_assert((E == 2 && (R == 224 || R == 128 || R == 256)) || (E == 1 && (R == 224 || R == 128)),
+                "no swizzle for this tile");
+  // 128 or 256 16-bit columns: a k row is one or two full bank rows, so the
+  // bank of a chunk depends only on its position mod 16 and the same XOR
+  // spreads the 8 k rows x 2 chunks of a half-wavefront transpose read
   if constexpr (E == 2 && R == 224) return 2 * ((k >> 3) & 1);
   else if constexpr (E == 2) return 2 * ((k & 3) | (((k >> 3) & 1) << 2));
   else if constexpr (R == 224) return (k >> 4) & 1;
