@@ -54,8 +54,9 @@ COPY_CALIB_BYTES = 256 << 20
 
 # Kernel sources whose hash keys the stored traffic counters of the dominant kernel.
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_gemm_bf16_ag.json")
-TRAFFIC_SOURCES = ["comm_matmul_tensor_amd/csrc/gemm_mfma.hpp", "comm_matmul_tensor_amd/csrc/gemm_bf16.hip",
-                   "comm_matmul_tensor_amd/csrc/device.hpp", "comm_matmul_tensor_amd/csrc/kernels.hpp"]
+TRAFFIC_SOURCES = ["comm_matmul_tensor_amd/csrc/gemm_mfma.hpp", "comm_matmul_tensor_amd/csrc/gemm16.hpp",
+                   "comm_matmul_tensor_amd/csrc/gemm_bf16.hip", "comm_matmul_tensor_amd/csrc/device.hpp",
+                   "comm_matmul_tensor_amd/csrc/kernels.hpp"]
 
 
 def log(msg):

@@ -292,7 +292,7 @@ mc2_status mc2_allgather_matmul(const void* const* shards, int world_size, int64
   int64_t slabs = (k + 63) / 64 < kArrivalSlabs ? (k + 63) / 64 : kArrivalSlabs;
   const int64_t slab_cols = ((k + slabs - 1) / slabs + 63) / 64 * 64;
   slabs = (k + slab_cols - 1) / slab_cols;
-  int64_t rows_chunk = gemm16_tile_rows(m, n);
+  int64_t rows_chunk = gemm16_tile_rows(m, n, a.b_kmajor);
   while (((m + rows_chunk - 1) / rows_chunk) * slabs > kArrivalFlags) rows_chunk *= 2;
   const int64_t chunks = (m + rows_chunk - 1) / rows_chunk;
   const int64_t first_chunk = (int64_t)rank_id * m_local / rows_chunk;
@@ -321,7 +321,7 @@ mc2_status mc2_allgather_matmul(const void* const* shards, int world_size, int64
   a.rows_chunk = rows_chunk;
   a.slab_cols = slab_cols;
   a.slabs = (int)slabs;
-  a.first_row_tile = (int)(first_chunk * rows_chunk / gemm16_tile_rows(m, n));
+  a.first_row_tile = (int)(first_chunk * rows_chunk / gemm16_tile_rows(m, n, a.b_kmajor));
   a.status_flag = ds->flags + kFallbackSlot;
   e = launch_gemm16(a, st);
   if (e == hipSuccess) e = hipEventRecord(ds->join, ds->copy_stream);

@@ -1,257 +1,21 @@
-// K1: 16-bit float GEMM on MFMA (v_mfma_f32_16x16x32_{bf16,f16}) with fp32
-// accumulation and a single rounding of each output, for
-//   AllGatherMatmul  out = AllGather_m(shards) @ x2    (torch_npu
-//                    npu_all_gather_base_mm page, "function" and "outputs")
-//   dX_partial       = dY @ W                          (hyper_parallel mc2.py,
-//   dW               = dY^T @ AllGather_m(X)            AllGatherMatmulFunction.backward)
-//
-// The tiling, LDS layout, transpose reads and XCD tile order are described
-// in gemm_mfma.hpp.  Specific to this kernel:
-//  - AllGather: A's row blocks are the rank shards, resolved per thread once
-//    before the K loop, so the "communication" is the addressing of the
-//    loads.  The gathered copy (gather_out) is written from the A tiles
-//    already in LDS, each K step by one workgroup of the row of tiles (the
-//    work spreads evenly): one write per element and no extra global read.
-//  - Epilogue: fp32 -> bf16 / fp16 with round-to-nearest-even, staged through
-//    LDS and stored as 16-byte row chunks.
-//  - MatmulReduceScatter (hyper_parallel mc2.py, module docstring and
-//    MatmulReduceScatterFunction.forward, Y = ReduceScatter_m(X @ W^T)): C is
-//    this rank's partial.  The tiles of its own row block are handed out
-//    last and store their rounded rows into the block output; the other rows
-//    of C are the blocks it sends.  A streaming pass then sums the block
-//    output with the blocks the other ranks sent, in rank order in fp32, and
-//    rounds once.  Reducing inside the GEMM epilogue instead made every own
-//    tile read seven scattered 256-byte row pieces per row at the same time,
-//    well below streaming bandwidth; the separate pass reads whole rows.
-#include <algorithm>
-
-#include "gemm_mfma.hpp"
+// K1 entry points and the bf16 instantiations; the fp16 ones are compiled in
+// gemm_f16.hip (same implementation, gemm16.hpp) so the two build in parallel.
+#include "gemm16.hpp"
 
 namespace mc2 {
-namespace {
 
-using namespace gemm;
-
-template <int DT>
-struct Ops16 {
-  typedef f32x4 Acc;
-  static __device__ __forceinline__ Acc mfma(u32x4 a, u32x4 b, Acc c) {
-    if constexpr (DT == DT_BF16)
-      return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
-    else
-      return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
-  }
-  static __device__ __forceinline__ uint16_t cvt(float f) {
-    return DT == DT_BF16 ? f32_to_bf16_bits(f) : f32_to_f16_bits(f);
-  }
-  static __device__ __forceinline__ float dec(uint32_t bits) {
-    return DT == DT_BF16 ? bf16_bits_to_f32(bits & 0xFFFFu) : f16_bits_to_f32(bits & 0xFFFFu);
-  }
-};
-
-// Reduce-scatter store of a staged tile (Problem::rs_out): the rows of the
-// own block go to rs_out (row t of the block to rs_out row t), the others
-// to C.  The rank-ordered sum with the received blocks follows in
-// rs_reduce_kernel.
-template <int BM, int BN, bool VEC>
-__device__ __forceinline__ void store_rs_tile(const uint16_t* h0, const uint16_t* h1, uint16_t* C, const Problem& p,
-                                              int64_t m0, int64_t n0) {
-  constexpr int kRowChunks = BN / 8;
-  const int64_t n = p.n;
-  for (int c = threadIdx.x; c < BM * kRowChunks; c += kThreads) {
-    const int row = c / kRowChunks, col = (c % kRowChunks) * 8;
-    const int64_t grow = m0 + row, gcol = n0 + col;
-    if (grow >= p.m) continue;
-    const uint16_t* src = staged_chunk<BM, BN>(h0, h1, row, col);
-    const int64_t t = grow - p.rs_row0;
-    uint16_t* dst = (t >= 0 && t < p.rs_rows) ? static_cast<uint16_t*>(p.rs_out) + t * n : C + grow * n;
-    if (VEC && gcol + 8 <= n) {
-      *reinterpret_cast<u32x4*>(dst + gcol) = *reinterpret_cast<const u32x4*>(src);
-    } else {
-      for (int e = 0; e < 8; e++)
-        if (gcol + e < n) dst[gcol + e] = src[e];
-    }
-  }
+// Arrival mode needs AK (A K-major); B may be either layout.
+int gemm16_tile_rows(int64_t m, int64_t n, int b_kmajor) {
+  const TileChoice* t = b_kmajor ? tiles16<true, true>() : tiles16<true, false>();
+  return t[pick_tile(m, n, t, kNumTiles16)].bm;
 }
-
-// The reduction of the own block, in place in rs_out: element e becomes
-// round(B_0 + B_1 + ... + B_{ranks-1}) summed in fp32 in rank order, B_j =
-// rs_recv[j][e] and B_rank = the rounded partial the GEMM left in rs_out.
-// A streaming pass over whole rows (HBM-bound): 8 elements per thread and
-// step, every block's load issued before the sum.
-struct RsReduceArgs {
-  uint16_t* out;
-  const uint16_t* recv[kMaxRanks];  // own and unused slots: out
-  int ranks;
-  int64_t elems;
-};
-
-template <int DT, bool VEC>
-__global__ __launch_bounds__(256) void rs_reduce_kernel(RsReduceArgs a) {
-  using O = Ops16<DT>;
-  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-  if constexpr (VEC) {
-    const int64_t chunks = a.elems / 8;
-    for (int64_t c = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; c < chunks; c += stride) {
-      u32x4 v[kMaxRanks];
-#pragma unroll
-      for (int j = 0; j < kMaxRanks; j++) v[j] = reinterpret_cast<const u32x4*>(a.recv[j])[c];
-      float sum[8];
-#pragma unroll
-      for (int j = 0; j < kMaxRanks; j++) {
-        const bool used = j < a.ranks;
-#pragma unroll
-        for (int e = 0; e < 8; e++) {
-          const float f = O::dec(v[j][e / 2] >> (16 * (e & 1)));
-          sum[e] = j == 0 ? f : (used ? sum[e] + f : sum[e]);
-        }
-      }
-      u32x4 o;
-#pragma unroll
-      for (int w = 0; w < 4; w++) o[w] = (uint32_t)O::cvt(sum[2 * w]) | ((uint32_t)O::cvt(sum[2 * w + 1]) << 16);
-      reinterpret_cast<u32x4*>(a.out)[c] = o;
-    }
-  } else {
-    for (int64_t e = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; e < a.elems; e += stride) {
-      float sum = 0.0f;
-      for (int j = 0; j < a.ranks; j++) sum = j == 0 ? O::dec(a.recv[j][e]) : sum + O::dec(a.recv[j][e]);
-      a.out[e] = O::cvt(sum);
-    }
-  }
-}
-
-template <int DT>
-hipError_t launch_rs_reduce(const GemmArgs& g, hipStream_t s) {
-  RsReduceArgs a{};
-  a.out = static_cast<uint16_t*>(g.rs_out);
-  for (int j = 0; j < kMaxRanks; j++)
-    a.recv[j] = (j < g.rs_ranks && j != g.rs_rank) ? static_cast<const uint16_t*>(g.rs_recv[j]) : a.out;
-  a.ranks = g.rs_ranks;
-  a.elems = g.rs_rows * g.n;
-  // 16-byte chunks when every row of every block starts 16-byte aligned
-  const bool vec = g.n % 8 == 0;
-  const int64_t work = vec ? a.elems / 8 : a.elems;
-  const int64_t blocks = std::min<int64_t>((work + 255) / 256, 256 * 16);
-  if (vec) rs_reduce_kernel<DT, true><<<(unsigned)blocks, 256, 0, s>>>(a);
-  else rs_reduce_kernel<DT, false><<<(unsigned)blocks, 256, 0, s>>>(a);
-  return hipGetLastError();
-}
-
-// ARR: arrival emulation (A arrives in p.arrived piece by piece; gemm_mfma.hpp).
-template <int BM, int BN, bool AK, bool BKM, bool VEC, int DT, bool ARR>
-__global__ __launch_bounds__(kThreads, 1) void gemm16_kernel(Problem p, void* c) {
-  constexpr int FM = BM / 32, FN = BN / 32;
-  __shared__ __attribute__((aligned(1024))) uint8_t s0[lds_stage_array_bytes<BM, BN>()];
-  __shared__ __attribute__((aligned(1024))) uint8_t s1[lds_stage_array_bytes<BM, BN>()];
-  __shared__ __attribute__((aligned(1024))) uint8_t s2[lds_stage_array_bytes<BM, BN>()];
-  int tm, tn;
-  tile_of_block(p.m, p.n, BM, BN, p.tile_order_cols, p.tile_group, tm, tn, p.first_row_tile);
-  const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
-  const int tiles_n = (int)((p.n + BN - 1) / BN);
-
-  typename Ops16<DT>::Acc acc[FM][FN];
-#pragma unroll
-  for (int i = 0; i < FM; i++)
-#pragma unroll
-    for (int j = 0; j < FN; j++) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  run_mainloop<2, BM, BN, AK, BKM, VEC, ARR, Ops16<DT>>(p, m0, n0, tn, tiles_n, s0, s1, s2, acc);
-
-  uint16_t* h0 = reinterpret_cast<uint16_t*>(s0);
-  uint16_t* h1 = reinterpret_cast<uint16_t*>(s1);
-  stage_c16<BM, BN>(h0, h1, [&](int i, int j, int r, int, int) { return Ops16<DT>::cvt(acc[i][j][r]); });
-  if (p.rs_out) store_rs_tile<BM, BN, VEC>(h0, h1, static_cast<uint16_t*>(c), p, m0, n0);
-  else store_c16_tile<BM, BN, VEC>(h0, h1, static_cast<uint16_t*>(c), p.m, p.n, m0, n0);
-}
-
-template <int BM, int BN, bool AK, bool BKM, int DT>
-hipError_t launch_cfg(Problem p, void* c, hipStream_t s) {
-  const int64_t tiles = ((p.m + BM - 1) / BM) * ((p.n + BN - 1) / BN);
-  // 16-byte vector access needs every row of every operand and of C to start
-  // 16-byte aligned; the buffer-load staging needs operands below 2 GiB and
-  // gathered row blocks of a multiple of 8 rows (otherwise: checked path)
-  const int64_t a_bytes = AK ? (p.ready ? p.m : p.rows_per_part) * p.k * 2 : p.k * p.m * 2;
-  const int parts = p.rows_per_part == p.m ? 1 : 2;
-  const bool vec = (p.k % 8 == 0) && (AK || p.m % 8 == 0) && (p.n % 8 == 0) &&
-                   dma_buffers_ok(a_bytes, p.k * p.n * 2, parts, p.rows_per_part) &&
-                   dma_buffers_ok(p.rows_per_part * p.k * 2, 0, parts, p.rows_per_part);
-  p.tile_order_cols = prefer_column_order(p.m, p.n, p.k, 2) ? 1 : 0;
-  p.tile_group = choose_tile_group(p.m, p.n, BM, BN, p.tile_order_cols);
-  if (p.rs_out) {  // own block last: start at the tile row after it
-    const int64_t tiles_m = (p.m + BM - 1) / BM;
-    p.first_row_tile = (int)(((p.rs_row0 + p.rs_rows) / BM) % tiles_m);
-  }
-  if constexpr (AK) {
-    if (p.ready) {
-      if (vec) gemm16_kernel<BM, BN, AK, BKM, true, DT, true><<<(unsigned)tiles, kThreads, 0, s>>>(p, c);
-      else gemm16_kernel<BM, BN, AK, BKM, false, DT, true><<<(unsigned)tiles, kThreads, 0, s>>>(p, c);
-      return hipGetLastError();
-    }
-  }
-  if (vec) gemm16_kernel<BM, BN, AK, BKM, true, DT, false><<<(unsigned)tiles, kThreads, 0, s>>>(p, c);
-  else gemm16_kernel<BM, BN, AK, BKM, false, DT, false><<<(unsigned)tiles, kThreads, 0, s>>>(p, c);
-  return hipGetLastError();
-}
-
-const TileChoice kTiles16[] = {{128, 224}, {224, 128}, {128, 256}, {128, 128}};
-constexpr int kNumTiles16 = sizeof(kTiles16) / sizeof(kTiles16[0]);
-
-template <bool AK, bool BKM, int DT>
-hipError_t launch_layout(const Problem& p, void* c, hipStream_t s) {
-  switch (pick_tile(p.m, p.n, kTiles16, kNumTiles16)) {
-    case 0: return launch_cfg<128, 224, AK, BKM, DT>(p, c, s);
-    case 1: return launch_cfg<224, 128, AK, BKM, DT>(p, c, s);
-    case 2: return launch_cfg<128, 256, AK, BKM, DT>(p, c, s);
-    default: return launch_cfg<128, 128, AK, BKM, DT>(p, c, s);
-  }
-}
-
-template <int DT>
-hipError_t launch_dt(const GemmArgs& g, hipStream_t s) {
-  Problem p{};
-  for (int i = 0; i < kMaxRanks; i++) p.a_parts[i] = g.a_parts[i < g.num_parts ? i : 0];
-  p.rows_per_part = g.rows_per_part;
-  p.b = g.b;
-  p.gather_out = g.gather_out;
-  p.m = g.m;
-  p.n = g.n;
-  p.k = g.k;
-  p.a_ld = g.k * 2;  // plain A: one K segment
-  p.kseg = g.k;
-  p.kseg_stride = 0;
-  p.a_part_bytes = g.rows_per_part * g.k * 2;
-  if (g.rs_out) {
-    p.rs_out = g.rs_out;
-    p.rs_row0 = g.rs_row0;
-    p.rs_rows = g.rs_rows;
-  }
-  if (g.ready_flags) {  // arrival emulation: A arrives in gather_out, which the kernel only reads
-    p.ready = g.ready_flags;
-    p.ready_value = g.ready_value;
-    p.fallbacks = g.status_flag;
-    p.arrived = g.gather_out;
-    p.rows_chunk = g.rows_chunk;
-    p.slab_cols = g.slab_cols;
-    p.slabs = g.slabs;
-    p.first_row_tile = g.first_row_tile;
-    p.gather_out = nullptr;
-  }
-  if (g.a_kmajor && g.b_kmajor) return launch_layout<true, true, DT>(p, g.c, s);
-  if (g.a_kmajor && !g.b_kmajor) return launch_layout<true, false, DT>(p, g.c, s);
-  if (!g.a_kmajor && !g.b_kmajor) return launch_layout<false, false, DT>(p, g.c, s);
-  return launch_layout<false, true, DT>(p, g.c, s);
-}
-
-}  // namespace
-
-int gemm16_tile_rows(int64_t m, int64_t n) { return kTiles16[pick_tile(m, n, kTiles16, kNumTiles16)].bm; }
 
 hipError_t launch_gemm16(const GemmArgs& g, hipStream_t s) {
   if (g.m < 1 || g.n < 1 || g.k < 1 || g.num_parts < 1 || g.num_parts > kMaxRanks) return hipErrorInvalidValue;
   if (g.num_parts * g.rows_per_part != g.m) return hipErrorInvalidValue;
   if (g.gather_out && !g.a_kmajor) return hipErrorInvalidValue;
   if (g.ready_flags) {
-    const int bm = gemm16_tile_rows(g.m, g.n);
+    const int bm = gemm16_tile_rows(g.m, g.n, g.b_kmajor);
     if (!g.gather_out || !g.status_flag || !g.a_kmajor || g.rows_chunk < bm || g.rows_chunk % bm != 0 ||
         g.slabs < 1 || g.slab_cols < 1 || g.slab_cols % 64 != 0 || (int64_t)g.slabs * g.slab_cols < g.k ||
         g.first_row_tile < 0 || (int64_t)g.first_row_tile * bm >= g.m)
@@ -265,9 +29,7 @@ hipError_t launch_gemm16(const GemmArgs& g, hipStream_t s) {
       if (j != g.rs_rank && !g.rs_recv[j]) return hipErrorInvalidValue;
   }
   if (g.dtype != DT_BF16 && g.dtype != DT_F16) return hipErrorInvalidValue;
-  hipError_t e = g.dtype == DT_BF16 ? launch_dt<DT_BF16>(g, s) : launch_dt<DT_F16>(g, s);
-  if (e != hipSuccess || !g.rs_out) return e;
-  return g.dtype == DT_BF16 ? launch_rs_reduce<DT_BF16>(g, s) : launch_rs_reduce<DT_F16>(g, s);
+  return g.dtype == DT_BF16 ? launch_gemm16_dt<DT_BF16>(g, s) : launch_gemm16_f16(g, s);
 }
 
 }  // namespace mc2

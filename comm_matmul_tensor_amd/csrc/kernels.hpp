@@ -41,7 +41,7 @@ struct GemmArgs {
   // gather_out; rows [g rows_chunk, (g+1) rows_chunk) x columns
   // [s slab_cols, (s+1) slab_cols) may be read once
   // ready_flags[g * slabs + s] == ready_value.  rows_chunk must be a
-  // multiple of gemm16_tile_rows(m, n) and slab_cols of 64.  Tile row
+  // multiple of gemm16_tile_rows(m, n, b_kmajor) and slab_cols of 64.  Tile row
   // first_row_tile is handed out first; *status_flag counts wavefronts
   // whose wait timed out (they read A from a_parts instead).
   const unsigned* ready_flags;
@@ -61,8 +61,11 @@ struct GemmArgs {
   int64_t rs_row0, rs_rows;
 };
 hipError_t launch_gemm16(const GemmArgs& a, hipStream_t s);
-// Tile height (rows of C per workgroup) launch_gemm16 uses for an (m, n) C.
-int gemm16_tile_rows(int64_t m, int64_t n);
+// The fp16 part of launch_gemm16 (its own translation unit).
+hipError_t launch_gemm16_f16(const GemmArgs& a, hipStream_t s);
+// Tile height (rows of C per workgroup) launch_gemm16 uses for an (m, n) C
+// with A K-major and B K-major (b_kmajor = 1) or N-major.
+int gemm16_tile_rows(int64_t m, int64_t n, int b_kmajor);
 
 // ---- arrival emulation: copy of the shards into gather_out piece by piece
 // (row chunk g, slab s of K), each piece followed by its ready flag

@@ -107,9 +107,10 @@ def test_ag_full_config_sampled(mc2):
     assert_close16(o[rows], want, "bf16", "sampled rows")
 
 
-# the last two take the 128 x 256 tile for dX (whole and ragged in both dimensions)
+# the last three take the 256 x 128 tile for dX (whole, and ragged in both
+# dimensions) and the 128 x 256 tile for dW
 @pytest.mark.parametrize("m,n_l,k", [(64, 256, 32), (200, 300, 130), (1024, 256, 520), (33, 1000, 7),
-                                     (4096, 256, 2048), (8190, 264, 2040)])
+                                     (4096, 256, 2048), (8190, 264, 2040), (256, 4096, 2048)])
 @pytest.mark.parametrize("dtype", ["bf16", "f16"])
 def test_backward_shapes(mc2, m, n_l, k, dtype):
     import torch
