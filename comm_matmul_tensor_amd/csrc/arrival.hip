@@ -10,10 +10,13 @@
 // AllGather delivers them), so the GEMM's tiles can start on the first slab
 // of K while later slabs are still being copied.
 //
-// Visibility across XCDs: the copy's stores are device-scope atomic stores,
-// which write through the XCD's L2, so the release fence before the flag has
-// no dirty lines of the piece to write back (a fence that had to write back
-// a whole piece made the copy several times slower).
+// Visibility across XCDs: the copy's stores carry the device-scope cache
+// policy (sc1), so they write through the XCD's L2 and the release fence
+// before the flag has no dirty lines of the piece to write back (a fence that
+// had to write back a whole piece made the copy several times slower).  They
+// are 16-byte buffer stores, whole 128-byte lines per eight lanes; 8-byte
+// device-scope atomic stores (the same policy) serve a gather_out of 2 GiB or
+// more and rows that are not whole 16-byte pieces.
 #include "device.hpp"
 #include "kernels.hpp"
 
@@ -22,6 +25,7 @@ namespace {
 
 constexpr int kCopyThreads = 256;
 constexpr int kBatch = 16;  // 16-byte loads in flight per thread
+constexpr int kPolicyDevice = 16;  // buffer store cache policy: sc1, coherent device-wide
 
 __global__ __launch_bounds__(kCopyThreads) void arrive_kernel(ArrivalArgs a) {
   // piece w: slab w / chunks of row chunk (first_chunk + w % chunks) % chunks
@@ -41,6 +45,9 @@ __global__ __launch_bounds__(kCopyThreads) void arrive_kernel(ArrivalArgs a) {
     // and steps its (row, piece) position without dividing.  kBatch loads per
     // thread are issued before their stores.
     const int per_row = (int)(cols / 8), n = (int)rows * per_row;
+    const bool buf = m * a.k * 2 < ((int64_t)1 << 31);  // byte offsets fit the buffer's 32 bits
+    const __amdgpu_buffer_rsrc_t rsrc =
+        __builtin_amdgcn_make_buffer_rsrc(gout, 0, buf ? (int)(m * a.k * 2) : 0, 0x00020000);
     const int dq = kCopyThreads / per_row, dc = kCopyThreads % per_row;
     int r = (int)threadIdx.x / per_row, c = (int)threadIdx.x % per_row;
     for (int i0 = (int)threadIdx.x; i0 < n; i0 += kBatch * kCopyThreads) {
@@ -65,7 +72,9 @@ __global__ __launch_bounds__(kCopyThreads) void arrive_kernel(ArrivalArgs a) {
       }
 #pragma unroll
       for (int j = 0; j < kBatch; j++)
-        if (dst[j] >= 0) {
+        if (dst[j] >= 0 && buf) {
+          __builtin_amdgcn_raw_buffer_store_b128(v[j], rsrc, (int)(dst[j] * 2), 0, kPolicyDevice);
+        } else if (dst[j] >= 0) {
           uint64_t* d = reinterpret_cast<uint64_t*>(gout + dst[j]);
           __hip_atomic_store(d, (uint64_t)v[j][0] | ((uint64_t)v[j][1] << 32), __ATOMIC_RELAXED,
                              __HIP_MEMORY_SCOPE_AGENT);
