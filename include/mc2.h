@@ -165,7 +165,8 @@ mc2_status mc2_matmul_grad_input(const void* dy, const void* w, int64_t m, int64
  * recv      world_size pointers: recv[j], j != rank_id, is a (m / ws, n)
  *           row-major block of `dtype`; recv[rank_id] is not read (may be NULL)
  * out, partial_out  as above, of `dtype` (F16 or BF16)
- * All pointers are caller-owned device memory, 16-byte aligned.
+ * All pointers are caller-owned device memory, 16-byte aligned; out must not
+ * overlap partial_out or a received block (the sum is formed in place in out).
  */
 mc2_status mc2_matmul_reduce_scatter(const void* x, const void* x2, int world_size, int rank_id, int64_t m,
                                      int64_t k, int64_t n, int x2_trans, mc2_dtype dtype, const void* const* recv,
