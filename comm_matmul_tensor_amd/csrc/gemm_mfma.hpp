@@ -564,9 +564,11 @@ __device__ __forceinline__ void mainloop_fast(const Problem& p, int64_t m0, int6
   constexpr int ND = DA::kN + DB::kN;  // DMA instructions per thread and step
   DA da;
   DB db;
+  DA da_shards;  // arrival: A from the shards, for a wavefront whose wait timed out
   if constexpr (ARR) {
     const void* arrived[1] = {p.arrived};
     da.init_k(arrived, p.m, p.k * E, m0, p.m, p.m * p.k * E);
+    da_shards.init_k(p.a_parts, p.rows_per_part, p.a_ld, m0, p.m, p.a_part_bytes);
   } else if constexpr (AK) {
     da.init_k(p.a_parts, p.rows_per_part, p.a_ld, m0, p.m, p.a_part_bytes);
   } else {
@@ -597,7 +599,7 @@ __device__ __forceinline__ void mainloop_fast(const Problem& p, int64_t m0, int6
     if (fell_back) return;
     if (!wait_flag(flags + kt / sps, p.ready_value)) {
       fell_back = true;
-      da.init_k(p.a_parts, p.rows_per_part, p.a_ld, m0, p.m, p.a_part_bytes);
+      da = da_shards;
       if (threadIdx.x % 64 == 0) __hip_atomic_fetch_add(p.fallbacks, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   };
