@@ -24,9 +24,12 @@ Inputs are generated on the host, copied to HBM before timing, and stay
 resident.  --copy-calib adds a plain 256 MiB device copy to every step (the
 reference kernel for scaling FETCH_SIZE / WRITE_SIZE counters to bytes);
 --summarize DIR turns a directory of rocprofv3 CSV output into the summary
-kept under profiles/.  W warm-up steps, then exactly K timed steps between two
-synchronisations.  Per-kernel durations come from HIP events recorded on the
-stream the kernels run on (torch's current stream, which libmc2 is handed).
+kept under profiles/.  W warm-up steps (default 5), then exactly K timed steps
+(default 50) between two synchronisations.  Per-call durations come from HIP
+events recorded on the stream the kernels run on (torch's current stream,
+which libmc2 is handed); each row reports their mean (the roofline figure),
+minimum and median.  Every step runs all rows, so each call finds the caches
+holding the other rows' data (largely dirty outputs), not its own inputs.
 The headline value is the AllGatherMatmul's TFLOP/s; every row's figure and
 its roofline fraction are in "rows".  The oracle (CPU) is timed on a bounded
 sample of the AllGatherMatmul workload for the "cpu_baseline" entry.
@@ -66,8 +69,8 @@ def log(msg):
 def parse():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--rows", default=",".join(ALL_ROWS), help="comma-separated subset of rows")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-parity", action="store_true", help="skip the sampled oracle check")
@@ -561,6 +564,7 @@ def main():
         out_rows[row.name] = {"achieved": round(achieved, 2), "unit": row.unit, "bound": row.bound,
                               "peak": row.peak, "frac": round(achieved / row.peak, 4),
                               "us_per_call": round(avg_ms * 1e3, 2), "min_us": round(min(ms) * 1e3, 2),
+                              "median_us": round(sorted(ms)[len(ms) // 2] * 1e3, 2),
                               "kernels": [k for k, _ in row.launches]}
     if not args.no_parity:
         for row in rows:
