@@ -19,6 +19,14 @@ typedef int i32x2 __attribute__((ext_vector_type(2)));
 // dtype codes, mirroring mc2_dtype (kept as plain ints for template use)
 enum : int { DT_F32 = 0, DT_F16 = 1, DT_BF16 = 2, DT_I8 = 3, DT_I32 = 4, DT_E4M3FN = 5, DT_E5M2 = 6, DT_E8M0 = 7 };
 
+// 16-byte store of output that no later step of this kernel reads:
+// non-temporal, so the output streams to memory without displacing the
+// operands' lines from the caches or making the caches write back other
+// dirty lines first.
+__device__ __forceinline__ void store_out16(void* dst, u32x4 v) {
+  __builtin_nontemporal_store(v, static_cast<u32x4*>(dst));
+}
+
 // fp32 -> bf16 bits, round to nearest even (the gfx950 conversion is RNE).
 __device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
   __bf16 h = (__bf16)f;

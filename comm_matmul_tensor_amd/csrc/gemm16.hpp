@@ -66,9 +66,13 @@ __device__ __forceinline__ void store_rs_tile(const uint16_t* h0, const uint16_t
     if (grow >= p.m) continue;
     const uint16_t* src = staged_chunk<BM, BN>(h0, h1, row, col);
     const int64_t t = grow - p.rs_row0;
-    uint16_t* dst = (t >= 0 && t < p.rs_rows) ? static_cast<uint16_t*>(p.rs_out) + t * n : C + grow * n;
+    const bool own = t >= 0 && t < p.rs_rows;
+    uint16_t* dst = own ? static_cast<uint16_t*>(p.rs_out) + t * n : C + grow * n;
     if (VEC && gcol + 8 <= n) {
-      *reinterpret_cast<u32x4*>(dst + gcol) = *reinterpret_cast<const u32x4*>(src);
+      // rs_reduce_kernel reads the own block right after: plain stores keep it in the caches
+      const u32x4 v = *reinterpret_cast<const u32x4*>(src);
+      if (own) *reinterpret_cast<u32x4*>(dst + gcol) = v;
+      else store_out16(dst + gcol, v);
     } else {
       for (int e = 0; e < 8; e++)
         if (gcol + e < n) dst[gcol + e] = src[e];
@@ -111,7 +115,7 @@ __global__ __launch_bounds__(256) void rs_reduce_kernel(RsReduceArgs a) {
       u32x4 o;
 #pragma unroll
       for (int w = 0; w < 4; w++) o[w] = (uint32_t)O::cvt(sum[2 * w]) | ((uint32_t)O::cvt(sum[2 * w + 1]) << 16);
-      reinterpret_cast<u32x4*>(a.out)[c] = o;
+      store_out16(reinterpret_cast<u32x4*>(a.out) + c, o);
     }
   } else {
     for (int64_t e = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; e < a.elems; e += stride) {

@@ -341,7 +341,7 @@ __device__ __forceinline__ void copy_gather(const uint8_t* As, void* gout, int64
     const u32x4 v = *reinterpret_cast<const u32x4*>(As + swz(row, chunk));
     T* dst = static_cast<T*>(gout) + grow * k + gk;
     if (gk + CH <= k && (k % CH) == 0) {
-      *reinterpret_cast<u32x4*>(dst) = v;
+      store_out16(dst, v);
     } else {
       T e[CH];
       __builtin_memcpy(e, &v, 16);
@@ -886,7 +886,7 @@ __device__ __forceinline__ void store_c16_tile(const uint16_t* h0, const uint16_
     if (grow >= m) continue;
     const uint16_t* src = staged_chunk<BM, BN>(h0, h1, row, col);
     if (VEC && gcol + 8 <= n) {
-      *reinterpret_cast<u32x4*>(C + grow * n + gcol) = *reinterpret_cast<const u32x4*>(src);
+      store_out16(C + grow * n + gcol, *reinterpret_cast<const u32x4*>(src));
     } else {
       for (int j = 0; j < 8; j++)
         if (gcol + j < n) C[grow * n + gcol + j] = src[j];
