@@ -28,10 +28,15 @@ COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-result", f"-I{os.p
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
     extra = []
-    if os.path.basename(src).startswith("gemm_"):
+    name = os.path.basename(src)
+    if name.startswith("gemm_"):
         # MFMA accumulators in VGPRs: the AGPR form made the register allocator
         # rotate accumulators through copies inside the main loop.
         extra = ["-mllvm", "-amdgpu-mfma-vgpr-form"]
+    elif name == "gemm256.hip":
+        # 256 accumulators per lane: AGPR form; and full unrolling of the
+        # 64-MFMA half steps, which exceed the default unroll limit
+        extra = ["-mllvm", "-pragma-unroll-threshold=1000000"]
     cmd = [HIPCC] + COMMON + DEVICE_FLAGS + extra + ["-c", src, "-o", obj]
     if src.endswith(".cpp"):
         cmd = [HIPCC, "-x", "hip"] + COMMON + DEVICE_FLAGS + ["-c", src, "-o", obj]

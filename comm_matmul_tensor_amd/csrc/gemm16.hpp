@@ -30,6 +30,13 @@
 #include "gemm_mfma.hpp"
 
 namespace mc2 {
+
+// The 256 x 256 tile launches (gemm256.hip, its own translation unit: the
+// 256 accumulator registers per lane of that tile need the AGPR form of the
+// MFMAs, while the other tiles are built with their accumulators in VGPRs).
+template <bool AK, bool BKM, int DT>
+hipError_t launch_gemm16_256(const gemm::Problem& p, void* c, hipStream_t s);
+
 namespace {
 
 using namespace gemm;
@@ -147,9 +154,10 @@ hipError_t launch_rs_reduce(const GemmArgs& g, hipStream_t s) {
 template <int BM, int BN, bool AK, bool BKM, bool VEC, int DT, bool ARR>
 __global__ __launch_bounds__(kThreads, 1) void gemm16_kernel(Problem p, void* c) {
   constexpr int FM = BM / 32, FN = BN / 32;
+  constexpr int NS = lds_stages<BM, BN>();
   __shared__ __attribute__((aligned(1024))) uint8_t s0[lds_stage_array_bytes<BM, BN>()];
   __shared__ __attribute__((aligned(1024))) uint8_t s1[lds_stage_array_bytes<BM, BN>()];
-  __shared__ __attribute__((aligned(1024))) uint8_t s2[lds_stage_array_bytes<BM, BN>()];
+  __shared__ __attribute__((aligned(1024))) uint8_t s2[NS == 3 ? lds_stage_array_bytes<BM, BN>() : 16];
   int tm, tn;
   tile_of_block(p.m, p.n, BM, BN, p.tile_order_cols, p.tile_group, tm, tn, p.first_row_tile);
   const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
@@ -161,7 +169,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm16_kernel(Problem p, void* c)
 #pragma unroll
     for (int j = 0; j < FN; j++) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  run_mainloop<2, BM, BN, AK, BKM, VEC, ARR, Ops16<DT>>(p, m0, n0, tn, tiles_n, s0, s1, s2, acc);
+  run_mainloop<2, BM, BN, AK, BKM, VEC, ARR, NS, Ops16<DT>>(p, m0, n0, tn, tiles_n, s0, s1, s2, acc);
 
   uint16_t* h0 = reinterpret_cast<uint16_t*>(s0);
   uint16_t* h1 = reinterpret_cast<uint16_t*>(s1);
@@ -187,13 +195,15 @@ hipError_t launch_cfg(Problem p, void* c, hipStream_t s) {
     const int64_t tiles_m = (p.m + BM - 1) / BM;
     p.first_row_tile = (int)(((p.rs_row0 + p.rs_rows) / BM) % tiles_m);
   }
-  if constexpr (AK) {
+  if constexpr (AK && lds_stages<BM, BN>() == 3) {
     if (p.ready) {
       if (vec) gemm16_kernel<BM, BN, AK, BKM, true, DT, true><<<(unsigned)tiles, kThreads, 0, s>>>(p, c);
       else gemm16_kernel<BM, BN, AK, BKM, false, DT, true><<<(unsigned)tiles, kThreads, 0, s>>>(p, c);
       return hipGetLastError();
     }
   }
+  // the two-stage loop has neither the arrival wait nor the gather copy
+  if (lds_stages<BM, BN>() == 2 && (p.ready || p.gather_out)) return hipErrorInvalidValue;
   if (vec) gemm16_kernel<BM, BN, AK, BKM, true, DT, false><<<(unsigned)tiles, kThreads, 0, s>>>(p, c);
   else gemm16_kernel<BM, BN, AK, BKM, false, DT, false><<<(unsigned)tiles, kThreads, 0, s>>>(p, c);
   return hipGetLastError();
@@ -202,21 +212,31 @@ hipError_t launch_cfg(Problem p, void* c, hipStream_t s) {
 // Tile shapes in order of preference among equal scores.  Of 256 x 128 and
 // 128 x 256 (equal work per tile) the one with the narrower N-major operand
 // comes first: that operand is read with transpose reads, which move fewer
-// bytes per cycle than the K-major operand's 16-byte reads.
-const TileChoice kTilesBN[] = {{128, 224}, {224, 128}, {256, 128}, {128, 256}, {128, 128}};  // B N-major
-const TileChoice kTilesAM[] = {{128, 224}, {224, 128}, {128, 256}, {256, 128}, {128, 128}};  // otherwise
-constexpr int kNumTiles16 = sizeof(kTilesBN) / sizeof(kTilesBN[0]);
+// bytes per cycle than the K-major operand's 16-byte reads.  256 x 256 (two
+// LDS stages) comes last and is used neither with the arrival wait nor with
+// the gather copy: the first kNumTiles3 entries (three stages) serve those.
+// It is left out with a K-contiguous A and an N-contiguous B: there the
+// transpose-read offsets of its eight B fragments push the 256-accumulator
+// kernel past its registers, and the 256 x 128 tile measured faster.
+const TileChoice kTilesBN[] = {{128, 224}, {224, 128}, {256, 128}, {128, 256}, {128, 128}};  // A K-, B N-major
+const TileChoice kTilesAM[] = {{128, 224}, {224, 128}, {128, 256}, {256, 128}, {128, 128}, {256, 256}};  // otherwise
+constexpr int kNumTiles3 = 5;
 
 template <bool AK, bool BKM>
 constexpr const TileChoice* tiles16() { return (AK && !BKM) ? kTilesBN : kTilesAM; }
+template <bool AK, bool BKM>
+constexpr int num_tiles16() { return (AK && !BKM) ? 5 : 6; }
 
 template <bool AK, bool BKM, int DT>
 hipError_t launch_layout(const Problem& p, void* c, hipStream_t s) {
-  const TileChoice t = tiles16<AK, BKM>()[pick_tile(p.m, p.n, tiles16<AK, BKM>(), kNumTiles16)];
+  const int count = (p.ready || p.gather_out) ? kNumTiles3 : num_tiles16<AK, BKM>();
+  const TileChoice t = tiles16<AK, BKM>()[pick_tile(p.m, p.n, tiles16<AK, BKM>(), count)];
   if (t.bm == 128 && t.bn == 224) return launch_cfg<128, 224, AK, BKM, DT>(p, c, s);
   if (t.bm == 224 && t.bn == 128) return launch_cfg<224, 128, AK, BKM, DT>(p, c, s);
   if (t.bm == 256 && t.bn == 128) return launch_cfg<256, 128, AK, BKM, DT>(p, c, s);
   if (t.bm == 128 && t.bn == 256) return launch_cfg<128, 256, AK, BKM, DT>(p, c, s);
+  if constexpr (!(AK && !BKM))
+    if (t.bm == 256 && t.bn == 256) return launch_gemm16_256<AK, BKM, DT>(p, c, s);
   return launch_cfg<128, 128, AK, BKM, DT>(p, c, s);
 }
 

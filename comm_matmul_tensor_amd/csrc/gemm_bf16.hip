@@ -7,7 +7,7 @@ namespace mc2 {
 // Arrival mode needs AK (A K-major); B may be either layout.
 int gemm16_tile_rows(int64_t m, int64_t n, int b_kmajor) {
   const TileChoice* t = b_kmajor ? tiles16<true, true>() : tiles16<true, false>();
-  return t[pick_tile(m, n, t, kNumTiles16)].bm;
+  return t[pick_tile(m, n, t, kNumTiles3)].bm;
 }
 
 hipError_t launch_gemm16(const GemmArgs& g, hipStream_t s) {

@@ -551,11 +551,21 @@ struct FragReader {
 // so the poll completes under the wait every step already makes and a slab
 // that is on time costs no extra wait.  A wavefront whose wait times out
 // reads the rest of A from the shards.
-template <int E, int BM, int BN, bool AK, bool BKM, bool GATHER, bool ARR, typename Ops>
+//
+// Two stages (NS = 2, for tiles whose three stages would not fit in LDS):
+// the DMA of step kt+2 goes into step kt's own stage during half 1 of step
+// kt, right after the barrier that ends every read of that stage, and has
+// until the barrier of step kt+1 to land (one step, against one and a half
+// with three stages):
+//   read half 1 of step kt; MFMAs of half 0;
+//   wait for the DMA of step kt+1, barrier;
+//   issue the DMA of step kt+2; read half 0 of step kt+1; MFMAs of half 1.
+template <int E, int BM, int BN, bool AK, bool BKM, bool GATHER, bool ARR, int NS, typename Ops>
 __device__ __forceinline__ void mainloop_fast(const Problem& p, int64_t m0, int64_t n0, int gather_phase,
                                               int gather_every, uint8_t* L0, uint8_t* L1, uint8_t* L2,
                                               typename Ops::Acc (&acc)[BM / 32][BN / 32]) {
   static_assert(!ARR || (AK && !GATHER), "arrival needs a K-contiguous A and no gather copy");
+  static_assert(NS == 3 || (NS == 2 && !ARR), "two stages: no arrival wait");
   constexpr int BK = kRowBytes / E;  // K elements per step
   constexpr int kATile = BM * kRowBytes;
   constexpr int WM = BM / 2, WN = BN / 2, FM = WM / 16, FN = WN / 16;
@@ -695,6 +705,27 @@ __device__ __forceinline__ void mainloop_fast(const Problem& p, int64_t m0, int6
     half(fa1, fb1, C0(), C0(), false, nn, kt + 2, FULL || kt + 1 < nk, nxt, 0, fa0, fb0);
     __builtin_amdgcn_sched_barrier(0);
   };
+  // Two stages.  FULL: steps kt+1 and kt+2 exist.
+  auto step2 = [&](int kt, auto FULL_, uint8_t* cur, uint8_t* nxt) {
+    constexpr bool FULL = decltype(FULL_)::value;
+    const bool dma2 = FULL || kt + 2 < nk;
+    if (GATHER && kt == next_gather) {
+      copy_gather<E, BM>(cur, p.gather_out, p.m, p.k, m0, (int64_t)kt * BK);
+      next_gather += gather_every;
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    // half 0 of step kt; reads of half 1 of step kt
+    half(fa0, fb0, C0(), C0(), false, cur, kt + 2, true, cur, 1, fa1, fb1);
+    // the DMA of step kt+1 (issued during step kt-1) has landed
+    wait_vmcnt<0>();
+    lds_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    // half 1 of step kt; the DMA of step kt+2 into this step's stage, which
+    // no wavefront reads any more; reads of half 0 of step kt+1
+    half(fa1, fb1, C0(), CD(), dma2, cur, kt + 2, FULL || kt + 1 < nk, nxt, 0, fa0, fb0);
+    if (dma2) advance_a();
+    __builtin_amdgcn_sched_barrier(0);
+  };
 
   if constexpr (ARR) {
     wait_step(0);
@@ -715,15 +746,25 @@ __device__ __forceinline__ void mainloop_fast(const Problem& p, int64_t m0, int6
   using Full = std::integral_constant<bool, true>;
   using Part = std::integral_constant<bool, false>;
   int kt = 0;
-  for (; kt + 4 < nk; kt += 3) {
-    step(kt, Full(), L0, L1, L2);
-    step(kt + 1, Full(), L1, L2, L0);
-    step(kt + 2, Full(), L2, L0, L1);
+  if constexpr (NS == 2) {
+    for (; kt + 3 < nk; kt += 2) {
+      step2(kt, Full(), L0, L1);
+      step2(kt + 1, Full(), L1, L0);
+    }
+    if (kt < nk) step2(kt, Part(), L0, L1);
+    if (kt + 1 < nk) step2(kt + 1, Part(), L1, L0);
+    if (kt + 2 < nk) step2(kt + 2, Part(), L0, L1);
+  } else {
+    for (; kt + 4 < nk; kt += 3) {
+      step(kt, Full(), L0, L1, L2);
+      step(kt + 1, Full(), L1, L2, L0);
+      step(kt + 2, Full(), L2, L0, L1);
+    }
+    if (kt < nk) step(kt, Part(), L0, L1, L2);
+    if (kt + 1 < nk) step(kt + 1, Part(), L1, L2, L0);
+    if (kt + 2 < nk) step(kt + 2, Part(), L2, L0, L1);
+    if (kt + 3 < nk) step(kt + 3, Part(), L0, L1, L2);
   }
-  if (kt < nk) step(kt, Part(), L0, L1, L2);
-  if (kt + 1 < nk) step(kt + 1, Part(), L1, L2, L0);
-  if (kt + 2 < nk) step(kt + 2, Part(), L2, L0, L1);
-  if (kt + 3 < nk) step(kt + 3, Part(), L0, L1, L2);
 }
 
 // Checked path (edge tiles, ragged K): bounds-tested register
@@ -792,7 +833,7 @@ constexpr int stage_bytes() { return (BM + BN) * kRowBytes; }
 // workgroup of column tile tn copies the steps kt with kt % tiles_n == tn).
 // ARR: arrival emulation (see mainloop_fast; the checked path waits for the
 // whole row chunk first).
-template <int E, int BM, int BN, bool AK, bool BKM, bool VEC, bool ARR, typename Ops>
+template <int E, int BM, int BN, bool AK, bool BKM, bool VEC, bool ARR, int NS, typename Ops>
 __device__ __forceinline__ void run_mainloop(const Problem& p, int64_t m0, int64_t n0, int tn, int tiles_n,
                                              uint8_t* L0, uint8_t* L1, uint8_t* L2,
                                              typename Ops::Acc (&acc)[BM / 32][BN / 32]) {
@@ -800,10 +841,17 @@ __device__ __forceinline__ void run_mainloop(const Problem& p, int64_t m0, int64
   const int gather_every = (AK && !ARR && p.gather_out != nullptr) ? tiles_n : 0;
   if constexpr (VEC) {
     if (p.k % BK == 0 && p.kseg % BK == 0) {  // whole steps, each inside one K segment
-      if constexpr (ARR) mainloop_fast<E, BM, BN, AK, BKM, false, true, Ops>(p, m0, n0, tn, 0, L0, L1, L2, acc);
-      else if (AK && gather_every > 0)
-        mainloop_fast<E, BM, BN, AK, BKM, AK, false, Ops>(p, m0, n0, tn, gather_every, L0, L1, L2, acc);
-      else mainloop_fast<E, BM, BN, AK, BKM, false, false, Ops>(p, m0, n0, tn, gather_every, L0, L1, L2, acc);
+      if constexpr (ARR) {
+        mainloop_fast<E, BM, BN, AK, BKM, false, true, NS, Ops>(p, m0, n0, tn, 0, L0, L1, L2, acc);
+      } else if constexpr (AK && NS == 3) {
+        if (gather_every > 0)
+          mainloop_fast<E, BM, BN, AK, BKM, true, false, NS, Ops>(p, m0, n0, tn, gather_every, L0, L1, L2, acc);
+        else mainloop_fast<E, BM, BN, AK, BKM, false, false, NS, Ops>(p, m0, n0, tn, gather_every, L0, L1, L2, acc);
+      } else {
+        // no gather copy with two stages (the host picks no two-stage tile
+        // when gather_out is set)
+        mainloop_fast<E, BM, BN, AK, BKM, false, false, NS, Ops>(p, m0, n0, tn, gather_every, L0, L1, L2, acc);
+      }
       return;
     }
   }
@@ -900,6 +948,11 @@ __device__ __forceinline__ void store_c16(uint16_t* h0, uint16_t* h1, uint16_t* 
   stage_c16<BM, BN>(h0, h1, cvt);
   store_c16_tile<BM, BN, VEC>(h0, h1, C, m, n, m0, n0);
 }
+
+// LDS stages of the main loop: three, or two for the 256 x 256 tile (whose
+// three stages would exceed the 160 KB of LDS).
+template <int BM, int BN>
+constexpr int lds_stages() { return BM * BN >= 256 * 256 ? 2 : 3; }
 
 // LDS bytes of one stage array: an operand stage, or half of the 16-bit C tile.
 template <int BM, int BN>

@@ -127,6 +127,48 @@ def test_backward_shapes(mc2, m, n_l, k, dtype):
     assert_close16(mc2_inputs.from_torch(dw), oracle.matmul_grad_weight(t["dy"], t["ag_x"], dtype), dtype, "dW")
 
 
+# Outputs of 4096 x 4096 and ragged 4059 x 4083, with a contraction that is a
+# whole number of K steps (fast path; 256 is the smallest allowed, 4 steps,
+# and 320 an odd number of steps) or not (300: checked path).  dW (A
+# M-contiguous) takes the two-stage 256 x 256 tile there; dX (A K-, B
+# N-contiguous) the 256 x 128 one.
+@pytest.mark.parametrize("m,n_l,k", [(4096, 256, 4096), (4059, 320, 4083), (4059, 300, 4083)])
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_big_tile_grad_input(mc2, m, n_l, k, dtype):
+    import torch
+    print(f"big-tile dX m={m} n_l={n_l} k={k} {dtype}", flush=True)
+    specs = mc2_inputs.configs.scaled("bwd", m=m, n_local=n_l, k=k)
+    specs = {s: mc2_inputs.TensorSpec(v.tid, v.shape, v.dist, v.a, v.b, dtype) for s, v in specs.items()
+             if s in ("dy", "w")}
+    t = mc2_inputs.make(specs, seed=m + n_l + k)
+    dx = mc2.mc2_matmul_grad_input(mc2_inputs.to_torch(t["dy"], dtype), mc2_inputs.to_torch(t["w"], dtype))
+    torch.cuda.synchronize()
+    assert_close16(mc2_inputs.from_torch(dx), oracle.matmul_grad_input(t["dy"], t["w"], dtype), dtype, "dX")
+
+
+@pytest.mark.parametrize("m,n_l,k", [(256, 4096, 4096), (264, 4059, 4083)])
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_big_tile_grad_weight(mc2, m, n_l, k, dtype):
+    import torch
+    print(f"big-tile dW m={m} n_l={n_l} k={k} {dtype}", flush=True)
+    specs = mc2_inputs.configs.scaled("bwd", m=m, n_local=n_l, k=k)
+    specs = {s: mc2_inputs.TensorSpec(v.tid, v.shape, v.dist, v.a, v.b, dtype) for s, v in specs.items()
+             if s in ("dy", "ag_x")}
+    t = mc2_inputs.make(specs, seed=m + n_l + k)
+    dw = mc2.mc2_matmul_grad_weight(mc2_inputs.to_torch(t["dy"], dtype), mc2_inputs.to_torch(t["ag_x"], dtype))
+    torch.cuda.synchronize()
+    assert_close16(mc2_inputs.from_torch(dw), oracle.matmul_grad_weight(t["dy"], t["ag_x"], dtype), dtype, "dW")
+
+
+@pytest.mark.parametrize("x2_trans", [False, True])
+def test_big_tile_allgather_without_gather_output(mc2, x2_trans):
+    """AllGatherMatmul of a 4096 x 4096 output with gather_output off: with x2 given
+    as (n, k) the 256 x 256 tile (with gather_out only the three-stage tiles are used)."""
+    out, g, want, _ = _ag(mc2, 8, 512, 256, 4096, "bf16", x2_trans=x2_trans, seed=21, gather=False)
+    assert g is None
+    assert_close16(out, want, "bf16", "out")
+
+
 def test_backward_full_config_sampled(mc2):
     """dY (8192, 1792), W (1792, 4096), AG(X) (8192, 4096): 32 sampled rows of dX and of dW."""
     import torch

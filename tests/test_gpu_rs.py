@@ -71,13 +71,15 @@ def _check_partial(part, ref_part, rank, r, dtype):
 
 
 # (r, m, k, n, x2_trans, dtype, rank): tile-aligned blocks, blocks that straddle
-# tiles (m / r = 37), ragged n, k off the 8-element vector path, n = 1, and a
-# GEMM large enough for the 128 x 256 tile
+# tiles (m / r = 37), ragged n, k off the 8-element vector path, n = 1, a
+# GEMM large enough for the 128 x 256 tile, and two with 4096 x 4096 partials
+# (the 256 x 256 tile)
 @pytest.mark.parametrize("r,m,k,n,x2_trans,dtype,rank", [
     (2, 256, 256, 128, False, "bf16", 1), (4, 512, 512, 256, True, "bf16", 2), (8, 1024, 320, 200, False, "f16", 5),
     (8, 296, 256, 72, True, "bf16", 7), (4, 100, 300, 33, False, "bf16", 0), (2, 64, 1000, 1, False, "f16", 0),
     (8, 1024, 512, 448, True, "f16", 3), (4, 1536, 768, 512, False, "bf16", 1),
-    (8, 4096, 256, 2048, True, "bf16", 6)])
+    (8, 4096, 256, 2048, True, "bf16", 6), (2, 4096, 256, 4096, True, "bf16", 1),
+    (2, 4096, 320, 4096, False, "f16", 0)])
 def test_rs_shapes(mc2, r, m, k, n, x2_trans, dtype, rank):
     print(f"rs r={r} m={m} k={k} n={n} trans={x2_trans} {dtype} rank={rank}", flush=True)
     xs, x2s = _system(r, m, k, n, x2_trans, dtype, seed=300 + r + m + k)
