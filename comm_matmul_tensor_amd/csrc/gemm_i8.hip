@@ -6,8 +6,9 @@
 //   out[i][j] = round16( (float(acc[i][j]) * s1[i]) * s2[j] + bias[j] )
 //
 // A = q (m, k) int8 row-major (K-contiguous, staged by direct-to-LDS loads),
-// B = x2 (k, n) int8 row-major (N-contiguous, transposed in registers to the
-// K-major LDS layout).  Tiling, LDS layout and XCD order are described in
+// B = x2 (k, n) int8 row-major (N-contiguous: staged as loaded and read with
+// ds_read_b64_tr_b8 on the fast path, transposed in registers to the K-major
+// LDS layout on the checked path).  Tiling, LDS layout and XCD order are described in
 // gemm_mfma.hpp.  Integer accumulation is exact, so
 // the result does not depend on the order of the K loop; |acc| stays below
 // 2^31 because rank_size * h <= 35000 and |q|, |x2| <= 128.
