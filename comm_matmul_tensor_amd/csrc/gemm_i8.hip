@@ -53,10 +53,11 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_i8_kernel(Problem p, GemmI8A
     for (int i = 0; i < FM; i++)
 #pragma unroll
       for (int j = 0; j < FN; j++) {
-        const int64_t col = n0 + wn * WN + 16 * j + lane % 16;
+        // accumulator layout: stage_c16
+        const int64_t row = m0 + wm * WM + 16 * i + lane % 16;
 #pragma unroll
         for (int r = 0; r < 4; r++) {
-          const int64_t row = m0 + wm * WM + 16 * i + 4 * (lane / 16) + r;
+          const int64_t col = n0 + wn * WN + 16 * j + 4 * (lane / 16) + r;
           if (row < p.m && col < p.n) g.acc_out[row * p.n + col] = acc[i][j][r];
         }
       }

@@ -13,29 +13,23 @@
 // Workgroup: 256 threads = 4 wavefronts in a 2 x 2 grid; each wavefront owns a
 // (BM/2) x (BN/2) block of C as 16 x 16 MFMA tiles.
 //
-// LDS layout.  Both operand tiles are stored K-major: one 128-byte row per
-// m (or n) index, rows packed densely, and the eight 16-byte chunks of row r
-// permuted by XOR with r % 8.  Every MFMA fragment is then one ds_read_b128
-// per lane (16 lanes read 16 rows at the same logical chunk), which on
-// gfx950 measured faster than any padded layout and about twice as fast per
-// byte as the ds_read_b64_tr transpose reads.
+// LDS layout.  A K-contiguous operand tile is stored K-major: one 128-byte
+// row per m (or n) index, rows packed densely, the eight 16-byte chunks of
+// row r permuted by XOR with r % 8; each MFMA fragment is one ds_read_b128
+// per lane (16 lanes read 16 rows at the same logical chunk).  An
+// MN-contiguous operand tile stays as it is in memory: one row of R
+// elements per k, its 16-byte chunks XOR-swizzled by k (mn_swz); each
+// fragment is two transpose reads (ds_read_b64_tr_b16 / _b8), so no
+// operand needs a transpose pass.
 //
-// Staging, for tiles wholly inside the matrices:
-//  - K-contiguous operand: direct-to-LDS loads (global_load_lds_dwordx4).
-//    Each wavefront instruction fills one 1 KB block = 8 rows; lane l lands
-//    in physical chunk l % 8 of row l / 8 of the block, so it fetches logical
-//    chunk (l % 8) ^ (l / 8) from global memory.  No registers, no ds_write.
-//  - MN-contiguous operand: each thread loads a square block (8 k x 8 n for
-//    2-byte elements, 16 x 16 for int8) as 16-byte rows along n, transposes it
-//    in registers with v_perm_b32, and writes 8 or 16 K-major chunks with
-//    ds_write_b128.  Odd blocks write their rows in the order i ^ 1 (a
-//    per-lane byte selector makes that free), so each write instruction
-//    touches both halves of the 64 banks.
-// Two LDS stages (separate arrays, so the compiler can tell the DMA target
-// from the buffer being read) and two register sets: the DMA for step k+1 and
-// the global loads for step k+2 are in flight while the MFMAs of step k run;
-// one barrier per step.  Tiles that cross a matrix edge use a checked path:
-// bounds-tested register loads (zero fill) into the same layout.
+// Staging.  Fast path (whole K steps, 16-byte aligned rows; tiles may cross
+// the M / N edges, their loads clamped): both operands go global -> LDS with
+// direct-to-LDS buffer loads (buffer_load_dwordx4 ... lds), no registers and
+// no ds_write, into a ring of three LDS stages (two for the 256 x 256 tile);
+// the schedule is described at mainloop_fast.  Checked path (ragged K or
+// unaligned rows): bounds-tested register loads with zero fill into the
+// K-major layout (MN-contiguous operands transposed in registers with
+// v_perm_b32), two stages, one barrier per step.
 //
 // Tile order: workgroup b is dispatched to XCD b % 8.  Tiles are renumbered so
 // each XCD owns a contiguous 1/8 of them, walking along rows of tiles (the
@@ -323,7 +317,7 @@ __device__ __forceinline__ void compute_step(const uint8_t* As, const uint8_t* B
 #pragma unroll
     for (int i = 0; i < FM; i++)
 #pragma unroll
-      for (int j = 0; j < FN; j++) acc[i][j] = Ops::mfma(fa[i], fb[j], acc[i][j]);
+      for (int j = 0; j < FN; j++) acc[i][j] = Ops::mfma(fb[j], fa[i], acc[i][j]);  // C layout: stage_c16
   }
 }
 
@@ -650,7 +644,7 @@ __device__ __forceinline__ void mainloop_fast(const Problem& p, int64_t m0, int6
     const int64_t offa = a_next, offb = (int64_t)kt_dma * db.step_bytes;
 #pragma unroll
     for (int q = 0; q < NM; q++) {
-      acc[q / FN][q % FN] = Ops::mfma(fa[q / FN], fb[q % FN], acc[q / FN][q % FN]);
+      acc[q / FN][q % FN] = Ops::mfma(fb[q % FN], fa[q / FN], acc[q / FN][q % FN]);
       if constexpr (NDH > 0) {
 #pragma unroll
         for (int d = 0; d < NDH; d++)
@@ -892,8 +886,12 @@ __device__ __forceinline__ void tile_of_block(int64_t m, int64_t n, int bm, int 
 
 // Writes a wavefront's rounded 16-bit C fragments to an LDS copy of the C tile
 // (rows [0, BM/2) in h0, rows [BM/2, BM) in h1) and waits for the whole
-// workgroup.  cvt(i, j, r, row, col) returns the 16-bit output of element r
-// of fragment (i, j) at tile coordinates (row, col).
+// workgroup.  The MFMAs take B's fragment as their first operand and A's as
+// the second, so they compute C^T: element r of accumulator (i, j) of lane l
+// is C at row 16 i + l % 16 and column 16 j + 4 (l / 16) + r of the
+// wavefront's block, and each lane writes its four consecutive columns with
+// one 8-byte LDS store.  cvt(i, j, r, row, col) returns the 16-bit output of
+// that element at tile coordinates (row, col).
 template <int BM, int BN, typename Cvt>
 __device__ __forceinline__ void stage_c16(uint16_t* h0, uint16_t* h1, Cvt cvt) {
   constexpr int WM = BM / 2, WN = BN / 2;
@@ -906,12 +904,12 @@ __device__ __forceinline__ void stage_c16(uint16_t* h0, uint16_t* h1, Cvt cvt) {
   for (int i = 0; i < FM; i++)
 #pragma unroll
     for (int j = 0; j < FN; j++) {
-      const int col = wn * WN + 16 * j + lane % 16;
-#pragma unroll
-      for (int r = 0; r < 4; r++) {
-        const int row = 16 * i + 4 * (lane / 16) + r;  // row inside the half
-        half[row * kPitch + col] = cvt(i, j, r, wm * WM + row, col);
-      }
+      const int row = 16 * i + lane % 16;  // row inside the half
+      const int col = wn * WN + 16 * j + 4 * (lane / 16);
+      const int trow = wm * WM + row;
+      const uint32_t w0 = (uint32_t)cvt(i, j, 0, trow, col) | ((uint32_t)cvt(i, j, 1, trow, col + 1) << 16);
+      const uint32_t w1 = (uint32_t)cvt(i, j, 2, trow, col + 2) | ((uint32_t)cvt(i, j, 3, trow, col + 3) << 16);
+      *reinterpret_cast<u32x2*>(half + row * kPitch + col) = u32x2{w0, w1};
     }
   __syncthreads();
 }
