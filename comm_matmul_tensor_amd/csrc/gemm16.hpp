@@ -216,8 +216,7 @@ hipError_t launch_cfg(Problem p, void* c, hipStream_t s) {
 // LDS stages) comes last and is used neither with the arrival wait nor with
 // the gather copy: the first kNumTiles3 entries (three stages) serve those.
 // It is left out with a K-contiguous A and an N-contiguous B: there the
-// transpose-read offsets of its eight B fragments push the 256-accumulator
-// kernel past its registers, and the 256 x 128 tile measured faster.
+// 256 x 128 tile measured faster (column-parallel dX: 129 against 137 us).
 const TileChoice kTilesBN[] = {{128, 224}, {224, 128}, {256, 128}, {128, 256}, {128, 128}};  // A K-, B N-major
 const TileChoice kTilesAM[] = {{128, 224}, {224, 128}, {128, 256}, {256, 128}, {128, 128}, {256, 256}};  // otherwise
 constexpr int kNumTiles3 = 5;
