@@ -73,7 +73,7 @@ def _check_partial(part, ref_part, rank, r, dtype):
 # (r, m, k, n, x2_trans, dtype, rank): tile-aligned blocks, blocks that straddle
 # tiles (m / r = 37), ragged n, k off the 8-element vector path, n = 1, a
 # GEMM large enough for the 128 x 256 tile, and two with 4096 x 4096 partials
-# (the 256 x 256 tile)
+# (x2 given as (n, k): the 256 x 256 tile; x2 as (k, n): 256 x 128)
 @pytest.mark.parametrize("r,m,k,n,x2_trans,dtype,rank", [
     (2, 256, 256, 128, False, "bf16", 1), (4, 512, 512, 256, True, "bf16", 2), (8, 1024, 320, 200, False, "f16", 5),
     (8, 296, 256, 72, True, "bf16", 7), (4, 100, 300, 33, False, "bf16", 0), (2, 64, 1000, 1, False, "f16", 0),
