@@ -62,15 +62,34 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_i8_kernel(Problem p, GemmI8A
         }
       }
   }
+  // The lane's rows and columns of C (accumulator layout: stage_c16): FM rows
+  // and FN x 4 columns, so each scale and bias value is loaded once per lane
+  // (inside the per-element epilogue the stores through acc_out kept the
+  // compiler from reusing the loads).
   const uint16_t* bias = static_cast<const uint16_t*>(g.bias);
+  float s1v[FM], s2v[FN][4], bv[FN][4];
+#pragma unroll
+  for (int i = 0; i < FM; i++) {
+    const int64_t row = m0 + wm * WM + 16 * i + lane % 16;
+    s1v[i] = row < p.m ? g.s1[row] : 0.0f;
+  }
+#pragma unroll
+  for (int j = 0; j < FN; j++)
+#pragma unroll
+    for (int r = 0; r < 4; r++) {
+      const int64_t col = n0 + wn * WN + 16 * j + 4 * (lane / 16) + r;
+      const bool in = col < p.n;
+      s2v[j][r] = in ? g.s2[col] : 0.0f;
+      bv[j][r] = (bias && in) ? (DT == DT_BF16 ? bf16_bits_to_f32(bias[col]) : f16_bits_to_f32(bias[col])) : 0.0f;
+    }
   store_c16<BM, BN, VEC>(reinterpret_cast<uint16_t*>(s0), reinterpret_cast<uint16_t*>(s1), static_cast<uint16_t*>(g.out),
                          p.m, p.n, m0, n0,
                          [&](int i, int j, int r, int row, int col) -> uint16_t {
                            const int64_t gr = m0 + row, gc = n0 + col;
                            if (gr >= p.m || gc >= p.n) return 0;
-                           float v = (float)acc[i][j][r] * g.s1[gr];
-                           v = v * g.s2[gc];
-                           if (bias) v = v + (DT == DT_BF16 ? bf16_bits_to_f32(bias[gc]) : f16_bits_to_f32(bias[gc]));
+                           float v = (float)acc[i][j][r] * s1v[i];
+                           v = v * s2v[j][r];
+                           if (bias) v = v + bv[j][r];
                            return DT == DT_BF16 ? f32_to_bf16_bits(v) : f32_to_f16_bits(v);
                          });
 }
