@@ -32,11 +32,27 @@ __device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
   __bf16 h = (__bf16)f;
   return __builtin_bit_cast(uint16_t, h);
 }
+// Two fp32 values -> two 16-bit values (lo in bits 0-15), round to nearest
+// even; bf16 converts both with one packed conversion.
+template <int DT>
+__device__ __forceinline__ uint32_t pack2_16(float lo, float hi);
+
 // fp32 -> fp16 bits, round to nearest even.
 __device__ __forceinline__ uint16_t f32_to_f16_bits(float f) {
   _Float16 h = (_Float16)f;
   return __builtin_bit_cast(uint16_t, h);
 }
+template <>
+__device__ __forceinline__ uint32_t pack2_16<DT_BF16>(float lo, float hi) {
+  typedef float f32x2 __attribute__((ext_vector_type(2)));
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{lo, hi}, bf16x2));
+}
+template <>
+__device__ __forceinline__ uint32_t pack2_16<DT_F16>(float lo, float hi) {
+  return (uint32_t)f32_to_f16_bits(lo) | ((uint32_t)f32_to_f16_bits(hi) << 16);
+}
+
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
 __device__ __forceinline__ float f16_bits_to_f32(uint32_t b) {
   return (float)__builtin_bit_cast(_Float16, (uint16_t)b);

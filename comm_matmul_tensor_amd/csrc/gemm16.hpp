@@ -173,7 +173,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm16_kernel(Problem p, void* c)
 
   uint16_t* h0 = reinterpret_cast<uint16_t*>(s0);
   uint16_t* h1 = reinterpret_cast<uint16_t*>(s1);
-  stage_c16<BM, BN>(h0, h1, [&](int i, int j, int r, int, int) { return Ops16<DT>::cvt(acc[i][j][r]); });
+  stage_c16<BM, BN, DT>(h0, h1, [&](int i, int j, int r, int, int) { return acc[i][j][r]; });
   if (p.rs_out) store_rs_tile<BM, BN, VEC>(h0, h1, static_cast<uint16_t*>(c), p, m0, n0);
   else store_c16_tile<BM, BN, VEC>(h0, h1, static_cast<uint16_t*>(c), p.m, p.n, m0, n0);
 }

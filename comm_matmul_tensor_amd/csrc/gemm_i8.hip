@@ -82,16 +82,16 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_i8_kernel(Problem p, GemmI8A
       s2v[j][r] = in ? g.s2[col] : 0.0f;
       bv[j][r] = (bias && in) ? (DT == DT_BF16 ? bf16_bits_to_f32(bias[col]) : f16_bits_to_f32(bias[col])) : 0.0f;
     }
-  store_c16<BM, BN, VEC>(reinterpret_cast<uint16_t*>(s0), reinterpret_cast<uint16_t*>(s1), static_cast<uint16_t*>(g.out),
-                         p.m, p.n, m0, n0,
-                         [&](int i, int j, int r, int row, int col) -> uint16_t {
-                           const int64_t gr = m0 + row, gc = n0 + col;
-                           if (gr >= p.m || gc >= p.n) return 0;
-                           float v = (float)acc[i][j][r] * s1v[i];
-                           v = v * s2v[j][r];
-                           if (bias) v = v + bv[j][r];
-                           return DT == DT_BF16 ? f32_to_bf16_bits(v) : f32_to_f16_bits(v);
-                         });
+  store_c16<BM, BN, VEC, DT>(reinterpret_cast<uint16_t*>(s0), reinterpret_cast<uint16_t*>(s1),
+                             static_cast<uint16_t*>(g.out), p.m, p.n, m0, n0,
+                             [&](int i, int j, int r, int row, int col) -> float {
+                               const int64_t gr = m0 + row, gc = n0 + col;
+                               if (gr >= p.m || gc >= p.n) return 0.0f;
+                               float v = (float)acc[i][j][r] * s1v[i];
+                               v = v * s2v[j][r];
+                               if (bias) v = v + bv[j][r];
+                               return v;
+                             });
 }
 
 template <int BM, int BN, int DT>

@@ -890,10 +890,11 @@ __device__ __forceinline__ void tile_of_block(int64_t m, int64_t n, int bm, int 
 // the second, so they compute C^T: element r of accumulator (i, j) of lane l
 // is C at row 16 i + l % 16 and column 16 j + 4 (l / 16) + r of the
 // wavefront's block, and each lane writes its four consecutive columns with
-// one 8-byte LDS store.  cvt(i, j, r, row, col) returns the 16-bit output of
-// that element at tile coordinates (row, col).
-template <int BM, int BN, typename Cvt>
-__device__ __forceinline__ void stage_c16(uint16_t* h0, uint16_t* h1, Cvt cvt) {
+// one 8-byte LDS store.  val(i, j, r, row, col) returns the fp32 value of that
+// element at tile coordinates (row, col); DT is the 16-bit output format
+// (round to nearest even, two values per conversion).
+template <int BM, int BN, int DT, typename Val>
+__device__ __forceinline__ void stage_c16(uint16_t* h0, uint16_t* h1, Val val) {
   constexpr int WM = BM / 2, WN = BN / 2;
   constexpr int FM = WM / 16, FN = WN / 16;
   constexpr int kPitch = BN + 8;
@@ -907,8 +908,8 @@ __device__ __forceinline__ void stage_c16(uint16_t* h0, uint16_t* h1, Cvt cvt) {
       const int row = 16 * i + lane % 16;  // row inside the half
       const int col = wn * WN + 16 * j + 4 * (lane / 16);
       const int trow = wm * WM + row;
-      const uint32_t w0 = (uint32_t)cvt(i, j, 0, trow, col) | ((uint32_t)cvt(i, j, 1, trow, col + 1) << 16);
-      const uint32_t w1 = (uint32_t)cvt(i, j, 2, trow, col + 2) | ((uint32_t)cvt(i, j, 3, trow, col + 3) << 16);
+      const uint32_t w0 = pack2_16<DT>(val(i, j, 0, trow, col), val(i, j, 1, trow, col + 1));
+      const uint32_t w1 = pack2_16<DT>(val(i, j, 2, trow, col + 2), val(i, j, 3, trow, col + 3));
       *reinterpret_cast<u32x2*>(half + row * kPitch + col) = u32x2{w0, w1};
     }
   __syncthreads();
@@ -940,10 +941,10 @@ __device__ __forceinline__ void store_c16_tile(const uint16_t* h0, const uint16_
   }
 }
 
-template <int BM, int BN, bool VEC, typename Cvt>
+template <int BM, int BN, bool VEC, int DT, typename Val>
 __device__ __forceinline__ void store_c16(uint16_t* h0, uint16_t* h1, uint16_t* C, int64_t m, int64_t n, int64_t m0,
-                                          int64_t n0, Cvt cvt) {
-  stage_c16<BM, BN>(h0, h1, cvt);
+                                          int64_t n0, Val val) {
+  stage_c16<BM, BN, DT>(h0, h1, val);
   store_c16_tile<BM, BN, VEC>(h0, h1, C, m, n, m0, n0);
 }
 
