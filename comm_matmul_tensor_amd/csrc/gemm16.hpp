@@ -67,6 +67,19 @@ __device__ __forceinline__ void store_rs_tile(const uint16_t* h0, const uint16_t
                                               int64_t m0, int64_t n0) {
   constexpr int kRowChunks = BN / 8;
   const int64_t n = p.n;
+  if constexpr (VEC && unrolled_store<BM, BN>()) {  // tile inside C: unrolled (as store_c16_tile)
+    if (m0 + BM <= p.m && n0 + BN <= n) {
+#pragma unroll
+      for (int it = 0; it < BM * kRowChunks / kThreads; it++) {
+        const int c = threadIdx.x + it * kThreads, row = c / kRowChunks, col = (c % kRowChunks) * 8;
+        const int64_t grow = m0 + row, t = grow - p.rs_row0;
+        const u32x4 v = *reinterpret_cast<const u32x4*>(staged_chunk<BM, BN>(h0, h1, row, col));
+        if (t >= 0 && t < p.rs_rows) *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(p.rs_out) + t * n + n0 + col) = v;
+        else store_out16(C + grow * n + n0 + col, v);
+      }
+      return;
+    }
+  }
   for (int c = threadIdx.x; c < BM * kRowChunks; c += kThreads) {
     const int row = c / kRowChunks, col = (c % kRowChunks) * 8;
     const int64_t grow = m0 + row, gcol = n0 + col;
@@ -151,7 +164,8 @@ hipError_t launch_rs_reduce(const GemmArgs& g, hipStream_t s) {
 }
 
 // ARR: arrival emulation (A arrives in p.arrived piece by piece; gemm_mfma.hpp).
-template <int BM, int BN, bool AK, bool BKM, bool VEC, int DT, bool ARR>
+// GA: the call writes gather_out (the gather copy runs in the main loop).
+template <int BM, int BN, bool AK, bool BKM, bool VEC, int DT, bool ARR, bool GA = false>
 __global__ __launch_bounds__(kThreads, 1) void gemm16_kernel(Problem p, void* c) {
   constexpr int FM = BM / 32, FN = BN / 32;
   constexpr int NS = lds_stages<BM, BN>();
@@ -169,13 +183,13 @@ __global__ __launch_bounds__(kThreads, 1) void gemm16_kernel(Problem p, void* c)
 #pragma unroll
     for (int j = 0; j < FN; j++) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  run_mainloop<2, BM, BN, AK, BKM, VEC, ARR, NS, Ops16<DT>>(p, m0, n0, tn, tiles_n, s0, s1, s2, acc);
+  run_mainloop<2, BM, BN, AK, BKM, VEC, ARR, NS, Ops16<DT>, GA ? 1 : 0>(p, m0, n0, tn, tiles_n, s0, s1, s2, acc);
 
   uint16_t* h0 = reinterpret_cast<uint16_t*>(s0);
   uint16_t* h1 = reinterpret_cast<uint16_t*>(s1);
   stage_c16<BM, BN, DT>(h0, h1, [&](int i, int j, int r, int, int) { return acc[i][j][r]; });
   if (p.rs_out) store_rs_tile<BM, BN, VEC>(h0, h1, static_cast<uint16_t*>(c), p, m0, n0);
-  else store_c16_tile<BM, BN, VEC>(h0, h1, static_cast<uint16_t*>(c), p.m, p.n, m0, n0);
+  else store_c16_tile<BM, BN, VEC>(h0, h1, static_cast<uint16_t*>(c), p.m, p.n, m0, n0, !GA);
 }
 
 template <int BM, int BN, bool AK, bool BKM, int DT>
@@ -204,6 +218,13 @@ hipError_t launch_cfg(Problem p, void* c, hipStream_t s) {
   }
   // the two-stage loop has neither the arrival wait nor the gather copy
   if (lds_stages<BM, BN>() == 2 && (p.ready || p.gather_out)) return hipErrorInvalidValue;
+  if constexpr (AK && lds_stages<BM, BN>() == 3) {
+    if (p.gather_out) {
+      if (vec) gemm16_kernel<BM, BN, AK, BKM, true, DT, false, true><<<(unsigned)tiles, kThreads, 0, s>>>(p, c);
+      else gemm16_kernel<BM, BN, AK, BKM, false, DT, false, true><<<(unsigned)tiles, kThreads, 0, s>>>(p, c);
+      return hipGetLastError();
+    }
+  }
   if (vec) gemm16_kernel<BM, BN, AK, BKM, true, DT, false><<<(unsigned)tiles, kThreads, 0, s>>>(p, c);
   else gemm16_kernel<BM, BN, AK, BKM, false, DT, false><<<(unsigned)tiles, kThreads, 0, s>>>(p, c);
   return hipGetLastError();

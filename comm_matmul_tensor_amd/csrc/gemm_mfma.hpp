@@ -827,7 +827,9 @@ constexpr int stage_bytes() { return (BM + BN) * kRowBytes; }
 // workgroup of column tile tn copies the steps kt with kt % tiles_n == tn).
 // ARR: arrival emulation (see mainloop_fast; the checked path waits for the
 // whole row chunk first).
-template <int E, int BM, int BN, bool AK, bool BKM, bool VEC, bool ARR, int NS, typename Ops>
+// GMODE: 0 = no gather copy, 1 = gather copy (p.gather_out set), 2 = decided
+// from p.gather_out at run time (the first two compile one fast loop only).
+template <int E, int BM, int BN, bool AK, bool BKM, bool VEC, bool ARR, int NS, typename Ops, int GMODE = 2>
 __device__ __forceinline__ void run_mainloop(const Problem& p, int64_t m0, int64_t n0, int tn, int tiles_n,
                                              uint8_t* L0, uint8_t* L1, uint8_t* L2,
                                              typename Ops::Acc (&acc)[BM / 32][BN / 32]) {
@@ -837,7 +839,9 @@ __device__ __forceinline__ void run_mainloop(const Problem& p, int64_t m0, int64
     if (p.k % BK == 0 && p.kseg % BK == 0) {  // whole steps, each inside one K segment
       if constexpr (ARR) {
         mainloop_fast<E, BM, BN, AK, BKM, false, true, NS, Ops>(p, m0, n0, tn, 0, L0, L1, L2, acc);
-      } else if constexpr (AK && NS == 3) {
+      } else if constexpr (AK && NS == 3 && GMODE == 1) {
+        mainloop_fast<E, BM, BN, AK, BKM, true, false, NS, Ops>(p, m0, n0, tn, gather_every, L0, L1, L2, acc);
+      } else if constexpr (AK && NS == 3 && GMODE == 2) {
         if (gather_every > 0)
           mainloop_fast<E, BM, BN, AK, BKM, true, false, NS, Ops>(p, m0, n0, tn, gather_every, L0, L1, L2, acc);
         else mainloop_fast<E, BM, BN, AK, BKM, false, false, NS, Ops>(p, m0, n0, tn, gather_every, L0, L1, L2, acc);
@@ -922,11 +926,28 @@ __device__ __forceinline__ const uint16_t* staged_chunk(const uint16_t* h0, cons
   return (row < WM ? h0 + row * kPitch : h1 + (row - WM) * kPitch) + col;
 }
 
-// Stores the staged tile with 16-byte row-contiguous stores.
+// Stores the staged tile with 16-byte row-contiguous stores.  With
+// unrolled set, a tile wholly inside C takes an unrolled loop without bounds
+// tests, so its LDS reads are issued together instead of one wait per chunk
+// (used for tiles of at most 16 chunks per thread, and not after the gather
+// copy, where it measured slower); other tiles take the checked loop.
+template <int BM, int BN>
+constexpr bool unrolled_store() { return BM * (BN / 8) % kThreads == 0 && BM * (BN / 8) / kThreads <= 16; }
+
 template <int BM, int BN, bool VEC>
 __device__ __forceinline__ void store_c16_tile(const uint16_t* h0, const uint16_t* h1, uint16_t* C, int64_t m,
-                                               int64_t n, int64_t m0, int64_t n0) {
+                                               int64_t n, int64_t m0, int64_t n0, bool unrolled = true) {
   constexpr int kRowChunks = BN / 8;
+  if constexpr (VEC && unrolled_store<BM, BN>()) {
+    if (unrolled && m0 + BM <= m && n0 + BN <= n) {
+#pragma unroll
+      for (int it = 0; it < BM * kRowChunks / kThreads; it++) {
+        const int c = threadIdx.x + it * kThreads, row = c / kRowChunks, col = (c % kRowChunks) * 8;
+        store_out16(C + (m0 + row) * n + n0 + col, *reinterpret_cast<const u32x4*>(staged_chunk<BM, BN>(h0, h1, row, col)));
+      }
+      return;
+    }
+  }
   for (int c = threadIdx.x; c < BM * kRowChunks; c += kThreads) {
     const int row = c / kRowChunks, col = (c % kRowChunks) * 8;
     const int64_t grow = m0 + row, gcol = n0 + col;
