@@ -69,7 +69,7 @@ __device__ __forceinline__ void store_rs_tile(const uint16_t* h0, const uint16_t
   const int64_t n = p.n;
   if constexpr (VEC && unrolled_store<BM, BN>()) {  // tile inside C: unrolled (as store_c16_tile)
     if (m0 + BM <= p.m && n0 + BN <= n) {
-#pragma unroll
+#pragma unroll 16
       for (int it = 0; it < BM * kRowChunks / kThreads; it++) {
         const int c = threadIdx.x + it * kThreads, row = c / kRowChunks, col = (c % kRowChunks) * 8;
         const int64_t grow = m0 + row, t = grow - p.rs_row0;

@@ -929,10 +929,10 @@ __device__ __forceinline__ const uint16_t* staged_chunk(const uint16_t* h0, cons
 // Stores the staged tile with 16-byte row-contiguous stores.  With
 // unrolled set, a tile wholly inside C takes an unrolled loop without bounds
 // tests, so its LDS reads are issued together instead of one wait per chunk
-// (used for tiles of at most 16 chunks per thread, and not after the gather
+// (16 chunks at a time: the 256 x 256 tile has 32; not after the gather
 // copy, where it measured slower); other tiles take the checked loop.
 template <int BM, int BN>
-constexpr bool unrolled_store() { return BM * (BN / 8) % kThreads == 0 && BM * (BN / 8) / kThreads <= 16; }
+constexpr bool unrolled_store() { return BM * (BN / 8) % kThreads == 0 && BM * (BN / 8) / kThreads <= 32; }
 
 template <int BM, int BN, bool VEC>
 __device__ __forceinline__ void store_c16_tile(const uint16_t* h0, const uint16_t* h1, uint16_t* C, int64_t m,
@@ -940,7 +940,7 @@ __device__ __forceinline__ void store_c16_tile(const uint16_t* h0, const uint16_
   constexpr int kRowChunks = BN / 8;
   if constexpr (VEC && unrolled_store<BM, BN>()) {
     if (unrolled && m0 + BM <= m && n0 + BN <= n) {
-#pragma unroll
+#pragma unroll 16
       for (int it = 0; it < BM * kRowChunks / kThreads; it++) {
         const int c = threadIdx.x + it * kThreads, row = c / kRowChunks, col = (c % kRowChunks) * 8;
         store_out16(C + (m0 + row) * n + n0 + col, *reinterpret_cast<const u32x4*>(staged_chunk<BM, BN>(h0, h1, row, col)));
