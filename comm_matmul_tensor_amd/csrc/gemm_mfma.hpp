@@ -424,7 +424,9 @@ struct DmaOperand {
       // the instruction's 8 rows (32 i + 8 w ...) lie in one row block
       int64_t g0 = mn0 + 32 * i + 8 * w;
       g0 = g0 < mn_ext ? g0 : mn_ext - 1;
-      const int64_t part = g0 / rows_per_part;
+      // row block of those rows: none to find for a single block; otherwise a
+      // 32-bit division (m is below 2^31)
+      const int64_t part = rows_per_part >= mn_ext ? 0 : (int64_t)((uint32_t)g0 / (uint32_t)rows_per_part);
       rsrc[i] = make_rsrc(parts[part], part_bytes);
       voff[i] = (uint32_t)((r - part * rows_per_part) * ld_bytes + c * 16);
     }
