@@ -24,8 +24,10 @@
  *        with sum, parameter table (scale shapes (bs, H/128) fp32 or
  *        (bs, H/64, 2) E8M0) and constraints (group size 128; mx).
  *
- * Precision: the float GEMMs and the dequantisation are evaluated in fp64 and
- * rounded once to the output type (the definition, up to summation order).
+ * Precision: the float GEMMs are evaluated in fp64 (products exact, the sum
+ * over k ascending) and rounded once to the output type (the definition, up
+ * to summation order).  The dequantisation acc x s1 x s2 + bias is formed
+ * exactly and rounded once.
  * The per-token quantisation takes its integer decisions in fp32, the
  * precision of the GPU kernel, because the pages fix none.  The int8 GEMM is
  * exact (int64, checked to fit int32).  QuantAllReduce sums fp64 products in
@@ -312,18 +314,112 @@ int64_t orc_int8_matmul(const int8_t* q, const int8_t* x2, int64_t m, int64_t n,
 }
 
 /*
- * output = output_quant x x1_scale x x2_scale + bias, per token x per channel,
- * evaluated in fp64 and rounded once to out_dtype (bf16 or fp16).
- * bias may be NULL (zero).
+ * Exact rounding of a value given as an integer significand and a power of
+ * two: (-1)^neg (N + t) 2^E with N > 0 and 0 <= t < 1, where t is known only
+ * as zero (sticky = 0) or strictly between 0 and 1 (sticky = 1).  Rounds to
+ * the binary format with p significand bits, smallest normal exponent emin
+ * and largest exponent emax, ties to even, overflow to infinity, and returns
+ * the result as a double (exact: at most 11 significant bits).
  */
+static double round_exact(int neg, unsigned __int128 N, int E, int sticky, int p, int emin, int emax) {
+  int nb = 0;
+  for (unsigned __int128 t = N; t; t >>= 1) nb++;
+  const int lead = nb - 1 + E;                           /* exponent of N's leading bit */
+  const int ulp = (lead < emin ? emin : lead) - (p - 1); /* exponent of the format's last place */
+  const int drop = ulp - E;                              /* low bits of N below that place */
+  unsigned __int128 q;
+  if (drop <= 0) {
+    q = N << -drop; /* N fits in p bits at this scale; t < 1 ulp of N is below half a place */
+  } else if (drop > nb) {
+    q = 0; /* below half of the last place */
+  } else {
+    q = drop == 128 ? 0 : N >> drop;
+    const unsigned __int128 rem = N - (q << drop), half = (unsigned __int128)1 << (drop - 1);
+    if (rem > half || (rem == half && (sticky || (q & 1)))) q += 1;
+  }
+  double v = ldexp((double)q, ulp);
+  if (v > ldexp(2.0 - ldexp(1.0, 1 - p), emax)) v = INFINITY;
+  return neg ? -v : v;
+}
+
+/* x = M 2^E with M an odd integer (or 0) of at most 24 bits (any binary32 value). */
+static void split_odd(double x, int64_t* M, int* E) {
+  int e;
+  double f = frexp(x, &e); /* x = f 2^e, |f| in [0.5, 1) */
+  int64_t m = (int64_t)ldexp(f, 24);
+  e -= 24;
+  while (m != 0 && (m & 1) == 0) {
+    m /= 2;
+    e++;
+  }
+  *M = m;
+  *E = e;
+}
+
+static int bitlen128(unsigned __int128 v) {
+  int n = 0;
+  for (; v; v >>= 1) n++;
+  return n;
+}
+
+/*
+ * output = output_quant x x1_scale x x2_scale + bias, per token x per channel,
+ * rounded once from its exact value to out_dtype (bf16 or fp16): acc x s1 x s2
+ * is an integer of at most 31 + 24 + 24 bits times a power of two, formed
+ * exactly in 128-bit integers, and the bias (a 16-bit float) is added
+ * exactly as well.  When the sum would not fit 128 bits, the two terms lie
+ * so far apart that the smaller one is below the last of 16 zero bits
+ * appended to the larger one: it then only decides the direction of
+ * rounding and enters as a sticky bit.  bias may be NULL (zero).
+ * Non-finite scales or bias fall back to fp64 arithmetic (NaN and infinity
+ * propagate).
+ */
+static double dequant_exact(int32_t acc, float s1, float s2, double bias, int dtype) {
+  const int p = dtype == O_BF16 ? 8 : 11, emin = dtype == O_BF16 ? -126 : -14, emax = dtype == O_BF16 ? 127 : 15;
+  if (!isfinite(s1) || !isfinite(s2) || !isfinite(bias)) return (double)acc * s1 * s2 + bias;
+  int64_t M1, M2, Mb;
+  int E1, E2, Eb;
+  split_odd(s1, &M1, &E1);
+  split_odd(s2, &M2, &E2);
+  split_odd(bias, &Mb, &Eb);
+  const __int128 P = (__int128)acc * M1 * M2; /* |P| < 2^79 */
+  const int EP = E1 + E2;
+  if (P == 0 && Mb == 0) return (double)acc * s1 * s2 + bias; /* zeros: exact, IEEE signs */
+  if (P == 0) return round_exact(Mb < 0, (unsigned __int128)(Mb < 0 ? -Mb : Mb), Eb, 0, p, emin, emax);
+  if (Mb == 0) return round_exact(P < 0, (unsigned __int128)(P < 0 ? -P : P), EP, 0, p, emin, emax);
+  /* both non-zero: hi is the term with the larger exponent, lo the other */
+  __int128 hi = P, lo = Mb;
+  int ehi = EP, elo = Eb;
+  if (Eb > EP) {
+    hi = Mb;
+    lo = P;
+    ehi = Eb;
+    elo = EP;
+  }
+  const int d = ehi - elo;
+  const int bh = bitlen128((unsigned __int128)(hi < 0 ? -hi : hi));
+  if (bh + d <= 125) { /* hi 2^d + lo fits: exact */
+    const __int128 S = hi * ((__int128)1 << d) + lo;
+    if (S == 0) return 0.0;
+    return round_exact(S < 0, (unsigned __int128)(S < 0 ? -S : S), elo, 0, p, emin, emax);
+  }
+  /* Here d > 125 - bh.  If hi is the product (bh <= 79), lo is the bias (at most 11
+     bits) and d > 46; if hi is the bias (bh <= 11), lo is the product (at most 79
+     bits) and d > 114.  Either way |lo| < 2^(d - 16): below one unit of |hi| 2^16 at
+     exponent ehi - 16, so the value is |hi| 2^16 plus (same sign) or minus (opposite
+     sign) a fraction of that unit. */
+  const unsigned __int128 H = (unsigned __int128)(hi < 0 ? -hi : hi) << 16;
+  const int same = (hi < 0) == (lo < 0);
+  return round_exact(hi < 0, same ? H : H - 1, ehi - 16, 1, p, emin, emax);
+}
+
 void orc_dequant(const int32_t* acc, const float* s1, const float* s2, const uint16_t* bias,
                  int64_t m, int64_t n, int out_dtype, uint16_t* out) {
 #pragma omp parallel for schedule(static)
   for (int64_t i = 0; i < m; i++)
     for (int64_t j = 0; j < n; j++) {
-      double v = (double)acc[i * n + j] * (double)s1[i] * (double)s2[j];
-      if (bias) v += dec16(out_dtype, bias[j]);
-      out[i * n + j] = enc16(out_dtype, v);
+      const double b = bias ? dec16(out_dtype, bias[j]) : 0.0;
+      out[i * n + j] = enc16(out_dtype, dequant_exact(acc[i * n + j], s1[i], s2[j], b, out_dtype));
     }
 }
 

@@ -329,6 +329,76 @@ def test_dequant_unit_and_power_of_two_scales():
     assert np.array_equal(oracle.dequant(acc, s1, s2, None), want)
 
 
+def _exact_dequant_codes(acc, s1, s2, bias_bits, fmt):
+    """round(acc x s1 x s2 + bias) from exact rationals, element by element."""
+    b = decode16(bias_bits, fmt) if bias_bits is not None else np.zeros(acc.shape[1])
+    return np.array([[round_rne(Fraction(int(acc[i, j])) * Fraction(float(s1[i])) * Fraction(float(s2[j]))
+                                + Fraction(float(b[j])), fmt) for j in range(acc.shape[1])]
+                     for i in range(acc.shape[0])], dtype=np.uint16)
+
+
+@pytest.mark.parametrize("fmt", ["bf16", "f16"])
+def test_dequant_exact_rational_non_power_of_two_scales(fmt):
+    """acc x s1 x s2 + bias with scales that are not powers of two (up to 79 significant
+    bits in the product) equals the exact rational value rounded once, for int32
+    accumulators across their whole range and biases of both signs."""
+    rng = np.random.default_rng(19)
+    m, n = 12, 16
+    acc = np.concatenate([rng.integers(-2 ** 31, 2 ** 31, (m // 2, n)),
+                          rng.integers(-3000, 3000, (m // 2, n))]).astype(np.int32)
+    acc[0, :4] = [2 ** 31 - 1, -2 ** 31, 0, 1]
+    s1 = rng.uniform(1e-3, 1e-2, m).astype(np.float32)
+    s2 = rng.uniform(1e-3, 1e-2, n).astype(np.float32)
+    if fmt == "f16":  # keep the products inside fp16's range
+        s1 = (s1 * np.float32(2.0 ** -12)).astype(np.float32)
+    bias = enc(rng.normal(0.0, 1.0, n) * (100.0 if fmt == "bf16" else 1.0), fmt)
+    got = oracle.dequant(acc, s1, s2, bias, fmt)
+    want = _exact_dequant_codes(acc, s1, s2, bias, fmt)
+    assert np.array_equal(bits(got), want)
+    got0 = oracle.dequant(acc, s1, s2, None, fmt)
+    assert np.array_equal(bits(got0), _exact_dequant_codes(acc, s1, s2, None, fmt))
+
+
+@pytest.mark.parametrize("fmt", ["bf16", "f16"])
+def test_dequant_far_apart_terms(fmt):
+    """Product and bias many binades apart (the smaller term only decides the rounding
+    direction), both signs, against exact rationals."""
+    rng = np.random.default_rng(23)
+    n = 16
+    acc = rng.integers(-2 ** 31, 2 ** 31, (4, n)).astype(np.int32)
+    lo, hi = (1e-38, 1.0) if fmt == "bf16" else (1e-20, 2.0 ** -22)
+    s1 = np.array([lo, lo, hi, hi], np.float32)               # rows 0-1: tiny products
+    s2 = rng.uniform(0.3, 0.9, n).astype(np.float32)
+    if fmt == "f16":
+        s2 = (s2 * np.float32(2.0 ** -8)).astype(np.float32)
+    big, small = (3.0e4, 1e-30) if fmt == "bf16" else (1000.0, 2.0 ** -20)
+    signs = np.where(rng.integers(0, 2, n) == 1, 1.0, -1.0)
+    for b in (big * signs, small * signs):
+        bias = enc(b, fmt)
+        got = oracle.dequant(acc, s1, s2, bias, fmt)
+        assert np.array_equal(bits(got), _exact_dequant_codes(acc, s1, s2, bias, fmt))
+
+
+def test_dequant_rounds_once_across_a_tie():
+    """A product that needs 55 significant bits: acc x s1 x s2 = (2^54 + 1) 2^-80, with
+    2^54 + 1 = 1417 x 10325701 x 1231205 (5 13 37 109 246241 279073).  Adding the bias
+    2^-34 puts the exact value 2^-80 above the midpoint between the bf16 values 2^-26
+    and 2^-26 + 2^-33, so it rounds up; fp64 evaluation would first round the product
+    to 2^-26, land exactly on the midpoint and round to even (down)."""
+    acc = np.array([[1417]], np.int32)
+    s1 = np.array([10325701 * 2.0 ** -40], np.float32)
+    s2 = np.array([1231205 * 2.0 ** -40], np.float32)
+    assert float(s1[0]) == 10325701 * 2.0 ** -40 and float(s2[0]) == 1231205 * 2.0 ** -40
+    assert 1417 * 10325701 * 1231205 == 2 ** 54 + 1
+    bias = enc([2.0 ** -34], "bf16")
+    got = oracle.dequant(acc, s1, s2, bias, "bf16")
+    assert got[0, 0] == round_rne(Fraction(2 ** 54 + 1, 2 ** 80) + Fraction(1, 2 ** 34), "bf16")
+    assert decode16(got, "bf16")[0, 0] == 2.0 ** -26 + 2.0 ** -33
+    # the same with the opposite sign of the product lands below the midpoint of -2^-26
+    got = oracle.dequant(-acc, s1, s2, enc([-2.0 ** -34], "bf16"), "bf16")
+    assert decode16(got, "bf16")[0, 0] == -(2.0 ** -26 + 2.0 ** -33)
+
+
 def test_alltoall_chain_is_composition_of_steps():
     specs = mc2_inputs.configs.scaled("a16w8", r=4, bs=32, h=64, n=24)
     t = mc2_inputs.make(specs, seed=16)
