@@ -1,12 +1,14 @@
 // libmc2 C ABI: host-side validation, device checks and kernel dispatch.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cstring>
 #include <mutex>
 #include <string>
 
 #include "kernels.hpp"
 #include "mc2.h"
+#include "testing.h"
 #include "validate.hpp"
 
 namespace mc2 {
@@ -28,6 +30,11 @@ struct DeviceState {
 };
 DeviceState g_dev[kMaxDevices];
 std::mutex g_dev_mutex;
+
+// Arrival test hook (testing.h): the GEMM's wait limit and how many leading
+// slabs of K the copy raises flags for (negative: all).
+std::atomic<uint64_t> g_arrival_wait_ticks{kArrivalWaitTicks};
+std::atomic<int> g_arrival_raised_slabs{-1};
 
 mc2_status hip_fail(hipError_t e, const char* where) {
   return fail(MC2_ERR_HIP, std::string(where) + ": " + hipGetErrorString(e));
@@ -70,7 +77,9 @@ constexpr size_t kFlagBytes = (kArrivalFlags + 1) * sizeof(unsigned);
 // Creates the arrival-emulation resources of device `dev` once.  The flags
 // sit in uncached device memory so that the GEMM's polls read memory, not a
 // stale cache line; that memory is kept until the process ends.
-mc2_status arrival_setup(int dev, DeviceState** out) {
+// *epoch receives this call's flag value (never 0, the flags' initial value),
+// taken under the lock so concurrent callers get distinct values.
+mc2_status arrival_setup(int dev, DeviceState** out, unsigned* epoch = nullptr) {
   std::lock_guard<std::mutex> lock(g_dev_mutex);
   DeviceState& st = g_dev[dev];
   if (!st.arrival_ready) {
@@ -83,6 +92,10 @@ mc2_status arrival_setup(int dev, DeviceState** out) {
     if (e == hipSuccess) e = hipDeviceSynchronize();
     if (e != hipSuccess) return hip_fail(e, "arrival emulation set-up");
     st.arrival_ready = true;
+  }
+  if (epoch) {
+    if (++st.epoch == 0) ++st.epoch;
+    *epoch = st.epoch;
   }
   *out = &st;
   return MC2_OK;
@@ -285,9 +298,8 @@ mc2_status mc2_allgather_matmul(const void* const* shards, int world_size, int64
   // once its piece has arrived.  `stream` then joins the copy stream, so work
   // enqueued after this call sees the whole gather_out.
   DeviceState* ds = nullptr;
-  if ((s = arrival_setup(dev, &ds)) != MC2_OK) return s;
-  unsigned epoch = ++ds->epoch;
-  if (epoch == 0) epoch = ++ds->epoch;  // flags start at 0: never wait for 0
+  unsigned epoch = 0;
+  if ((s = arrival_setup(dev, &ds, &epoch)) != MC2_OK) return s;
   const int64_t m = a.m;
   int64_t slabs = (k + 63) / 64 < kArrivalSlabs ? (k + 63) / 64 : kArrivalSlabs;
   const int64_t slab_cols = ((k + slabs - 1) / slabs + 63) / 64 * 64;
@@ -305,6 +317,8 @@ mc2_status mc2_allgather_matmul(const void* const* shards, int world_size, int64
   c.rows_chunk = rows_chunk;
   c.slab_cols = slab_cols;
   c.slabs = (int)slabs;
+  const int raised = g_arrival_raised_slabs.load();
+  c.raised_slabs = raised < 0 || raised > slabs ? (int)slabs : raised;
   c.chunks = (int)chunks;
   c.r = world_size;
   c.first_chunk = (int)first_chunk;
@@ -323,6 +337,7 @@ mc2_status mc2_allgather_matmul(const void* const* shards, int world_size, int64
   a.slabs = (int)slabs;
   a.first_row_tile = (int)(first_chunk * rows_chunk / gemm16_tile_rows(m, n, a.b_kmajor));
   a.status_flag = ds->flags + kFallbackSlot;
+  a.wait_ticks = g_arrival_wait_ticks.load();
   e = launch_gemm16(a, st);
   if (e == hipSuccess) e = hipEventRecord(ds->join, ds->copy_stream);
   if (e == hipSuccess) e = hipStreamWaitEvent(st, ds->join, 0);
@@ -343,6 +358,13 @@ mc2_status mc2_allgather_arrival_fallbacks(int reset, unsigned* count) {
   if (e == hipSuccess && reset) e = hipMemset(ds->flags + kFallbackSlot, 0, sizeof(unsigned));
   if (e == hipSuccess && reset) e = hipDeviceSynchronize();
   if (e != hipSuccess) return hip_fail(e, "allgather_arrival_fallbacks");
+  return MC2_OK;
+}
+
+mc2_status mc2_testing_arrival(uint64_t wait_ticks, int raised_slabs) {
+  clear_error();
+  g_arrival_wait_ticks.store(wait_ticks ? wait_ticks : kArrivalWaitTicks);
+  g_arrival_raised_slabs.store(raised_slabs);
   return MC2_OK;
 }
 

@@ -17,6 +17,8 @@
 // are 16-byte buffer stores, whole 128-byte lines per eight lanes; 8-byte
 // device-scope atomic stores (the same policy) serve a gather_out of 2 GiB or
 // more and rows that are not whole 16-byte pieces.
+#include <type_traits>
+
 #include "device.hpp"
 #include "kernels.hpp"
 
@@ -43,45 +45,74 @@ __global__ __launch_bounds__(kCopyThreads) void arrive_kernel(ArrivalArgs a) {
   if ((a.k % 8 == 0) && (a.slab_cols % 8 == 0)) {
     // 16-byte pieces in row-major order; thread t takes pieces t, t + 256, ...
     // and steps its (row, piece) position without dividing.  kBatch loads per
-    // thread are issued before their stores.
+    // thread are issued before their stores.  A chunk inside one shard (the
+    // usual case) reads through that shard's pointer, loaded once for the
+    // workgroup; a chunk across a shard edge finds each row's shard per lane.
     const int per_row = (int)(cols / 8), n = (int)rows * per_row;
     const bool buf = m * a.k * 2 < ((int64_t)1 << 31);  // byte offsets fit the buffer's 32 bits
     const __amdgpu_buffer_rsrc_t rsrc =
         __builtin_amdgcn_make_buffer_rsrc(gout, 0, buf ? (int)(m * a.k * 2) : 0, 0x00020000);
     const int dq = kCopyThreads / per_row, dc = kCopyThreads % per_row;
-    int r = (int)threadIdx.x / per_row, c = (int)threadIdx.x % per_row;
-    for (int i0 = (int)threadIdx.x; i0 < n; i0 += kBatch * kCopyThreads) {
-      u32x4 v[kBatch];
-      int64_t dst[kBatch];
+    const uint16_t* one_src = static_cast<const uint16_t*>(a.shards[b0]);
+    const int64_t one_row0 = b0 * a.block_rows;
+    // Straight-line batches: a lane whose j-th piece lies past the end
+    // repeats its first piece (always valid: i0 < n), loading and storing the
+    // same bytes to the same place again, so neither loads nor stores sit
+    // behind per-lane branches (which made the compiler wait for every
+    // earlier store before each store).
+    auto copy = [&](auto ONE_, auto BUF_) {
+      constexpr bool ONE = decltype(ONE_)::value, BUF = decltype(BUF_)::value;
+      int r = (int)threadIdx.x / per_row, c = (int)threadIdx.x % per_row;
+      for (int i0 = (int)threadIdx.x; i0 < n; i0 += kBatch * kCopyThreads) {
+        u32x4 v[kBatch];
+        int64_t dst[kBatch];
+        int64_t R0 = 0, col0 = 0;
 #pragma unroll
-      for (int j = 0; j < kBatch; j++) {
-        dst[j] = -1;
-        if (i0 + j * kCopyThreads < n) {
-          const int64_t R = row0 + r;
-          const int64_t bb = one_shard ? b0 : (int64_t)((uint32_t)R / (uint32_t)a.block_rows);
-          const int64_t lr = R - bb * a.block_rows, col = c0 + (int64_t)c * 8;
-          v[j] = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(a.shards[bb]) + lr * a.k + col);
+        for (int j = 0; j < kBatch; j++) {
+          int64_t R = row0 + r, col = c0 + (int64_t)c * 8;
+          if (j == 0) {
+            R0 = R;
+            col0 = col;
+          } else if (i0 + j * kCopyThreads >= n) {
+            R = R0;
+            col = col0;
+          }
+          const uint16_t* src;
+          if constexpr (ONE) {
+            src = one_src + (R - one_row0) * a.k + col;
+          } else {
+            const int64_t bb = (int64_t)((uint32_t)R / (uint32_t)a.block_rows);
+            src = static_cast<const uint16_t*>(a.shards[bb]) + (R - bb * a.block_rows) * a.k + col;
+          }
+          v[j] = *reinterpret_cast<const u32x4*>(src);
           dst[j] = R * a.k + col;
+          r += dq;
+          c += dc;
+          if (c >= per_row) {
+            c -= per_row;
+            r += 1;
+          }
         }
-        r += dq;
-        c += dc;
-        if (c >= per_row) {
-          c -= per_row;
-          r += 1;
+#pragma unroll
+        for (int j = 0; j < kBatch; j++) {
+          if constexpr (BUF) {
+            __builtin_amdgcn_raw_buffer_store_b128(v[j], rsrc, (int)(dst[j] * 2), 0, kPolicyDevice);
+          } else {
+            uint64_t* d = reinterpret_cast<uint64_t*>(gout + dst[j]);
+            __hip_atomic_store(d, (uint64_t)v[j][0] | ((uint64_t)v[j][1] << 32), __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(d + 1, (uint64_t)v[j][2] | ((uint64_t)v[j][3] << 32), __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+          }
         }
       }
-#pragma unroll
-      for (int j = 0; j < kBatch; j++)
-        if (dst[j] >= 0 && buf) {
-          __builtin_amdgcn_raw_buffer_store_b128(v[j], rsrc, (int)(dst[j] * 2), 0, kPolicyDevice);
-        } else if (dst[j] >= 0) {
-          uint64_t* d = reinterpret_cast<uint64_t*>(gout + dst[j]);
-          __hip_atomic_store(d, (uint64_t)v[j][0] | ((uint64_t)v[j][1] << 32), __ATOMIC_RELAXED,
-                             __HIP_MEMORY_SCOPE_AGENT);
-          __hip_atomic_store(d + 1, (uint64_t)v[j][2] | ((uint64_t)v[j][3] << 32), __ATOMIC_RELAXED,
-                             __HIP_MEMORY_SCOPE_AGENT);
-        }
-    }
+    };
+    using T1 = std::integral_constant<bool, true>;
+    using F1 = std::integral_constant<bool, false>;
+    if (one_shard && buf) copy(T1(), T1());
+    else if (one_shard) copy(T1(), F1());
+    else if (buf) copy(F1(), T1());
+    else copy(F1(), F1());
   } else {  // 16-bit elements, any row length
     const int64_t n = rows * cols;
     for (int64_t i = threadIdx.x; i < n; i += kCopyThreads) {
@@ -91,10 +122,11 @@ __global__ __launch_bounds__(kCopyThreads) void arrive_kernel(ArrivalArgs a) {
                          __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   }
-  // every wavefront's stores are visible device-wide, then one thread raises the flag
+  // every wavefront's stores are visible device-wide, then one thread raises
+  // the flag (of the first raised_slabs slabs: a test hook withholds the rest)
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
   __syncthreads();
-  if (threadIdx.x == 0)
+  if (threadIdx.x == 0 && sl < a.raised_slabs)
     __hip_atomic_store(a.flags + (int64_t)g * a.slabs + sl, a.epoch, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_SYSTEM);
 }
 
@@ -105,7 +137,8 @@ hipError_t launch_arrival_copy(const ArrivalArgs& a, hipStream_t s) {
   if (a.r < 1 || a.r > kMaxRanks || a.block_rows < 1 || a.k < 1 || a.rows_chunk < 1 || a.slab_cols < 1 ||
       a.slabs < 1 || a.chunks < 1 || (int64_t)a.chunks * a.rows_chunk < m ||
       (int64_t)(a.chunks - 1) * a.rows_chunk >= m || (int64_t)a.slabs * a.slab_cols < a.k ||
-      (int64_t)(a.slabs - 1) * a.slab_cols >= a.k || a.first_chunk < 0 || a.first_chunk >= a.chunks)
+      (int64_t)(a.slabs - 1) * a.slab_cols >= a.k || a.first_chunk < 0 || a.first_chunk >= a.chunks ||
+      a.raised_slabs < 0 || a.raised_slabs > a.slabs)
     return hipErrorInvalidValue;
   arrive_kernel<<<(unsigned)((int64_t)a.chunks * a.slabs), kCopyThreads, 0, s>>>(a);
   return hipGetLastError();

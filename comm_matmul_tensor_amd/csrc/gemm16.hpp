@@ -283,6 +283,7 @@ hipError_t launch_dt(const GemmArgs& g, hipStream_t s) {
     p.ready = g.ready_flags;
     p.ready_value = g.ready_value;
     p.fallbacks = g.status_flag;
+    p.wait_ticks = g.wait_ticks;
     p.arrived = g.gather_out;
     p.rows_chunk = g.rows_chunk;
     p.slab_cols = g.slab_cols;

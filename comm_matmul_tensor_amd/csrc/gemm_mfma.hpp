@@ -86,19 +86,18 @@ struct Problem {
   // ready[g * slabs + s] == ready_value.  rows_chunk is a multiple of the
   // tile height, so a tile waits on one flag per slab.  A workgroup whose
   // wait times out reads the rest of its rows from a_parts (the shards)
-  // instead and counts itself in *fallbacks.
+  // instead and counts itself in *fallbacks.  wait_ticks: the longest wait
+  // for one piece, in ticks of the 100 MHz real-time counter.
   const unsigned* ready;
   unsigned ready_value;
   unsigned* fallbacks;
+  uint64_t wait_ticks;
   const void* arrived;
   int64_t rows_chunk;
   int64_t slab_cols;
   int slabs;
   int first_row_tile;     // tile row handed out first (also without arrival; 0 by default)
 };
-
-// Longest wait for one row block, in ticks of the 100 MHz real-time counter.
-constexpr uint64_t kArrivalTimeoutTicks = 20000000ull;  // 200 ms
 
 // Row pointer of K-contiguous operand row `row` (row blocks of rows_per_part
 // rows live in separate buffers; resolved once per thread, outside the K loop).
@@ -114,15 +113,15 @@ __device__ __forceinline__ const uint8_t* kmajor_row(const void* const* parts, i
 }
 
 // Waits until *flag == value (raised by the copy kernel once its piece of A
-// is visible device-wide) or the time limit passes; returns whether the
-// piece arrived.  The flag lives in uncached memory, so every poll reads
+// is visible device-wide) or `ticks` of the 100 MHz real-time counter pass;
+// returns whether the piece arrived.  The flag lives in uncached memory, so every poll reads
 // memory.  Every wavefront polls for itself (the 64 lanes' loads of one
 // address are one request).
-__device__ __forceinline__ bool wait_flag(const unsigned* flag, unsigned value) {
+__device__ __forceinline__ bool wait_flag(const unsigned* flag, unsigned value, uint64_t ticks) {
   const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
   for (;;) {
     if (__hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM) == value) return true;
-    if (__builtin_amdgcn_s_memrealtime() - t0 > kArrivalTimeoutTicks) return false;
+    if (__builtin_amdgcn_s_memrealtime() - t0 > ticks) return false;
     __builtin_amdgcn_s_sleep(4);
   }
 }
@@ -135,7 +134,7 @@ __device__ __forceinline__ Problem arrival_problem(const Problem& p, int64_t m0)
   if (threadIdx.x == 0) {
     const unsigned* f = p.ready + (m0 / p.rows_chunk) * p.slabs;
     bool ok = true;
-    for (int sl = 0; ok && sl < p.slabs; sl++) ok = wait_flag(f + sl, p.ready_value);
+    for (int sl = 0; ok && sl < p.slabs; sl++) ok = wait_flag(f + sl, p.ready_value, p.wait_ticks);
     if (!ok) __hip_atomic_fetch_add(p.fallbacks, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     s_ok = ok;
   }
@@ -603,7 +602,7 @@ __device__ __forceinline__ void mainloop_fast(const Problem& p, int64_t m0, int6
   // Blocking wait for the slab of step kt; after a time-out A comes from the shards.
   auto wait_step = [&](int kt) {
     if (fell_back) return;
-    if (!wait_flag(flags + kt / sps, p.ready_value)) {
+    if (!wait_flag(flags + kt / sps, p.ready_value, p.wait_ticks)) {
       fell_back = true;
       da = da_shards;
       if (threadIdx.x % 64 == 0) __hip_atomic_fetch_add(p.fallbacks, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);

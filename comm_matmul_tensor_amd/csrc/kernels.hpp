@@ -43,9 +43,11 @@ struct GemmArgs {
   // ready_flags[g * slabs + s] == ready_value.  rows_chunk must be a
   // multiple of gemm16_tile_rows(m, n, b_kmajor) and slab_cols of 64.  Tile row
   // first_row_tile is handed out first; *status_flag counts wavefronts
-  // whose wait timed out (they read A from a_parts instead).
+  // whose wait timed out after wait_ticks ticks of the 100 MHz real-time
+  // counter (they read A from a_parts instead).
   const unsigned* ready_flags;
   unsigned ready_value;
+  uint64_t wait_ticks;
   int64_t rows_chunk;
   int64_t slab_cols;
   int slabs;
@@ -67,9 +69,14 @@ hipError_t launch_gemm16_f16(const GemmArgs& a, hipStream_t s);
 // with A K-major and B K-major (b_kmajor = 1) or N-major.
 int gemm16_tile_rows(int64_t m, int64_t n, int b_kmajor);
 
+// Default longest wait of the arrival GEMM for one piece: 200 ms of the
+// 100 MHz real-time counter.
+constexpr uint64_t kArrivalWaitTicks = 20000000ull;
+
 // ---- arrival emulation: copy of the shards into gather_out piece by piece
 // (row chunk g, slab s of K), each piece followed by its ready flag
-// (flags[g * slabs + s] = epoch).  Row chunk g covers gathered rows
+// (flags[g * slabs + s] = epoch; only for slabs s < raised_slabs, which is
+// `slabs` except under the time-out test hook).  Row chunk g covers gathered rows
 // [g rows_chunk, (g+1) rows_chunk); one workgroup per piece, slab by slab,
 // row chunk first_chunk first within a slab.
 struct ArrivalArgs {
@@ -81,6 +88,7 @@ struct ArrivalArgs {
   int64_t rows_chunk;
   int64_t slab_cols;
   int slabs;
+  int raised_slabs;    // slabs whose flags are raised (the others' pieces are copied only)
   int chunks;          // row chunks in the gathered matrix
   int r, first_chunk;
   unsigned epoch;

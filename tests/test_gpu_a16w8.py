@@ -109,8 +109,8 @@ def test_a16w8_largest_rank_h(mc2, h):
 
 
 def test_a16w8_full_config(mc2):
-    """bf16 (8192, 4096) on 8 ranks -> (1024, 32768) @ int8 (32768, 7168): every permuted
-    value, code and scale; accumulators and outputs on sampled tokens."""
+    """bf16 (8192, 4096) on 8 ranks -> (1024, 32768) @ int8 (32768, 7168): every code and
+    scale, every int32 accumulator (bit for bit) and every output element."""
     import torch
     seed, d, specs = mc2_inputs.CONFIGS["a16w8"]
     t = mc2_inputs.make("a16w8")
@@ -126,14 +126,10 @@ def test_a16w8_full_config(mc2):
     out2 = mc2.mc2_alltoall_quant_matmul(T(t["x1"], "bf16"), r, T(t["x2"], "i8"), T(t["x2_scale"], "f32"),
                                          T(t["x1_smooth"], "bf16"), T(t["bias"], "bf16"))
     torch.cuda.synchronize()
-    p = oracle.permute(t["x1"], r)
-    q_ref, s1_ref = oracle.smooth_quant(p, t["x1_smooth"])
-    assert_bits_equal(mc2_inputs.from_torch(q), q_ref, "q")
-    assert_bits_equal(mc2_inputs.from_torch(s1), s1_ref, "s1")
+    ref = oracle.alltoall_quant_matmul(t["x1"], r, t["x2"], t["x2_scale"], t["x1_smooth"], t["bias"])
+    assert_bits_equal(mc2_inputs.from_torch(q), ref["q"], "q")
+    assert_bits_equal(mc2_inputs.from_torch(s1), ref["s1"], "s1")
+    assert_bits_equal(mc2_inputs.from_torch(acc), ref["acc"], "acc")
     o = mc2_inputs.from_torch(out)
     assert_bits_equal(o, mc2_inputs.from_torch(out2), "run-to-run")
-    toks = np.unique(np.concatenate([[0, rows - 1], np.random.default_rng(2).choice(rows, 6, replace=False)]))
-    acc_ref = oracle.int8_matmul(np.ascontiguousarray(q_ref[toks]), t["x2"])
-    assert_bits_equal(mc2_inputs.from_torch(acc)[toks], acc_ref, "acc")
-    out_ref = oracle.dequant(acc_ref, s1_ref[toks], t["x2_scale"], t["bias"])
-    assert_close16(o[toks], out_ref, "bf16", "out")
+    assert_close16(o, ref["out"], "bf16", "out")

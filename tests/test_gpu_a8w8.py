@@ -108,7 +108,7 @@ def test_a8w8_largest_rank_h(mc2, h):
 
 def test_a8w8_full_config(mc2):
     """int8 (8192, 4096) on 8 ranks -> (1024, 32768) @ int8 (32768, 7168): every permuted
-    byte; accumulators and outputs on sampled tokens; two runs bit-identical."""
+    byte, every int32 accumulator and every output element; two runs bit-identical."""
     import torch
     seed, d, specs = mc2_inputs.CONFIGS["a8w8"]
     t = mc2_inputs.make("a8w8")
@@ -122,12 +122,9 @@ def test_a8w8_full_config(mc2):
     out = mc2.mc2_alltoall_quant_matmul_static(*args, permuted_out=perm, acc_out=acc)
     out2 = mc2.mc2_alltoall_quant_matmul_static(*args)
     torch.cuda.synchronize()
-    p_ref = oracle.permute_i8(t["x1"], r)
-    assert_bits_equal(mc2_inputs.from_torch(perm), p_ref, "permuted")
+    ref = oracle.alltoall_quant_matmul_static(t["x1"], r, t["x1_scale"], t["x2"], t["x2_scale"], t["bias"])
+    assert_bits_equal(mc2_inputs.from_torch(perm), oracle.permute_i8(t["x1"], r), "permuted")
+    assert_bits_equal(mc2_inputs.from_torch(acc), ref["acc"], "acc")
     o = mc2_inputs.from_torch(out)
     assert_bits_equal(o, mc2_inputs.from_torch(out2), "run-to-run")
-    toks = np.unique(np.concatenate([[0, rows - 1], np.random.default_rng(3).choice(rows, 6, replace=False)]))
-    acc_ref = oracle.int8_matmul(np.ascontiguousarray(p_ref[toks]), t["x2"])
-    assert_bits_equal(mc2_inputs.from_torch(acc)[toks], acc_ref, "acc")
-    out_ref = oracle.dequant(acc_ref, t["x1_scale"][toks], t["x2_scale"], t["bias"])
-    assert_close16(o[toks], out_ref, "bf16", "out", REL, RMS_REL)
+    assert_close16(o, ref["out"], "bf16", "out", REL, RMS_REL)
