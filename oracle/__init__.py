@@ -55,6 +55,8 @@ def _load():
             "orc_allgather_matmul": (None, [P, INT, I64, I64, P, I64, INT, INT, P, P]),
             "orc_matmul_reduce_scatter": (None, [P, P, INT, INT, INT, I64, I64, I64, P, INT, P, P]),
             "orc_permute": (None, [P, INT, I64, I64, P]),
+            "orc_add_bias": (None, [P, P, I64, I64, INT]),
+            "orc_bias_grad": (None, [P, I64, I64, INT, P]),
             "orc_smooth_quant": (None, [P, I64, I64, P, INT, P, P]),
             "orc_int8_matmul": (I64, [P, P, I64, I64, I64, P]),
             "orc_dequant": (None, [P, P, P, P, I64, I64, INT, P]),
@@ -161,6 +163,25 @@ def matmul_grad_weight(dy: np.ndarray, ag_x: np.ndarray, dtype: str = "bf16") ->
 
 
 # ---------------------------------------------------------------- AlltoAllQuantMatmul
+def add_bias(y: np.ndarray, bias: np.ndarray, dtype: str) -> np.ndarray:
+    """round(y + bias) per row: the listing's `out = out + bias` after the fused op."""
+    out = np.array(y, dtype=_STORAGE[dtype], copy=True, order="C")
+    bias = np.ascontiguousarray(bias, dtype=_STORAGE[dtype])
+    m, n = out.shape
+    assert bias.shape == (n,)
+    _load().orc_add_bias(_ptr(out), _ptr(bias), m, n, DT[dtype])
+    return out
+
+
+def bias_grad(dy: np.ndarray, dtype: str) -> np.ndarray:
+    """grad_bias = dy.sum(dim=0), rounded once to the dtype."""
+    dy = np.ascontiguousarray(dy, dtype=_STORAGE[dtype])
+    m, n = dy.shape
+    out = np.empty((n,), dtype=_STORAGE[dtype])
+    _load().orc_bias_grad(_ptr(dy), m, n, DT[dtype], _ptr(out))
+    return out
+
+
 def matmul_reduce_scatter(x: np.ndarray, x2: np.ndarray, recv: Sequence[Optional[np.ndarray]], rank: int,
                           dtype: str, x2_trans: bool = False) -> Dict[str, np.ndarray]:
     """One rank's share of Y = ReduceScatter_m(x @ x2): "partial" = round(x @ x2) (m, n)

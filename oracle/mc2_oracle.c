@@ -238,6 +238,37 @@ void orc_matmul_reduce_scatter(const uint16_t* x, const uint16_t* x2, int x2_tra
 }
 
 /* ------------------------------------------------------------------------ */
+/* [MC2] The tensor-parallel linear layer's bias and its gradient.           */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * AllGatherMatmulFunction.forward and MatmulReduceScatterFunction.forward add
+ * the bias to the fused op's output (the fused op itself takes no non-zero
+ * bias): y[i][j] = round(y[i][j] + bias[j]), the sum of two 16-bit values
+ * formed in fp64 (exact) and rounded once, in place on y (m, n).
+ */
+void orc_add_bias(uint16_t* y, const uint16_t* bias, int64_t m, int64_t n, int dtype) {
+#pragma omp parallel for schedule(static)
+  for (int64_t i = 0; i < m; i++)
+    for (int64_t j = 0; j < n; j++) y[i * n + j] = enc16(dtype, dec16(dtype, y[i * n + j]) + dec16(dtype, bias[j]));
+}
+
+/*
+ * grad_bias = grad_out.sum(dim=0) (both backward functions of the listing):
+ * gb[j] = round(sum over i ascending of dy[i][j]), the sum in fp64 (exact as
+ * long as a column's values span fewer than 53 - 8 - log2(m) binades) and
+ * rounded once to the dtype.
+ */
+void orc_bias_grad(const uint16_t* dy, int64_t m, int64_t n, int dtype, uint16_t* gb) {
+#pragma omp parallel for schedule(static)
+  for (int64_t j = 0; j < n; j++) {
+    double s = 0.0;
+    for (int64_t i = 0; i < m; i++) s += dec16(dtype, dy[i * n + j]);
+    gb[j] = enc16(dtype, s);
+  }
+}
+
+/* ------------------------------------------------------------------------ */
 /* [A2A] AlltoAllQuantMatmul, dynamic per-token A16W8.                       */
 /* ------------------------------------------------------------------------ */
 

@@ -575,3 +575,73 @@ def test_qar_exact_rational_on_generated_inputs():
             exact = sum(Fraction(float(dx[i][tok, c])) *
                         Fraction(2) ** (int(sc[i].reshape(2, 32)[tok, c // 32]) - 127) for i in range(8))
             assert int(out[tok, c]) == round_rne(exact, "bf16")
+
+
+# ----------------------------------------------------------------- layer bias and grad_bias (mc2.py listing)
+@pytest.mark.parametrize("fmt", ["bf16", "f16"])
+def test_add_bias_exact_rational(fmt):
+    """out + bias on 16-bit values equals the exact sum rounded once, including exact
+    cancellation, terms many binades apart and (fp16) overflow to infinity."""
+    rng = np.random.default_rng(41)
+    m, n = 6, 9
+    y = enc(rng.normal(0, 1, (m, n)) * np.exp2(rng.integers(-12, 12, (m, n))), fmt)
+    b = enc(rng.normal(0, 1, n) * np.exp2(rng.integers(-12, 12, n)), fmt)
+    if fmt == "f16":
+        y[1, 0], b[0] = enc([65504.0], fmt)[0], enc([32.0], fmt)[0]   # 65536 -> inf
+    y[0] = enc(-decode16(b, fmt), fmt)                       # row 0: y = -bias exactly
+    got = oracle.add_bias(y, b, fmt)
+    yv, bv = decode16(y, fmt), decode16(b, fmt)
+    want = np.array([[round_rne(Fraction(float(yv[i, j])) + Fraction(float(bv[j])), fmt) for j in range(n)]
+                     for i in range(m)], dtype=np.uint16)
+    assert np.array_equal(bits(got), want)
+    assert np.all(bits(got)[0] == 0)                          # x + (-x) = +0
+    if fmt == "f16":
+        assert bits(got)[1, 0] == 0x7C00
+
+
+def test_add_bias_zero_is_identity():
+    rng = np.random.default_rng(42)
+    y = enc(np.abs(rng.normal(0, 3, (5, 7))) + 0.5, "bf16")
+    assert np.array_equal(oracle.add_bias(y, np.zeros(7, np.uint16), "bf16"), y)
+
+
+@pytest.mark.parametrize("fmt", ["bf16", "f16"])
+def test_bias_grad_exact_rational_and_numpy(fmt):
+    """grad_bias = dy.sum(dim=0): the exact column sum rounded once (exact rationals on a
+    small case; numpy's float64 column sum, exact here, on a larger one)."""
+    rng = np.random.default_rng(43)
+    dy = enc(rng.normal(0, 1, (37, 5)), fmt)
+    got = oracle.bias_grad(dy, fmt)
+    v = decode16(dy, fmt)
+    want = [round_rne(sum(Fraction(float(v[i, j])) for i in range(37)), fmt) for j in range(5)]
+    assert bits(got).tolist() == want
+    dy = enc(rng.normal(0, 1, (4096, 64)), fmt)
+    s = decode16(dy, fmt).sum(axis=0)          # float64, exact: 8 + 13 bits of range + 12 of count
+    assert np.array_equal(bits(oracle.bias_grad(dy, fmt)), enc(s, fmt).view(np.uint16))
+
+
+def test_bias_grad_integer_columns():
+    """Small-integer gradients: every column sum is an exact integer (numpy int64)."""
+    rng = np.random.default_rng(44)
+    ints = rng.integers(-3, 4, (1000, 33))
+    got = oracle.bias_grad(enc(ints.astype(np.float64), "bf16"), "bf16")
+    assert np.array_equal(got, enc(ints.sum(axis=0).astype(np.float64), "bf16"))
+
+
+def test_column_parallel_layer_with_bias_equals_unsharded_linear():
+    """r ranks' column shards of W and bias, each rank's AllGatherMatmul + bias, stacked
+    along the output columns, equal the unsharded layer x W^T + b; with small-integer
+    operands every value is exact, so bit for bit (numpy int64 reference)."""
+    rng = np.random.default_rng(45)
+    r, m_l, k, n_l = 4, 8, 256, 16
+    xs = [rng.integers(-2, 3, (m_l, k)) for _ in range(r)]
+    W = rng.integers(-2, 3, (r * n_l, k))
+    b = rng.integers(-4, 5, r * n_l)
+    e = lambda a: enc(np.asarray(a, np.float64), "bf16")
+    outs = []
+    for j in range(r):
+        wj = np.ascontiguousarray(W[j * n_l:(j + 1) * n_l])
+        o, _ = oracle.allgather_matmul([e(x) for x in xs], e(wj), "bf16", x2_trans=True)
+        outs.append(oracle.add_bias(o, e(b[j * n_l:(j + 1) * n_l]), "bf16"))
+    full = np.concatenate(xs) @ W.T + b
+    assert np.array_equal(np.concatenate(outs, axis=1), e(full))
