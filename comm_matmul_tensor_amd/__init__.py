@@ -10,7 +10,7 @@ Functions carry the C names:
   mc2_allgather_matmul, mc2_allgather_arrival_fallbacks, mc2_matmul_grad_input, mc2_matmul_grad_weight,
   mc2_matmul_reduce_scatter,
   mc2_alltoall_quant_matmul_workspace_size, mc2_alltoall_quant_matmul, mc2_alltoall_quant_matmul_static,
-  mc2_quant_all_reduce, mc2_quant_reduce_scatter, mc2_status_string, mc2_last_error;
+  mc2_alltoall_quant_matmul_noalloc, mc2_quant_all_reduce, mc2_quant_reduce_scatter, mc2_status_string, mc2_last_error;
 and the test hook mc2_testing_arrival (csrc/testing.h, outside the public header).
 
 Every call checks each tensor's shape, dtype and device against the sizes it
@@ -67,6 +67,8 @@ _SIGS = {
     "mc2_matmul_reduce_scatter": [_P, _P, _INT, _INT, _I64, _I64, _I64, _INT, _INT, _P, _P, _P, _P],
     "mc2_alltoall_quant_matmul_static": [_P, _INT, _I64, _I64, _P, _P, _I64, _P, _P, _P, _INT, _P, _P, _P],
     "mc2_testing_arrival": [ctypes.c_uint64, _INT],
+    "mc2_alltoall_quant_matmul_noalloc": [_P, _INT, _I64, _I64, _INT, _P, _I64, _P, _P, _P, _P, _P, _P, _P, _P,
+                                          _P],
 }
 for _name, _args in _SIGS.items():
     _f = getattr(_lib, _name)
@@ -361,6 +363,39 @@ def mc2_alltoall_quant_matmul(x1: torch.Tensor, rank_size: int, x2: torch.Tensor
     return out
 
 
+# bytes of the library's own scratch array (include/mc2.h, MC2_NOALLOC_SCRATCH_BYTES)
+MC2_NOALLOC_SCRATCH_BYTES = 48 << 20
+
+
+def mc2_alltoall_quant_matmul_noalloc(x1: torch.Tensor, rank_size: int, x2: torch.Tensor, x2_scale: torch.Tensor,
+                                      x1_smooth: Optional[torch.Tensor] = None, bias: Optional[torch.Tensor] = None,
+                                      *, out: torch.Tensor, permuted_out: Optional[torch.Tensor] = None,
+                                      q_out: Optional[torch.Tensor] = None,
+                                      x1_scale_out: Optional[torch.Tensor] = None,
+                                      acc_out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """mc2_alltoall_quant_matmul for callers that cannot allocate: `out` must be given, and the
+    workspace is the library's own per-GPU array (calls overlapping on one GPU race on it)."""
+    bs, h, n, rows, cols = _a2a_sizes(x1, rank_size, x2)
+    _16bit(x1, "x1")
+    _want(x2_scale, "x2_scale", (n,), torch.float32)
+    _want(x1_smooth, "x1_smooth", (cols,), x1.dtype, optional=True)
+    _want(bias, "bias", (n,), x1.dtype, optional=True)
+    _want(out, "out", (rows, n), x1.dtype)
+    _want(permuted_out, "permuted_out", (rows, cols), x1.dtype, optional=True)
+    _want(q_out, "q_out", (rows, cols), torch.int8, optional=True)
+    _want(x1_scale_out, "x1_scale_out", (rows,), torch.float32, optional=True)
+    _want(acc_out, "acc_out", (rows, n), torch.int32, optional=True)
+    _same_device([("x1", x1), ("x2", x2), ("x2_scale", x2_scale), ("x1_smooth", x1_smooth), ("bias", bias),
+                  ("out", out), ("permuted_out", permuted_out), ("q_out", q_out), ("x1_scale_out", x1_scale_out),
+                  ("acc_out", acc_out)])
+    st = _stream_obj(stream)
+    _check(_lib.mc2_alltoall_quant_matmul_noalloc(
+        _dev(x1, "x1"), rank_size, bs, h, _dt(x1), _dev(x2, "x2"), n, _dev(x2_scale, "x2_scale"),
+        _opt(x1_smooth, "x1_smooth"), _opt(bias, "bias"), _dev(out, "out"), _opt(permuted_out, "permuted_out"),
+        _opt(q_out, "q_out"), _opt(x1_scale_out, "x1_scale_out"), _opt(acc_out, "acc_out"), st.cuda_stream))
+    return out
+
+
 def mc2_alltoall_quant_matmul_static(x1: torch.Tensor, rank_size: int, x1_scale: torch.Tensor, x2: torch.Tensor,
                                      x2_scale: torch.Tensor, bias: Optional[torch.Tensor] = None, *,
                                      out_dtype: torch.dtype = torch.bfloat16, out: Optional[torch.Tensor] = None,
@@ -464,6 +499,7 @@ __all__ = [
     "mc2_allgather_matmul", "mc2_allgather_arrival_fallbacks", "mc2_matmul_grad_input", "mc2_matmul_grad_weight",
     "mc2_matmul_reduce_scatter",
     "mc2_alltoall_quant_matmul_workspace_size", "mc2_alltoall_quant_matmul", "mc2_alltoall_quant_matmul_static",
+    "mc2_alltoall_quant_matmul_noalloc", "MC2_NOALLOC_SCRATCH_BYTES",
     "mc2_quant_all_reduce", "mc2_quant_reduce_scatter",
     "mc2_status_string", "mc2_last_error", "Mc2Error", "LIB_PATH",
 ]

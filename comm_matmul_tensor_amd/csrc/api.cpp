@@ -6,6 +6,7 @@
 #include <mutex>
 #include <string>
 
+#include "api_internal.hpp"
 #include "kernels.hpp"
 #include "mc2.h"
 #include "testing.h"
@@ -38,31 +39,6 @@ std::atomic<int> g_arrival_raised_slabs{-1};
 
 mc2_status hip_fail(hipError_t e, const char* where) {
   return fail(MC2_ERR_HIP, std::string(where) + ": " + hipGetErrorString(e));
-}
-
-// The current device must be a gfx950 (MI355X class) GPU.
-mc2_status current_device(int* dev_out) {
-  int count = 0;
-  if (hipGetDeviceCount(&count) != hipSuccess || count < 1) {
-    (void)hipGetLastError();
-    return fail(MC2_ERR_NO_DEVICE, "no HIP device");
-  }
-  int dev = 0;
-  hipError_t e = hipGetDevice(&dev);
-  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
-  if (dev < 0 || dev >= kMaxDevices) return fail(MC2_ERR_NO_DEVICE, "device index out of range");
-  std::lock_guard<std::mutex> lock(g_dev_mutex);
-  DeviceState& st = g_dev[dev];
-  if (!st.checked) {
-    hipDeviceProp_t p;
-    e = hipGetDeviceProperties(&p, dev);
-    if (e != hipSuccess) return hip_fail(e, "hipGetDeviceProperties");
-    st.ok = std::strncmp(p.gcnArchName, "gfx950", 6) == 0;
-    st.checked = true;
-  }
-  if (!st.ok) return fail(MC2_ERR_NO_DEVICE, "the current device is not gfx950");
-  *dev_out = dev;
-  return MC2_OK;
 }
 
 int dt(mc2_dtype d) { return static_cast<int>(d); }
@@ -104,6 +80,91 @@ mc2_status arrival_setup(int dev, DeviceState** out, unsigned* epoch = nullptr) 
 size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
 }  // namespace
+
+// The current device must be a gfx950 (MI355X class) GPU.
+mc2_status current_device(int* dev_out) {
+  int count = 0;
+  if (hipGetDeviceCount(&count) != hipSuccess || count < 1) {
+    (void)hipGetLastError();
+    return fail(MC2_ERR_NO_DEVICE, "no HIP device");
+  }
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) return fail(MC2_ERR_NO_DEVICE, "device index out of range");
+  std::lock_guard<std::mutex> lock(g_dev_mutex);
+  DeviceState& st = g_dev[dev];
+  if (!st.checked) {
+    hipDeviceProp_t p;
+    e = hipGetDeviceProperties(&p, dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDeviceProperties");
+    st.ok = std::strncmp(p.gcnArchName, "gfx950", 6) == 0;
+    st.checked = true;
+  }
+  if (!st.ok) return fail(MC2_ERR_NO_DEVICE, "the current device is not gfx950");
+  *dev_out = dev;
+  return MC2_OK;
+}
+
+// The A16W8 chain with a caller-provided workspace (the two public entry
+// points differ only in where the workspace comes from).
+mc2_status alltoall_quant_matmul_run(const void* x1, int rank_size, int64_t bs, int64_t h, mc2_dtype x1_dtype,
+                                     const int8_t* x2, int64_t n, const float* x2_scale, const void* x1_smooth,
+                                     const void* bias, void* out, void* permuted_out, int8_t* q_out,
+                                     float* x1_scale_out, int32_t* acc_out, void* workspace,
+                                     size_t workspace_bytes, void* stream, bool device_checked) {
+  size_t need = 0;
+  mc2_status s = mc2_alltoall_quant_matmul_workspace_size(rank_size, bs, h, n, &need);
+  if (s != MC2_OK) {
+    if (s == MC2_ERR_SHAPE && (!x1 || !x2 || !x2_scale || !out))
+      return fail(MC2_ERR_NULL, "alltoall_quant_matmul: x1, x2, x2_scale and out are required");
+    return s;
+  }
+  s = check_alltoall_quant_matmul(x1, rank_size, bs, h, x1_dtype, x2, n, x2_scale, x1_smooth, bias, out,
+                                  permuted_out, q_out, x1_scale_out, acc_out, workspace, workspace_bytes,
+                                  need);
+  if (s != MC2_OK) return s;
+  int dev;
+  if (!device_checked && (s = current_device(&dev)) != MC2_OK) return s;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const int64_t rows = bs / rank_size, cols = (int64_t)rank_size * h;
+  char* ws = static_cast<char*>(workspace);
+  int8_t* q = q_out ? q_out : reinterpret_cast<int8_t*>(ws);
+  ws += align_up((size_t)(rows * cols), 256);
+  float* s1 = x1_scale_out ? x1_scale_out : reinterpret_cast<float*>(ws);
+  ws += align_up((size_t)rows * 4, 256);
+
+  QuantArgs qa{};
+  qa.x1 = x1;
+  qa.smooth = x1_smooth;
+  qa.q = q;
+  qa.s1 = s1;
+  qa.permuted = permuted_out;
+  qa.bs = bs;
+  qa.h = h;
+  qa.r = rank_size;
+  qa.dtype = dt(x1_dtype);
+  hipError_t e = launch_permute_quant(qa, st);
+  if (e != hipSuccess) return hip_fail(e, "alltoall_quant_matmul quant launch");
+
+  GemmI8Args ga{};
+  ga.a = q;
+  ga.b = x2;
+  ga.s1 = s1;
+  ga.s2 = x2_scale;
+  ga.bias = bias;
+  ga.out = out;
+  ga.acc_out = acc_out;
+  ga.m = rows;
+  ga.n = n;
+  ga.k = cols;
+  ga.dtype = dt(x1_dtype);
+  ga.partials = reinterpret_cast<int32_t*>(ws);
+  e = launch_gemm_i8(ga, st);
+  if (e != hipSuccess) return hip_fail(e, "alltoall_quant_matmul gemm launch");
+  return MC2_OK;
+}
+
 }  // namespace mc2
 
 using namespace mc2;
@@ -387,56 +448,9 @@ mc2_status mc2_alltoall_quant_matmul(const void* x1, int rank_size, int64_t bs, 
                                      int8_t* q_out, float* x1_scale_out, int32_t* acc_out,
                                      void* workspace, size_t workspace_bytes, void* stream) {
   clear_error();
-  size_t need = 0;
-  mc2_status s = mc2_alltoall_quant_matmul_workspace_size(rank_size, bs, h, n, &need);
-  if (s != MC2_OK) {
-    if (s == MC2_ERR_SHAPE && (!x1 || !x2 || !x2_scale || !out))
-      return fail(MC2_ERR_NULL, "alltoall_quant_matmul: x1, x2, x2_scale and out are required");
-    return s;
-  }
-  s = check_alltoall_quant_matmul(x1, rank_size, bs, h, x1_dtype, x2, n, x2_scale, x1_smooth, bias, out,
-                                  permuted_out, q_out, x1_scale_out, acc_out, workspace, workspace_bytes,
-                                  need);
-  if (s != MC2_OK) return s;
-  int dev;
-  if ((s = current_device(&dev)) != MC2_OK) return s;
-  hipStream_t st = static_cast<hipStream_t>(stream);
-  const int64_t rows = bs / rank_size, cols = (int64_t)rank_size * h;
-  char* ws = static_cast<char*>(workspace);
-  int8_t* q = q_out ? q_out : reinterpret_cast<int8_t*>(ws);
-  ws += align_up((size_t)(rows * cols), 256);
-  float* s1 = x1_scale_out ? x1_scale_out : reinterpret_cast<float*>(ws);
-  ws += align_up((size_t)rows * 4, 256);
-
-  QuantArgs qa{};
-  qa.x1 = x1;
-  qa.smooth = x1_smooth;
-  qa.q = q;
-  qa.s1 = s1;
-  qa.permuted = permuted_out;
-  qa.bs = bs;
-  qa.h = h;
-  qa.r = rank_size;
-  qa.dtype = dt(x1_dtype);
-  hipError_t e = launch_permute_quant(qa, st);
-  if (e != hipSuccess) return hip_fail(e, "alltoall_quant_matmul quant launch");
-
-  GemmI8Args ga{};
-  ga.a = q;
-  ga.b = x2;
-  ga.s1 = s1;
-  ga.s2 = x2_scale;
-  ga.bias = bias;
-  ga.out = out;
-  ga.acc_out = acc_out;
-  ga.m = rows;
-  ga.n = n;
-  ga.k = cols;
-  ga.dtype = dt(x1_dtype);
-  ga.partials = reinterpret_cast<int32_t*>(ws);
-  e = launch_gemm_i8(ga, st);
-  if (e != hipSuccess) return hip_fail(e, "alltoall_quant_matmul gemm launch");
-  return MC2_OK;
+  return alltoall_quant_matmul_run(x1, rank_size, bs, h, x1_dtype, x2, n, x2_scale, x1_smooth, bias, out,
+                                   permuted_out, q_out, x1_scale_out, acc_out, workspace, workspace_bytes, stream,
+                                   false);
 }
 
 mc2_status mc2_alltoall_quant_matmul_static(const int8_t* x1, int rank_size, int64_t bs, int64_t h,

@@ -221,6 +221,29 @@ mc2_status mc2_alltoall_quant_matmul(const void* x1, int rank_size, int64_t bs, 
                                      void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * mc2_alltoall_quant_matmul without a workspace, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation).  Same arguments, results and errors as
+ * mc2_alltoall_quant_matmul, minus workspace and workspace_bytes: the
+ * workspace is a device array inside the library, MC2_NOALLOC_SCRATCH_BYTES
+ * (48 MiB) per GPU, held from the library's first use on that GPU until the
+ * process ends.  Sizes whose workspace (mc2_alltoall_quant_matmul_workspace_size)
+ * exceeds it are rejected with MC2_ERR_WORKSPACE before any device call; at
+ * rank_size h = 32768 that allows bs / rank_size up to 1535 tokens.  This call
+ * allocates nothing.  Every call on a GPU shares that GPU's array, so calls
+ * that overlap in time on one GPU (other streams, other host threads) race
+ * on it and must be serialised by the caller; the array keeps the last
+ * call's contents, which the next call overwrites before reading.
+ */
+#define MC2_NOALLOC_SCRATCH_BYTES ((size_t)48 << 20)
+mc2_status mc2_alltoall_quant_matmul_noalloc(const void* x1, int rank_size, int64_t bs, int64_t h,
+                                             mc2_dtype x1_dtype, const int8_t* x2, int64_t n,
+                                             const float* x2_scale, const void* x1_smooth,
+                                             const void* bias, void* out, void* permuted_out,
+                                             int8_t* q_out, float* x1_scale_out, int32_t* acc_out,
+                                             void* stream);
+
+/*
  * AlltoAllQuantMatmul, full quantisation (x1 mode 3, per-token; x2 mode 2,
  * per-channel) -- aclnnAlltoAllQuantMatmul page, "function" formulas, the
  * full-quant case: x1 arrives already int8, with one scale per token.

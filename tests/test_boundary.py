@@ -31,7 +31,7 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     names = _declared()
-    assert len(names) == 12, names
+    assert len(names) == 13, names
     for n in names:
         assert hasattr(lib, n), n
 
@@ -207,3 +207,18 @@ def test_valid_call_without_device_reports_no_device(lib):
     f.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_int64, ctypes.c_int,
                   ctypes.c_int, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p]
     assert f(_ptrs(A, A), _ptrs(B, B), 2, 8, 1024, 3, 0, C, 0, None) == 6
+
+
+def test_noalloc_rejects_sizes_beyond_its_array_on_the_host(lib):
+    """The no-allocation A16W8 call refuses sizes whose workspace exceeds its 48 MiB array
+    before any device call (this runs without a GPU), and names the limit."""
+    f = lib.mc2_alltoall_quant_matmul_noalloc
+    f.restype = ctypes.c_int
+    I64 = ctypes.c_int64
+    # rank_size 8, h 4096: 1536 tokens need 48 MiB of codes plus the scales
+    st = f(A, 8, I64(8 * 1536), I64(4096), 2, B, I64(16), C, None, None, A, None, None, None, None, None)
+    assert st == 5, st  # MC2_ERR_WORKSPACE
+    assert "50331648" in _err(lib)
+    # sizes the operator itself rejects keep their own status
+    st = f(A, 3, I64(8 * 1536), I64(4096), 2, B, I64(16), C, None, None, A, None, None, None, None, None)
+    assert st == 2, st  # MC2_ERR_SHAPE
