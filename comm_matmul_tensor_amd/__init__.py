@@ -7,8 +7,8 @@ CPU or PyTorch fallback: if ``libmc2.so`` is missing, importing this package
 raises.
 
 Functions carry the C names:
-  mc2_allgather_matmul, mc2_allgather_arrival_fallbacks, mc2_matmul_grad_input, mc2_matmul_grad_weight,
-  mc2_matmul_reduce_scatter,
+  mc2_allgather_matmul, mc2_allgather_matmul_bias, mc2_allgather_arrival_fallbacks, mc2_matmul_grad_input,
+  mc2_matmul_grad_weight, mc2_matmul_reduce_scatter, mc2_matmul_reduce_scatter_bias, mc2_bias_grad,
   mc2_alltoall_quant_matmul_workspace_size, mc2_alltoall_quant_matmul, mc2_alltoall_quant_matmul_static,
   mc2_alltoall_quant_matmul_noalloc, mc2_quant_all_reduce, mc2_quant_reduce_scatter, mc2_status_string, mc2_last_error;
 and the test hook mc2_testing_arrival (csrc/testing.h, outside the public header).
@@ -69,6 +69,9 @@ _SIGS = {
     "mc2_testing_arrival": [ctypes.c_uint64, _INT],
     "mc2_alltoall_quant_matmul_noalloc": [_P, _INT, _I64, _I64, _INT, _P, _I64, _P, _P, _P, _P, _P, _P, _P, _P,
                                           _P],
+    "mc2_allgather_matmul_bias": [_P, _INT, _I64, _I64, _P, _I64, _INT, _INT, _P, _P, _P, _INT, _INT, _P],
+    "mc2_matmul_reduce_scatter_bias": [_P, _P, _INT, _INT, _I64, _I64, _I64, _INT, _INT, _P, _P, _P, _P, _P],
+    "mc2_bias_grad": [_P, _I64, _I64, _INT, _P, _P],
 }
 for _name, _args in _SIGS.items():
     _f = getattr(_lib, _name)
@@ -188,7 +191,7 @@ def _16bit(t, name: str):
 def mc2_allgather_matmul(shards: Sequence[torch.Tensor], x2: torch.Tensor, *, x2_trans: bool = False,
                          out: Optional[torch.Tensor] = None, gather_out: Optional[torch.Tensor] = None,
                          gather_output: bool = True, mode: int = MC2_AG_FUSED_WRITE, rank_id: int = 0,
-                         stream=None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+                         stream=None, _bias: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
     """out = AllGather_m(shards) @ x2 and gather_out = AllGather_m(shards).
 
     x2 is (k, n), or with x2_trans=True a (n, k) buffer holding x2^T.
@@ -206,18 +209,37 @@ def mc2_allgather_matmul(shards: Sequence[torch.Tensor], x2: torch.Tensor, *, x2
     _want(x2, "x2", (n, k) if x2_trans else (k, n), dt)
     _want(out, "out", (r * m_local, n), dt, optional=True)
     _want(gather_out, "gather_out", (r * m_local, k), dt, optional=True)
+    _want(_bias, "bias", (n,), dt, optional=True)
     dev = _same_device([(f"shards[{i}]", s) for i, s in enumerate(shards)] +
-                       [("x2", x2), ("out", out), ("gather_out", gather_out)])
+                       [("x2", x2), ("out", out), ("gather_out", gather_out), ("bias", _bias)])
     st = _stream_obj(stream)
     with torch.cuda.stream(st):
         if out is None:
             out = torch.empty((r * m_local, n), dtype=dt, device=dev)
         if gather_out is None and (gather_output or mode == MC2_AG_ARRIVAL):
             gather_out = torch.empty((r * m_local, k), dtype=dt, device=dev)
-        _check(_lib.mc2_allgather_matmul(_ptrs(shards, "shards"), r, m_local, k, _dev(x2, "x2"), n,
-                                         int(x2_trans), _dt(shards[0]), _dev(out, "out"),
-                                         _opt(gather_out, "gather_out"), mode, rank_id, st.cuda_stream))
+        if _bias is None:
+            _check(_lib.mc2_allgather_matmul(_ptrs(shards, "shards"), r, m_local, k, _dev(x2, "x2"), n,
+                                             int(x2_trans), _dt(shards[0]), _dev(out, "out"),
+                                             _opt(gather_out, "gather_out"), mode, rank_id, st.cuda_stream))
+        else:
+            _check(_lib.mc2_allgather_matmul_bias(_ptrs(shards, "shards"), r, m_local, k, _dev(x2, "x2"), n,
+                                                  int(x2_trans), _dt(shards[0]), _dev(_bias, "bias"),
+                                                  _dev(out, "out"), _opt(gather_out, "gather_out"), mode, rank_id,
+                                                  st.cuda_stream))
     return out, gather_out
+
+
+def mc2_allgather_matmul_bias(shards: Sequence[torch.Tensor], x2: torch.Tensor, bias: torch.Tensor, *,
+                              x2_trans: bool = False, out: Optional[torch.Tensor] = None,
+                              gather_out: Optional[torch.Tensor] = None, gather_output: bool = True,
+                              mode: int = MC2_AG_FUSED_WRITE, rank_id: int = 0,
+                              stream=None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """The column-parallel layer's forward: out = AllGather_m(shards) @ x2 + bias (bias (n,))."""
+    if bias is None:
+        raise ValueError("bias is required")
+    return mc2_allgather_matmul(shards, x2, x2_trans=x2_trans, out=out, gather_out=gather_out,
+                                gather_output=gather_output, mode=mode, rank_id=rank_id, stream=stream, _bias=bias)
 
 
 def mc2_allgather_arrival_fallbacks(reset: bool = False) -> int:
@@ -256,8 +278,8 @@ def mc2_matmul_grad_input(dy: torch.Tensor, w: torch.Tensor, *, out: Optional[to
 
 def mc2_matmul_reduce_scatter(x: torch.Tensor, x2: torch.Tensor, recv: Sequence[Optional[torch.Tensor]],
                               rank_id: int, *, x2_trans: bool = False, out: Optional[torch.Tensor] = None,
-                              partial_out: Optional[torch.Tensor] = None,
-                              stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
+                              partial_out: Optional[torch.Tensor] = None, stream=None,
+                              _bias: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
     """Rank rank_id's share of ReduceScatter_m(x @ x2): returns (out, partial_out).
     recv[j] (j != rank_id) is the (m / len(recv), n) block rank j sends; x2 is (k, n), or
     (n, k) with x2_trans (the row-parallel forward passes the nn.Linear weight that way)."""
@@ -276,7 +298,8 @@ def mc2_matmul_reduce_scatter(x: torch.Tensor, x2: torch.Tensor, recv: Sequence[
             _want(b, f"recv[{j}]", (m // ws, n), x.dtype)
     _want(out, "out", (m // ws, n), x.dtype, optional=True)
     _want(partial_out, "partial_out", (m, n), x.dtype, optional=True)
-    dev = _same_device([("x", x), ("x2", x2), ("out", out), ("partial_out", partial_out)] +
+    _want(_bias, "bias", (n,), x.dtype, optional=True)
+    dev = _same_device([("x", x), ("x2", x2), ("out", out), ("partial_out", partial_out), ("bias", _bias)] +
                        [(f"recv[{j}]", b) for j, b in enumerate(recv) if j != rank_id])
     st = _stream_obj(stream)
     with torch.cuda.stream(st):
@@ -286,10 +309,41 @@ def mc2_matmul_reduce_scatter(x: torch.Tensor, x2: torch.Tensor, recv: Sequence[
             partial_out = torch.empty((m, n), dtype=x.dtype, device=dev)
         ptrs = (ctypes.c_void_p * ws)(*[None if j == rank_id else _dev(b, f"recv[{j}]")
                                         for j, b in enumerate(recv)])
-        _check(_lib.mc2_matmul_reduce_scatter(_dev(x, "x"), _dev(x2, "x2"), ws, rank_id, m, k, n,
-                                              int(bool(x2_trans)), _dt(x), ptrs, _dev(out, "out"),
-                                              _dev(partial_out, "partial_out"), st.cuda_stream))
+        if _bias is None:
+            _check(_lib.mc2_matmul_reduce_scatter(_dev(x, "x"), _dev(x2, "x2"), ws, rank_id, m, k, n,
+                                                  int(bool(x2_trans)), _dt(x), ptrs, _dev(out, "out"),
+                                                  _dev(partial_out, "partial_out"), st.cuda_stream))
+        else:
+            _check(_lib.mc2_matmul_reduce_scatter_bias(_dev(x, "x"), _dev(x2, "x2"), ws, rank_id, m, k, n,
+                                                       int(bool(x2_trans)), _dt(x), ptrs, _dev(_bias, "bias"),
+                                                       _dev(out, "out"), _dev(partial_out, "partial_out"),
+                                                       st.cuda_stream))
     return out, partial_out
+
+
+def mc2_matmul_reduce_scatter_bias(x: torch.Tensor, x2: torch.Tensor, recv: Sequence[Optional[torch.Tensor]],
+                                   rank_id: int, bias: torch.Tensor, *, x2_trans: bool = False,
+                                   out: Optional[torch.Tensor] = None, partial_out: Optional[torch.Tensor] = None,
+                                   stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """The row-parallel layer's forward share: out = ReduceScatter_m(x @ x2) block + bias (bias (n,))."""
+    if bias is None:
+        raise ValueError("bias is required")
+    return mc2_matmul_reduce_scatter(x, x2, recv, rank_id, x2_trans=x2_trans, out=out, partial_out=partial_out,
+                                     stream=stream, _bias=bias)
+
+
+def mc2_bias_grad(dy: torch.Tensor, *, out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """grad_bias = dy.sum(dim=0) for dy (m, n), rounded once to dy's dtype."""
+    m, n = _2d(dy, "dy")
+    _16bit(dy, "dy")
+    _want(out, "out", (n,), dy.dtype, optional=True)
+    dev = _same_device([("dy", dy), ("out", out)])
+    st = _stream_obj(stream)
+    with torch.cuda.stream(st):
+        if out is None:
+            out = torch.empty((n,), dtype=dy.dtype, device=dev)
+        _check(_lib.mc2_bias_grad(_dev(dy, "dy"), m, n, _dt(dy), _dev(out, "grad_bias"), st.cuda_stream))
+    return out
 
 
 def mc2_matmul_grad_weight(dy: torch.Tensor, ag_x: torch.Tensor, *, out: Optional[torch.Tensor] = None,
@@ -496,8 +550,9 @@ def mc2_quant_reduce_scatter(x: Sequence[torch.Tensor], scales: Sequence[torch.T
 
 
 __all__ = [
-    "mc2_allgather_matmul", "mc2_allgather_arrival_fallbacks", "mc2_matmul_grad_input", "mc2_matmul_grad_weight",
-    "mc2_matmul_reduce_scatter",
+    "mc2_allgather_matmul", "mc2_allgather_matmul_bias", "mc2_allgather_arrival_fallbacks",
+    "mc2_matmul_grad_input", "mc2_matmul_grad_weight", "mc2_matmul_reduce_scatter", "mc2_matmul_reduce_scatter_bias",
+    "mc2_bias_grad",
     "mc2_alltoall_quant_matmul_workspace_size", "mc2_alltoall_quant_matmul", "mc2_alltoall_quant_matmul_static",
     "mc2_alltoall_quant_matmul_noalloc", "MC2_NOALLOC_SCRATCH_BYTES",
     "mc2_quant_all_reduce", "mc2_quant_reduce_scatter",

@@ -267,10 +267,15 @@ mc2_status mc2_matmul_grad_input(const void* dy, const void* w, int64_t m, int64
   return MC2_OK;
 }
 
-mc2_status mc2_matmul_reduce_scatter(const void* x, const void* x2, int world_size, int rank_id, int64_t m,
-                                     int64_t k, int64_t n, int x2_trans, mc2_dtype dtype, const void* const* recv,
-                                     void* out, void* partial_out, void* stream) {
-  clear_error();
+}  // extern "C"
+
+namespace mc2 {
+namespace {
+
+// MatmulReduceScatter share with an optional bias added to the reduced block.
+mc2_status matmul_reduce_scatter_impl(const void* x, const void* x2, int world_size, int rank_id, int64_t m,
+                                      int64_t k, int64_t n, int x2_trans, mc2_dtype dtype, const void* const* recv,
+                                      const void* bias, void* out, void* partial_out, void* stream) {
   mc2_status s = check_matmul_reduce_scatter(x, x2, world_size, rank_id, m, k, n, dtype, recv, out, partial_out);
   if (s != MC2_OK) return s;
   int dev;
@@ -293,9 +298,34 @@ mc2_status mc2_matmul_reduce_scatter(const void* x, const void* x2, int world_si
   a.rs_rank = rank_id;
   a.rs_rows = m / world_size;
   a.rs_row0 = (int64_t)rank_id * a.rs_rows;
+  a.bias = bias;
   hipError_t e = launch_gemm16(a, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "matmul_reduce_scatter launch");
   return MC2_OK;
+}
+
+}  // namespace
+}  // namespace mc2
+
+extern "C" {
+
+mc2_status mc2_matmul_reduce_scatter(const void* x, const void* x2, int world_size, int rank_id, int64_t m,
+                                     int64_t k, int64_t n, int x2_trans, mc2_dtype dtype, const void* const* recv,
+                                     void* out, void* partial_out, void* stream) {
+  clear_error();
+  return matmul_reduce_scatter_impl(x, x2, world_size, rank_id, m, k, n, x2_trans, dtype, recv, nullptr, out,
+                                    partial_out, stream);
+}
+
+mc2_status mc2_matmul_reduce_scatter_bias(const void* x, const void* x2, int world_size, int rank_id, int64_t m,
+                                          int64_t k, int64_t n, int x2_trans, mc2_dtype dtype,
+                                          const void* const* recv, const void* bias, void* out, void* partial_out,
+                                          void* stream) {
+  clear_error();
+  mc2_status s = check_bias("matmul_reduce_scatter_bias", bias);
+  if (s != MC2_OK) return s;
+  return matmul_reduce_scatter_impl(x, x2, world_size, rank_id, m, k, n, x2_trans, dtype, recv, bias, out,
+                                    partial_out, stream);
 }
 
 mc2_status mc2_matmul_grad_weight(const void* dy, const void* ag_x, int64_t m, int64_t n_local,
@@ -322,11 +352,15 @@ mc2_status mc2_matmul_grad_weight(const void* dy, const void* ag_x, int64_t m, i
   return MC2_OK;
 }
 
-mc2_status mc2_allgather_matmul(const void* const* shards, int world_size, int64_t m_local,
-                                int64_t k, const void* x2, int64_t n, int x2_trans,
-                                mc2_dtype dtype, void* out, void* gather_out, mc2_ag_mode mode,
-                                int rank_id, void* stream) {
-  clear_error();
+}  // extern "C"
+
+namespace mc2 {
+namespace {
+
+// AllGatherMatmul with an optional bias added before the output's rounding.
+mc2_status allgather_matmul_impl(const void* const* shards, int world_size, int64_t m_local, int64_t k,
+                                 const void* x2, int64_t n, int x2_trans, mc2_dtype dtype, const void* bias,
+                                 void* out, void* gather_out, mc2_ag_mode mode, int rank_id, void* stream) {
   mc2_status s = check_allgather_matmul(shards, world_size, m_local, k, x2, n, dtype, out, gather_out,
                                         static_cast<int>(mode), rank_id);
   if (s != MC2_OK) return s;
@@ -343,6 +377,7 @@ mc2_status mc2_allgather_matmul(const void* const* shards, int world_size, int64
   a.n = n;
   a.k = k;
   a.dtype = dt(dtype);
+  a.bias = bias;
   if (mode == MC2_AG_FUSED_WRITE) {
     for (int i = 0; i < world_size; i++) a.a_parts[i] = shards[i];
     a.num_parts = world_size;
@@ -403,6 +438,41 @@ mc2_status mc2_allgather_matmul(const void* const* shards, int world_size, int64
   if (e == hipSuccess) e = hipEventRecord(ds->join, ds->copy_stream);
   if (e == hipSuccess) e = hipStreamWaitEvent(st, ds->join, 0);
   if (e != hipSuccess) return hip_fail(e, "allgather_matmul arrival launch");
+  return MC2_OK;
+}
+
+}  // namespace
+}  // namespace mc2
+
+extern "C" {
+
+mc2_status mc2_allgather_matmul(const void* const* shards, int world_size, int64_t m_local,
+                                int64_t k, const void* x2, int64_t n, int x2_trans,
+                                mc2_dtype dtype, void* out, void* gather_out, mc2_ag_mode mode,
+                                int rank_id, void* stream) {
+  clear_error();
+  return allgather_matmul_impl(shards, world_size, m_local, k, x2, n, x2_trans, dtype, nullptr, out, gather_out,
+                               mode, rank_id, stream);
+}
+
+mc2_status mc2_allgather_matmul_bias(const void* const* shards, int world_size, int64_t m_local, int64_t k,
+                                     const void* x2, int64_t n, int x2_trans, mc2_dtype dtype, const void* bias,
+                                     void* out, void* gather_out, mc2_ag_mode mode, int rank_id, void* stream) {
+  clear_error();
+  mc2_status s = check_bias("allgather_matmul_bias", bias);
+  if (s != MC2_OK) return s;
+  return allgather_matmul_impl(shards, world_size, m_local, k, x2, n, x2_trans, dtype, bias, out, gather_out,
+                               mode, rank_id, stream);
+}
+
+mc2_status mc2_bias_grad(const void* dy, int64_t m, int64_t n, mc2_dtype dtype, void* grad_bias, void* stream) {
+  clear_error();
+  mc2_status s = check_bias_grad(dy, m, n, dtype, grad_bias);
+  if (s != MC2_OK) return s;
+  int dev;
+  if ((s = current_device(&dev)) != MC2_OK) return s;
+  hipError_t e = launch_bias_grad(dy, m, n, dt(dtype), grad_bias, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "bias_grad launch");
   return MC2_OK;
 }
 

@@ -29,9 +29,9 @@ constexpr int kCopyThreads = 256;
 constexpr int kBatch = 16;  // 16-byte loads in flight per thread
 constexpr int kPolicyDevice = 16;  // buffer store cache policy: sc1, coherent device-wide
 
-__global__ __launch_bounds__(kCopyThreads) void arrive_kernel(ArrivalArgs a) {
-  // piece w: slab w / chunks of row chunk (first_chunk + w % chunks) % chunks
-  const int w = (int)blockIdx.x;
+// Copies piece w (slab w / chunks of row chunk (first_chunk + w % chunks) %
+// chunks) and raises its flag.
+__device__ __forceinline__ void copy_piece(const ArrivalArgs& a, const int w) {
   const int sl = w / a.chunks, g = (a.first_chunk + w % a.chunks) % a.chunks;
   const int64_t m = (int64_t)a.r * a.block_rows;
   const int64_t row0 = (int64_t)g * a.rows_chunk;
@@ -129,6 +129,10 @@ __global__ __launch_bounds__(kCopyThreads) void arrive_kernel(ArrivalArgs a) {
   if (threadIdx.x == 0 && sl < a.raised_slabs)
     __hip_atomic_store(a.flags + (int64_t)g * a.slabs + sl, a.epoch, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_SYSTEM);
 }
+
+// One workgroup per piece.  (A fixed grid walking the pieces in order
+// measured slower beside the GEMM: 142-155 us against 139 us.)
+__global__ __launch_bounds__(kCopyThreads) void arrive_kernel(ArrivalArgs a) { copy_piece(a, (int)blockIdx.x); }
 
 }  // namespace
 

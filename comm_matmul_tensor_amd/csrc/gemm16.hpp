@@ -108,8 +108,9 @@ __device__ __forceinline__ void store_rs_tile(const uint16_t* h0, const uint16_t
 struct RsReduceArgs {
   uint16_t* out;
   const uint16_t* recv[kMaxRanks];  // own and unused slots: out
+  const uint16_t* bias;             // (n) or NULL: added to the sum before the rounding
   int ranks;
-  int64_t elems;
+  int64_t elems, n;
 };
 
 template <int DT, bool VEC>
@@ -132,6 +133,11 @@ __global__ __launch_bounds__(256) void rs_reduce_kernel(RsReduceArgs a) {
           sum[e] = j == 0 ? f : (used ? sum[e] + f : sum[e]);
         }
       }
+      if (a.bias) {  // the chunk's 8 elements lie in one row (n % 8 == 0)
+        const u32x4 b = *reinterpret_cast<const u32x4*>(a.bias + (c * 8) % a.n);
+#pragma unroll
+        for (int e = 0; e < 8; e++) sum[e] = sum[e] + O::dec(b[e / 2] >> (16 * (e & 1)));
+      }
       u32x4 o;
 #pragma unroll
       for (int w = 0; w < 4; w++) o[w] = (uint32_t)O::cvt(sum[2 * w]) | ((uint32_t)O::cvt(sum[2 * w + 1]) << 16);
@@ -141,6 +147,7 @@ __global__ __launch_bounds__(256) void rs_reduce_kernel(RsReduceArgs a) {
     for (int64_t e = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; e < a.elems; e += stride) {
       float sum = 0.0f;
       for (int j = 0; j < a.ranks; j++) sum = j == 0 ? O::dec(a.recv[j][e]) : sum + O::dec(a.recv[j][e]);
+      if (a.bias) sum = sum + O::dec(a.bias[e % a.n]);
       a.out[e] = O::cvt(sum);
     }
   }
@@ -152,8 +159,10 @@ hipError_t launch_rs_reduce(const GemmArgs& g, hipStream_t s) {
   a.out = static_cast<uint16_t*>(g.rs_out);
   for (int j = 0; j < kMaxRanks; j++)
     a.recv[j] = (j < g.rs_ranks && j != g.rs_rank) ? static_cast<const uint16_t*>(g.rs_recv[j]) : a.out;
+  a.bias = static_cast<const uint16_t*>(g.bias);
   a.ranks = g.rs_ranks;
   a.elems = g.rs_rows * g.n;
+  a.n = g.n;
   // 16-byte chunks when every row of every block starts 16-byte aligned
   const bool vec = g.n % 8 == 0;
   const int64_t work = vec ? a.elems / 8 : a.elems;
@@ -187,7 +196,26 @@ __global__ __launch_bounds__(kThreads, 1) void gemm16_kernel(Problem p, void* c)
 
   uint16_t* h0 = reinterpret_cast<uint16_t*>(s0);
   uint16_t* h1 = reinterpret_cast<uint16_t*>(s1);
-  stage_c16<BM, BN, DT>(h0, h1, [&](int i, int j, int r, int, int) { return acc[i][j][r]; });
+  // bias epilogue: three-stage tiles only (the 256 x 256 tile's registers are
+  // all taken by its accumulators)
+  if (lds_stages<BM, BN>() == 3 && p.bias) {
+    // the lane's FN x 4 columns (accumulator layout: stage_c16), each bias
+    // value loaded once
+    constexpr int WN = BN / 2;
+    const int lane = threadIdx.x % 64, wn = (threadIdx.x / 64) % 2;
+    const uint16_t* bias = static_cast<const uint16_t*>(p.bias);
+    float bv[FN][4];
+#pragma unroll
+    for (int j = 0; j < FN; j++)
+#pragma unroll
+      for (int r = 0; r < 4; r++) {
+        const int64_t col = n0 + wn * WN + 16 * j + 4 * (lane / 16) + r;
+        bv[j][r] = col < p.n ? Ops16<DT>::dec(bias[col]) : 0.0f;
+      }
+    stage_c16<BM, BN, DT>(h0, h1, [&](int i, int j, int r, int, int) { return acc[i][j][r] + bv[j][r]; });
+  } else {
+    stage_c16<BM, BN, DT>(h0, h1, [&](int i, int j, int r, int, int) { return acc[i][j][r]; });
+  }
   if (p.rs_out) store_rs_tile<BM, BN, VEC>(h0, h1, static_cast<uint16_t*>(c), p, m0, n0);
   else store_c16_tile<BM, BN, VEC>(h0, h1, static_cast<uint16_t*>(c), p.m, p.n, m0, n0, !GA);
 }
@@ -217,7 +245,7 @@ hipError_t launch_cfg(Problem p, void* c, hipStream_t s) {
     }
   }
   // the two-stage loop has neither the arrival wait nor the gather copy
-  if (lds_stages<BM, BN>() == 2 && (p.ready || p.gather_out)) return hipErrorInvalidValue;
+  if (lds_stages<BM, BN>() == 2 && (p.ready || p.gather_out || p.bias)) return hipErrorInvalidValue;
   if constexpr (AK && lds_stages<BM, BN>() == 3) {
     if (p.gather_out) {
       if (vec) gemm16_kernel<BM, BN, AK, BKM, true, DT, false, true><<<(unsigned)tiles, kThreads, 0, s>>>(p, c);
@@ -249,7 +277,8 @@ constexpr int num_tiles16() { return (AK && !BKM) ? 5 : 6; }
 
 template <bool AK, bool BKM, int DT>
 hipError_t launch_layout(const Problem& p, void* c, hipStream_t s) {
-  const int count = (p.ready || p.gather_out) ? kNumTiles3 : num_tiles16<AK, BKM>();
+  // the arrival wait, the gather copy and the bias epilogue: three-stage tiles only
+  const int count = (p.ready || p.gather_out || p.bias) ? kNumTiles3 : num_tiles16<AK, BKM>();
   const TileChoice t = tiles16<AK, BKM>()[pick_tile(p.m, p.n, tiles16<AK, BKM>(), count)];
   if (t.bm == 128 && t.bn == 224) return launch_cfg<128, 224, AK, BKM, DT>(p, c, s);
   if (t.bm == 224 && t.bn == 128) return launch_cfg<224, 128, AK, BKM, DT>(p, c, s);
@@ -278,6 +307,8 @@ hipError_t launch_dt(const GemmArgs& g, hipStream_t s) {
     p.rs_out = g.rs_out;
     p.rs_row0 = g.rs_row0;
     p.rs_rows = g.rs_rows;
+  } else {
+    p.bias = g.bias;  // with rs_out the reduce-scatter pass adds it
   }
   if (g.ready_flags) {  // arrival emulation: A arrives in gather_out, which the kernel only reads
     p.ready = g.ready_flags;

@@ -80,6 +80,9 @@ struct Problem {
   // block to row t) instead of C.
   void* rs_out;
   int64_t rs_row0, rs_rows;
+  // Optional bias (n values of the output's 16-bit type) added to every row
+  // of C in the epilogue before the rounding (NULL: none).
+  const void* bias;
   // Arrival emulation (ready == NULL: off).  A arrives in `arrived` (the
   // gathered matrix) in pieces: rows [g rows_chunk, (g+1) rows_chunk) x
   // columns [s slab_cols, (s+1) slab_cols) may be read once

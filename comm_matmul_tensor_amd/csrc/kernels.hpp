@@ -61,6 +61,10 @@ struct GemmArgs {
   const void* rs_recv[kMaxRanks];
   int rs_ranks, rs_rank;
   int64_t rs_row0, rs_rows;
+  // bias (n values of dtype, NULL: none) added before the output's rounding:
+  // to every row of C, or with rs_out only to the reduced block (rs_out row t
+  // = round(sum + bias)); the rows C sends to other ranks carry none.
+  const void* bias;
 };
 hipError_t launch_gemm16(const GemmArgs& a, hipStream_t s);
 // The fp16 part of launch_gemm16 (its own translation unit).
@@ -72,6 +76,10 @@ int gemm16_tile_rows(int64_t m, int64_t n, int b_kmajor);
 // Default longest wait of the arrival GEMM for one piece: 200 ms of the
 // 100 MHz real-time counter.
 constexpr uint64_t kArrivalWaitTicks = 20000000ull;
+
+// ---- grad_bias: gb[j] = round(sum over rows i of dy[i][j]), (m, n) 16-bit dy,
+// the sum in fp64, rounded once to the same 16-bit type
+hipError_t launch_bias_grad(const void* dy, int64_t m, int64_t n, int dtype, void* gb, hipStream_t s);
 
 // ---- arrival emulation: copy of the shards into gather_out piece by piece
 // (row chunk g, slab s of K), each piece followed by its ready flag

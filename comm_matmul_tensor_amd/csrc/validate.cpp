@@ -111,6 +111,22 @@ mc2_status check_grad_weight(const void* dy, const void* ag_x, int64_t m, int64_
   return MC2_OK;
 }
 
+mc2_status check_bias(const char* who, const void* bias) {
+  // the layer's bias (hyper_parallel mc2.py, forward: out = out + bias)
+  if (!bias) return fail(MC2_ERR_NULL, std::string(who) + ": bias is required");
+  if (!aligned16(bias)) return fail(MC2_ERR_ALIGN, std::string(who) + ": bias not 16-byte aligned");
+  return MC2_OK;
+}
+
+mc2_status check_bias_grad(const void* dy, int64_t m, int64_t n, mc2_dtype dtype, const void* grad_bias) {
+  if (!dy || !grad_bias) return fail(MC2_ERR_NULL, "bias_grad: dy and grad_bias are required");
+  if (m < 1 || n < 1) return fail(MC2_ERR_SHAPE, "bias_grad: empty m or n");
+  if (m > INT32_MAX || n > INT32_MAX) return fail(MC2_ERR_SHAPE, "bias_grad: m or n above INT32_MAX");
+  if (!is_half(dtype)) return fail(MC2_ERR_DTYPE, "bias_grad: dtype must be F16 or BF16");
+  if (!aligned16(dy) || !aligned16(grad_bias)) return fail(MC2_ERR_ALIGN, "bias_grad: tensor not 16-byte aligned");
+  return MC2_OK;
+}
+
 mc2_status check_alltoall_sizes(int rank_size, int64_t bs, int64_t h, int64_t n) {
   // aclnnAlltoAllQuantMatmul "constraints": rankSize 2/4/8; BS divisible by
   // rankSize; BS and N at most INT32_MAX; no empty tensors; A16W8:

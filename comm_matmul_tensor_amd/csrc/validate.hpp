@@ -25,6 +25,8 @@ mc2_status check_matmul_reduce_scatter(const void* x, const void* x2, int world_
                                        const void* out, const void* partial_out);
 mc2_status check_grad_weight(const void* dy, const void* ag_x, int64_t m, int64_t n_local,
                              int64_t k, mc2_dtype dtype, const void* dw);
+mc2_status check_bias(const char* who, const void* bias);
+mc2_status check_bias_grad(const void* dy, int64_t m, int64_t n, mc2_dtype dtype, const void* grad_bias);
 mc2_status check_alltoall_sizes(int rank_size, int64_t bs, int64_t h, int64_t n);
 mc2_status check_alltoall_quant_matmul(const void* x1, int rank_size, int64_t bs, int64_t h,
                                        mc2_dtype x1_dtype, const void* x2, int64_t n,

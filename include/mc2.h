@@ -117,6 +117,20 @@ mc2_status mc2_allgather_matmul(const void* const* shards, int world_size, int64
                                 int rank_id, void* stream);
 
 /*
+ * The column-parallel layer's forward with its bias -- hyper_parallel mc2.py,
+ * AllGatherMatmulFunction.forward: the fused op runs without a bias and the
+ * layer then adds it, out = AllGather_m(shards) @ x2 + bias.  Same arguments
+ * and errors as mc2_allgather_matmul plus
+ * bias        (n) of `dtype`, required (16-byte aligned)
+ * The bias is added to the fp32 accumulator before the single rounding of
+ * out (the listing rounds the product to `dtype` and then adds; the two
+ * differ by at most one rounding of the output).  gather_out is unchanged.
+ */
+mc2_status mc2_allgather_matmul_bias(const void* const* shards, int world_size, int64_t m_local, int64_t k,
+                                     const void* x2, int64_t n, int x2_trans, mc2_dtype dtype, const void* bias,
+                                     void* out, void* gather_out, mc2_ag_mode mode, int rank_id, void* stream);
+
+/*
  * Number of GEMM wavefronts of MC2_AG_ARRIVAL calls on the current device
  * whose wait for a piece of gather_out timed out since the last reset (each
  * read its rows from the shards instead, so results are unaffected).
@@ -171,6 +185,33 @@ mc2_status mc2_matmul_grad_input(const void* dy, const void* w, int64_t m, int64
 mc2_status mc2_matmul_reduce_scatter(const void* x, const void* x2, int world_size, int rank_id, int64_t m,
                                      int64_t k, int64_t n, int x2_trans, mc2_dtype dtype, const void* const* recv,
                                      void* out, void* partial_out, void* stream);
+
+/*
+ * The row-parallel layer's forward with its bias -- hyper_parallel mc2.py,
+ * MatmulReduceScatterFunction.forward: out = ReduceScatter_m(x @ x2) + bias.
+ * Same arguments and errors as mc2_matmul_reduce_scatter plus
+ * bias        (n) of `dtype`, required (16-byte aligned)
+ * The bias enters only the reduced block: out = round(B_0 + ... + B_{ws-1}
+ * + bias), summed in fp32 in rank order then the bias, rounded once;
+ * partial_out (what this rank sends) carries no bias.
+ */
+mc2_status mc2_matmul_reduce_scatter_bias(const void* x, const void* x2, int world_size, int rank_id, int64_t m,
+                                          int64_t k, int64_t n, int x2_trans, mc2_dtype dtype,
+                                          const void* const* recv, const void* bias, void* out, void* partial_out,
+                                          void* stream);
+
+/*
+ * Bias gradient of the tensor-parallel linear layer -- hyper_parallel mc2.py,
+ * AllGatherMatmulFunction.backward (grad_bias = grad_out.sum(dim=0)) and
+ * MatmulReduceScatterFunction.backward (the same over the gathered
+ * grad_out_full, i.e. gather_out of the backward's AllGatherMatmul):
+ *   grad_bias[j] = round( sum over i < m of dy[i][j] )
+ * dy (m, n) row-major of `dtype` (F16 / BF16), grad_bias (n) of `dtype`.
+ * The sum runs in fp64 and is rounded once: exact, hence independent of the
+ * summation order, whenever a column's values span fewer than about
+ * 53 - 11 - log2(m) binades.
+ */
+mc2_status mc2_bias_grad(const void* dy, int64_t m, int64_t n, mc2_dtype dtype, void* grad_bias, void* stream);
 
 /*
  * Column-parallel backward, weight gradient -- hyper_parallel mc2.py,

@@ -31,7 +31,7 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     names = _declared()
-    assert len(names) == 13, names
+    assert len(names) == 16, names
     for n in names:
         assert hasattr(lib, n), n
 
