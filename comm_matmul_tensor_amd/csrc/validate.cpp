@@ -39,7 +39,7 @@ mc2_status check_allgather_matmul(const void* const* shards, int world_size, int
   if (k < 256 || k >= 65535)
     return fail(MC2_ERR_SHAPE, "allgather_matmul: k must lie in [256, 65535), got " + str(k));
   if (m_local < 1 || n < 1) return fail(MC2_ERR_SHAPE, "allgather_matmul: empty m_local or n");
-  if ((int64_t)world_size * m_local > INT32_MAX || n > INT32_MAX)
+  if (m_local > INT32_MAX / world_size || n > INT32_MAX)
     return fail(MC2_ERR_SHAPE, "allgather_matmul: m or n above INT32_MAX");
   // input and x2 are FLOAT16 or BFLOAT16, of the same type ("parameters")
   if (!is_half(dtype)) return fail(MC2_ERR_DTYPE, "allgather_matmul: dtype must be F16 or BF16");
@@ -138,7 +138,7 @@ mc2_status check_alltoall_sizes(int rank_size, int64_t bs, int64_t h, int64_t n)
     return fail(MC2_ERR_SHAPE, "alltoall_quant_matmul: bs must be divisible by rank_size");
   if (bs > INT32_MAX || n > INT32_MAX)
     return fail(MC2_ERR_SHAPE, "alltoall_quant_matmul: bs and n must not exceed INT32_MAX");
-  const int64_t kk = (int64_t)rank_size * h;
+  const int64_t kk = h > 35000 ? 35001 : (int64_t)rank_size * h;  // no overflow for huge h
   if (kk > 35000 || kk % 16 != 0)
     return fail(MC2_ERR_SHAPE, "alltoall_quant_matmul: rank_size*h must be a multiple of 16 in [1, 35000], got " + str(kk));
   return MC2_OK;
@@ -196,6 +196,7 @@ static mc2_status check_quant_reduce(const char* op, const void* const* x, const
     if (!x[i] || !scales[i]) return fail(MC2_ERR_NULL, o + "x or scales of rank " + str(i) + " is NULL");
   // no empty tensors; H in [1024, 8192] and 128-aligned ("constraints")
   if (rows < 1) return fail(MC2_ERR_SHAPE, o + "empty tensor");
+  if (rows > INT32_MAX) return fail(MC2_ERR_SHAPE, o + "rows above INT32_MAX");
   if (h < 1024 || h > 8192 || h % 128 != 0)
     return fail(MC2_ERR_SHAPE, o + "h must be a multiple of 128 in [1024, 8192], got " + str(h));
   // E8M0 scales go with E4M3FN / E5M2 x (mx); FLOAT scales with INT8,
