@@ -112,3 +112,12 @@ def from_torch(t) -> np.ndarray:
             (hasattr(torch, "float8_e8m0fnu") and t.dtype == torch.float8_e8m0fnu):
         return t.view(torch.uint8).numpy()
     return t.numpy()
+
+
+def pack_int4(codes: np.ndarray) -> np.ndarray:
+    """Storage of int4 inputs: codes (-8..7) along the last dimension (even length) two per
+    byte, value 2i in the low nibble of byte i and value 2i + 1 in the high nibble."""
+    c = np.asarray(codes).astype(np.int16)
+    assert c.shape[-1] % 2 == 0 and c.min(initial=0) >= -8 and c.max(initial=0) <= 7
+    u = (c & 0xF).astype(np.uint8)
+    return np.ascontiguousarray(u[..., 0::2] | (u[..., 1::2] << 4))

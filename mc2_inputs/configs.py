@@ -34,6 +34,12 @@ shapes:
 8 ``rs_dx``       MatmulReduceScatter completing the column-parallel dX: dY bf16
                   (8192, 1792), W bf16 (1792, 4096) with std 0.02, blocks
                   (1024, 4096) with std 0.85 (rank 0).
+9 ``a16w4``       AlltoAllQuantMatmul A16W4: ``a16w8``'s tensors with int4 weight
+                  codes U{-8..7} (32768, 7168), stored two per byte (pack_int4).
+10 ``a4w4``       AlltoAllQuantMatmul A4W4 (full quantisation): x1 int4 codes
+                  U{-8..7} (8192, 4096), one fp32 scale per permuted token in
+                  U(0.5, 0.7) (absmax / 7 of a unit-normal row is about 0.64),
+                  int4 weight codes as in ``a16w4``, scales and bias as ``a8w8``.
 """
 from __future__ import annotations
 
@@ -77,6 +83,23 @@ def _a8w8(r, bs, h, n):
         "x2_scale": TensorSpec(3, (n,), "uniform", 1e-3, 1e-2, "f32"),
         "bias": TensorSpec(4, (n,), "normal", 0.0, 1.0, "bf16"),
     }
+
+
+def _a16w4(r, bs, h, n):
+    """A16W8's tensors with int4 weight codes (-8..7); pack_int4 stores them two per byte."""
+    specs = _a16w8(r, bs, h, n)
+    specs["x2"] = TensorSpec(2, (r * h, n), "int", -8, 7, "i8")
+    return specs
+
+
+def _a4w4(r, bs, h, n):
+    """Full-quantisation tensors with int4 activation and weight codes (-8..7) and
+    per-token activation scales of about absmax / 7 of a unit-normal row."""
+    specs = _a8w8(r, bs, h, n)
+    specs["x1"] = TensorSpec(0, (bs, h), "int", -8, 7, "i8")
+    specs["x1_scale"] = TensorSpec(1, (bs // r,), "uniform", 0.5, 0.7, "f32")
+    specs["x2"] = TensorSpec(2, (r * h, n), "int", -8, 7, "i8")
+    return specs
 
 
 def _rs(r, m, k, n, x2_trans, w_std=0.02):
@@ -128,6 +151,8 @@ CONFIGS: Dict[str, tuple] = {
                _rs(8, 4096, 1792, 4096, True)),
     "rs_dx": (8, {"r": 8, "rank": 0, "m": 8192, "k": 1792, "n": 4096, "x2_trans": False},
               _rs(8, 8192, 1792, 4096, False)),
+    "a16w4": (9, {"r": 8, "bs": 8192, "h": 4096, "n": 7168}, _a16w4(8, 8192, 4096, 7168)),
+    "a4w4": (10, {"r": 8, "bs": 8192, "h": 4096, "n": 7168}, _a4w4(8, 8192, 4096, 7168)),
 }
 
 
@@ -140,6 +165,10 @@ def scaled(kind: str, **dims):
         return _a16w8(dims["r"], dims["bs"], dims["h"], dims["n"])
     if kind == "a8w8":
         return _a8w8(dims["r"], dims["bs"], dims["h"], dims["n"])
+    if kind == "a16w4":
+        return _a16w4(dims["r"], dims["bs"], dims["h"], dims["n"])
+    if kind == "a4w4":
+        return _a4w4(dims["r"], dims["bs"], dims["h"], dims["n"])
     if kind == "rs":
         return _rs(dims["r"], dims["m"], dims["k"], dims["n"], dims["x2_trans"], dims.get("w_std", 0.02))
     if kind == "bwd":

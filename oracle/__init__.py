@@ -56,6 +56,7 @@ def _load():
             "orc_matmul_reduce_scatter": (None, [P, P, INT, INT, INT, I64, I64, I64, P, INT, P, P]),
             "orc_permute": (None, [P, INT, I64, I64, P]),
             "orc_add_bias": (None, [P, P, I64, I64, INT]),
+            "orc_unpack_int4": (None, [P, I64, P]),
             "orc_bias_grad": (None, [P, I64, I64, INT, P]),
             "orc_smooth_quant": (None, [P, I64, I64, P, INT, P, P]),
             "orc_int8_matmul": (I64, [P, P, I64, I64, I64, P]),
@@ -163,6 +164,29 @@ def matmul_grad_weight(dy: np.ndarray, ag_x: np.ndarray, dtype: str = "bf16") ->
 
 
 # ---------------------------------------------------------------- AlltoAllQuantMatmul
+def unpack_int4(packed: np.ndarray) -> np.ndarray:
+    """(..., c) bytes holding two int4 codes each -> (..., 2c) int8 codes (low nibble first)."""
+    packed = np.ascontiguousarray(packed).view(np.uint8)
+    out = np.empty(packed.shape[:-1] + (2 * packed.shape[-1],), dtype=np.int8)
+    _load().orc_unpack_int4(_ptr(packed), out.size, _ptr(out))
+    return out
+
+
+def alltoall_quant_matmul_a16w4(x1, r: int, x2_packed, x2_scale, smooth=None, bias=None,
+                                dtype: str = "bf16") -> Dict[str, np.ndarray]:
+    """A16W4: the dynamic per-token chain of alltoall_quant_matmul with the int4 weight
+    (rank_size h, n / 2 bytes) unpacked to its codes."""
+    return alltoall_quant_matmul(x1, r, unpack_int4(x2_packed), x2_scale, smooth, bias, dtype)
+
+
+def alltoall_quant_matmul_a4w4(x1_packed, r: int, x1_scale, x2_packed, x2_scale, bias=None,
+                               dtype: str = "bf16") -> Dict[str, np.ndarray]:
+    """A4W4: the full-quantisation chain of alltoall_quant_matmul_static with the int4
+    activations (bs, h / 2 bytes) and weight (rank_size h, n / 2 bytes) unpacked."""
+    return alltoall_quant_matmul_static(unpack_int4(x1_packed), r, x1_scale, unpack_int4(x2_packed), x2_scale, bias,
+                                        dtype)
+
+
 def add_bias(y: np.ndarray, bias: np.ndarray, dtype: str) -> np.ndarray:
     """round(y + bias) per row: the listing's `out = out + bias` after the fused op."""
     out = np.array(y, dtype=_STORAGE[dtype], copy=True, order="C")

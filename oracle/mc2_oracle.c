@@ -585,6 +585,25 @@ int orc_quant_reduce_scatter(const void* const* x, const void* const* scales, in
 }
 
 /* ------------------------------------------------------------------------ */
+/* [A2A] int4 operands of A16W4 / A4W4.                                      */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * The constraints of the AlltoAllQuantMatmul page require N even for A16W4
+ * and H and N even for A4W4, which fits two 4-bit codes per byte along the
+ * last dimension.  Reading taken: two's-complement int4 codes (-8..7), value
+ * 2i of a row in the low nibble of byte i and value 2i + 1 in the high
+ * nibble.  n_values (even) codes from n_values / 2 bytes.
+ */
+void orc_unpack_int4(const uint8_t* packed, int64_t n_values, int8_t* out) {
+  for (int64_t i = 0; i < n_values / 2; i++) {
+    const int lo = packed[i] & 0xF, hi = packed[i] >> 4;
+    out[2 * i] = (int8_t)(lo >= 8 ? lo - 16 : lo);
+    out[2 * i + 1] = (int8_t)(hi >= 8 ? hi - 16 : hi);
+  }
+}
+
+/* ------------------------------------------------------------------------ */
 /* Array forms of the format routines (for the format tests).               */
 /* ------------------------------------------------------------------------ */
 int orc_decode_array(int dtype, int64_t n, const void* in, double* out) {

@@ -645,3 +645,42 @@ def test_column_parallel_layer_with_bias_equals_unsharded_linear():
         outs.append(oracle.add_bias(o, e(b[j * n_l:(j + 1) * n_l]), "bf16"))
     full = np.concatenate(xs) @ W.T + b
     assert np.array_equal(np.concatenate(outs, axis=1), e(full))
+
+
+# ----------------------------------------------------------------- int4 operands (A16W4 / A4W4)
+def test_unpack_int4_every_byte():
+    """Each byte splits into the unique pair of int4 codes lo, hi in [-8, 7] with
+    lo = byte (mod 16) and hi = byte / 16 (mod 16): its two's-complement nibbles."""
+    b = np.arange(256, dtype=np.uint8)
+    u = oracle.unpack_int4(b.reshape(1, 256)).reshape(256, 2).astype(np.int64)
+    lo, hi = u[:, 0], u[:, 1]
+    assert lo.min() == -8 and lo.max() == 7 and hi.min() == -8 and hi.max() == 7
+    assert np.array_equal(lo % 16, b.astype(np.int64) % 16) and np.array_equal(hi % 16, b.astype(np.int64) // 16)
+    assert len({(int(x), int(y)) for x, y in u}) == 256
+
+
+def test_unpack_int4_order_and_generator_round_trip():
+    """The reading's order (value 2i in the low nibble, 2i + 1 in the high one) on
+    hand-written bytes, and the generator's packing inverts the oracle's unpacking."""
+    got = oracle.unpack_int4(np.array([[0x21, 0xF8, 0x7F, 0x80]], np.uint8))
+    assert got.tolist() == [[1, 2, -8, -1, -1, 7, 0, -8]]
+    codes = mc2_inputs.fill(7, 3, "int", -8, 7, "i8", (37, 64))
+    assert np.array_equal(oracle.unpack_int4(mc2_inputs.pack_int4(codes)), codes)
+
+
+def test_a16w4_and_a4w4_chains_vs_numpy_int64():
+    """The int4 chains: accumulators equal numpy's int64 product of the permuted codes
+    (A4W4) or the quantised tokens (A16W4) with the unpacked weight."""
+    r, bs, h, n = 4, 32, 64, 24
+    t = mc2_inputs.make(mc2_inputs.configs.scaled("a16w4", r=r, bs=bs, h=h, n=n), seed=61)
+    w_packed = mc2_inputs.pack_int4(t["x2"])
+    res = oracle.alltoall_quant_matmul_a16w4(t["x1"], r, w_packed, t["x2_scale"], t["x1_smooth"], t["bias"])
+    q, s1 = oracle.smooth_quant(oracle.permute(t["x1"], r), t["x1_smooth"])
+    assert np.array_equal(res["q"], q) and np.array_equal(res["s1"], s1)
+    assert np.array_equal(res["acc"], q.astype(np.int64) @ t["x2"].astype(np.int64))
+    t = mc2_inputs.make(mc2_inputs.configs.scaled("a4w4", r=r, bs=bs, h=h, n=n), seed=62)
+    res = oracle.alltoall_quant_matmul_a4w4(mc2_inputs.pack_int4(t["x1"]), r, t["x1_scale"],
+                                            mc2_inputs.pack_int4(t["x2"]), t["x2_scale"], t["bias"])
+    p = t["x1"].reshape(r, bs // r, h).transpose(1, 0, 2).reshape(bs // r, r * h).astype(np.int64)
+    assert np.array_equal(res["acc"], p @ t["x2"].astype(np.int64))
+    assert np.array_equal(res["out"], oracle.dequant(res["acc"], t["x1_scale"], t["x2_scale"], t["bias"]))
