@@ -3,11 +3,14 @@
 // commOut.permute(1, 0, 2).view(BS/rankSize, rankSize*H), then
 // Quant(permutedOut * x1Scale)).
 //
-// One workgroup per token t.  The permute is pure addressing: row t of P is
-// the concatenation over ranks j of x1 row j*(bs/r) + t, so consecutive
-// threads read consecutive 16-byte chunks of the r source rows (coalesced)
-// and nothing is written for P unless the caller asks for it.  The token's
-// values stay in registers between the two passes:
+// The permute is pure addressing: row t of P is the concatenation over ranks
+// j of x1 row j*(bs/r) + t, so consecutive threads read consecutive 16-byte
+// chunks of the r source rows (coalesced) and nothing is written for P
+// unless the caller asks for it.  Two kernels: permute_quant_pipe, a
+// persistent grid that walks the tokens with the next tokens' loads in
+// flight (h % 8 == 0, no permuted copy: the usual case), and one workgroup
+// per token otherwise.  A token's values stay in registers between the two
+// passes:
 //   pass 1  y = P * smooth in fp32 (exact: two 8- or 11-bit significands),
 //           absmax over the row (wavefront then workgroup reduction; max is
 //           exact in any order)
@@ -173,6 +176,129 @@ __global__ __launch_bounds__(kVecThreads, 2) void permute_quant_vec(QuantArgs a)
   }
 }
 
+// Pipelined path (h % 8 == 0, no permuted_out copy): a persistent grid, one
+// 1024-thread workgroup per CU, walks the tokens t = b, b + G, ...  Thread x
+// owns the 16-byte column chunks x, x + 1024, ... (C of them) of every
+// token, so its smoothing factors are loaded once and stay in registers, and
+// the loads of the next D - 1 tokens are in flight while the current token
+// is reduced, quantised and stored (with one token per workgroup every
+// workgroup loaded, then reduced, then stored, and the loads came in
+// bursts).  y = P * smooth is recomputed from the raw values in the second
+// pass instead of being kept.  One barrier per token: the per-wavefront
+// maxima go to a slot of `red` that alternates between tokens.
+//
+// The loads are non-temporal buffer loads (x1 below 2 GiB): a 32-bit offset
+// per chunk and the token's row offset as a scalar.  Every load is issued
+// unconditionally -- chunks past the row's end re-load the last chunk
+// (neither counted nor stored), and loads past the workgroup's last token
+// re-load that token (an L2 hit) -- so no branch separates a load from its
+// use and the compiler waits only for the token being processed.
+constexpr int kPipeThreads = 1024;
+constexpr int kMaxChunks = 5;    // 16-byte chunks per thread: r*h <= 5 * 8 * 1024 = 40960
+// Cache policy of the x1 loads: non-temporal.  x1 is read exactly once, and
+// streaming it past the caches keeps it from evicting the dirty lines other
+// kernels left there (each such eviction is a write-back in the middle of
+// this kernel): 40.0 -> 27.5 us after a 512 MB write, 23.0 -> 26.0 us warm.
+constexpr int kLoadNT = 2;
+
+// D: tokens whose loads are in flight per workgroup (3 for up to 3 chunks per
+// thread, 2 above, where a third set of buffers would spill registers)
+template <int DT, int C, bool FULL, int D = (C <= 3 ? 3 : 2)>
+__global__ __launch_bounds__(kPipeThreads, 1) void permute_quant_pipe(QuantArgs a) {
+  __shared__ float red[2][kPipeThreads / 64];
+  const int64_t T = a.bs / a.r, h = a.h;
+  const int64_t cols = (int64_t)a.r * h;
+  const int chunks = (int)(cols / 8);
+  const uint16_t* sm = static_cast<const uint16_t*>(a.smooth);
+  const __amdgpu_buffer_rsrc_t rsrc =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(a.x1), (short)0, (int)(a.bs * h * 2), 0x00020000);
+  // chunk i of this thread: P elements [8 ch, 8 ch + 8) = source row j T + t, columns [c, c + 8)
+  uint32_t voff[C];
+  u32x4 smr[C];
+  bool valid[C];
+  const uint32_t one2 = DT == DT_BF16 ? 0x3F803F80u : 0x3C003C00u;  // two 16-bit ones
+#pragma unroll
+  for (int i = 0; i < C; i++) {
+    const int ch = (int)threadIdx.x + i * kPipeThreads;
+    valid[i] = FULL || ch < chunks;
+    const int64_t e = (int64_t)(valid[i] ? ch : chunks - 1) * 8, j = e / h, c = e - j * h;
+    voff[i] = (uint32_t)((j * T * h + c) * 2);
+    smr[i] = sm ? *reinterpret_cast<const u32x4*>(sm + e) : u32x4{one2, one2, one2, one2};
+  }
+  const int G = (int)gridDim.x;
+  const int n_my = (int)((T - blockIdx.x + G - 1) / G);  // tokens of this workgroup, >= 1
+  u32x4 buf[D][C];
+  auto issue = [&](u32x4 (&b)[C], int k) {
+    const int64_t t = blockIdx.x + (int64_t)(k < n_my ? k : n_my - 1) * G;
+    const int soff = (int)(t * h * 2);
+#pragma unroll
+    for (int i = 0; i < C; i++)
+      b[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rsrc, (int)voff[i], soff, kLoadNT));
+  };
+  auto yval = [&](const u32x4& raw, const u32x4& s, int k) {
+    float y = dec16<DT>(raw[k / 2] >> (16 * (k & 1)));
+    return y * dec16<DT>(s[k / 2] >> (16 * (k & 1)));
+  };
+  constexpr float kMagic = 12582912.0f;  // 1.5 * 2^23
+  auto process = [&](const u32x4 (&b)[C], int k) {
+    const int64_t t = blockIdx.x + (int64_t)k * G;
+    float amax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < C; i++) {
+      float cm = 0.0f;
+#pragma unroll
+      for (int e = 0; e < 8; e++) cm = fmaxf(cm, __builtin_fabsf(yval(b[i], smr[i], e)));
+      amax = fmaxf(amax, valid[i] ? cm : 0.0f);
+    }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 64));
+    float* slot = red[k & 1];
+    if (threadIdx.x % 64 == 0) slot[threadIdx.x / 64] = amax;
+    __syncthreads();
+    amax = slot[0];
+#pragma unroll
+    for (int w = 1; w < kPipeThreads / 64; w++) amax = fmaxf(amax, slot[w]);
+    const float s = amax / 127.0f;
+    if (threadIdx.x == 0) a.s1[t] = s;
+    const float inv = 1.0f / s;
+    const bool fast = s >= 1.17549435e-38f;  // see the bound above permute_quant_vec
+    const bool nonzero = amax > 0.0f;
+#pragma unroll
+    for (int i = 0; i < C; i++) {
+      float dmax = 0.0f;
+      uint32_t mb[8];
+#pragma unroll
+      for (int e = 0; e < 8; e++) {
+        const float qa = yval(b[i], smr[i], e) * inv;
+        const float m = __builtin_amdgcn_fmed3f(qa, -127.0f, 127.0f) + kMagic;
+        dmax = fmaxf(dmax, __builtin_fabsf(qa - (m - kMagic)));
+        mb[e] = __float_as_uint(m);
+      }
+      if (nonzero && (!fast || dmax >= 0.49997f)) {  // rare: redo this chunk with the IEEE division
+#pragma unroll
+        for (int e = 0; e < 8; e++) mb[e] = (uint32_t)quant1(yval(b[i], smr[i], e), s);
+      }
+      u32x2 qv;
+#pragma unroll
+      for (int w = 0; w < 2; w++)
+        qv[w] = (__builtin_amdgcn_perm(mb[4 * w + 3], mb[4 * w + 2], 0x0c0c0400u) << 16) |
+                __builtin_amdgcn_perm(mb[4 * w + 1], mb[4 * w], 0x0c0c0400u);
+      if (!nonzero) qv = u32x2{0u, 0u};  // an all-zero token: s = 0, codes 0
+      if (valid[i]) *reinterpret_cast<u32x2*>(a.q + t * cols + ((int64_t)threadIdx.x + i * kPipeThreads) * 8) = qv;
+    }
+  };
+#pragma unroll
+  for (int d = 0; d < D; d++) issue(buf[d], d);
+  for (int k0 = 0;; k0 += D) {
+#pragma unroll
+    for (int d = 0; d < D; d++) {
+      process(buf[d], k0 + d);
+      issue(buf[d], k0 + d + D);
+      if (k0 + d + 1 == n_my) return;
+    }
+  }
+}
+
 // General path (h not a multiple of 16): element by element, two passes
 // over global memory.  Same arithmetic as the vector path.
 template <int DT>
@@ -214,12 +340,43 @@ void launch_vec(const QuantArgs& a, int units_per_thread, hipStream_t s) {
   }
 }
 
+template <int DT, int C>
+void launch_pipe_c(const QuantArgs& a, bool full, unsigned grid, hipStream_t s) {
+  if (full) permute_quant_pipe<DT, C, true><<<grid, kPipeThreads, 0, s>>>(a);
+  else permute_quant_pipe<DT, C, false><<<grid, kPipeThreads, 0, s>>>(a);
+}
+
+template <int DT>
+void launch_pipe(const QuantArgs& a, int chunks_per_thread, hipStream_t s) {
+  const int64_t T = a.bs / a.r;
+  const unsigned grid = (unsigned)(T < 256 ? T : 256);
+  const bool full = (int64_t)a.r * a.h == (int64_t)chunks_per_thread * kPipeThreads * 8;
+  switch (chunks_per_thread) {
+    case 1: launch_pipe_c<DT, 1>(a, full, grid, s); break;
+    case 2: launch_pipe_c<DT, 2>(a, full, grid, s); break;
+    case 3: launch_pipe_c<DT, 3>(a, full, grid, s); break;
+    case 4: launch_pipe_c<DT, 4>(a, full, grid, s); break;
+    default: launch_pipe_c<DT, kMaxChunks>(a, full, grid, s); break;
+  }
+}
+
 }  // namespace
 
 hipError_t launch_permute_quant(const QuantArgs& a, hipStream_t s) {
   const int64_t T = a.bs / a.r;
   const int64_t cols = (int64_t)a.r * a.h;
   if (T < 1 || cols < 1) return hipErrorInvalidValue;
+  // pipelined path for h % 8 == 0 without the permuted copy; above 4 chunks
+  // per thread (r h > 32768) it would spill a few registers, so rows that
+  // split into 16-element units take the one-token-per-workgroup path there
+  const int cpt = (int)((cols / 8 + kPipeThreads - 1) / kPipeThreads);
+  if (a.h % 8 == 0 && cpt <= kMaxChunks && (cpt <= 4 || a.h % 16 != 0) && !a.permuted &&
+      a.bs * a.h * 2 < ((int64_t)1 << 31)) {
+    if (a.dtype == DT_BF16) launch_pipe<DT_BF16>(a, cpt, s);
+    else if (a.dtype == DT_F16) launch_pipe<DT_F16>(a, cpt, s);
+    else return hipErrorInvalidValue;
+    return hipGetLastError();
+  }
   // vector path when rows split into whole 16-element units and fit 3 units per thread
   const bool vec = a.h % 16 == 0 && cols <= (int64_t)kMaxUnits * kVecThreads * 16;
   const int upt = (int)((cols / 16 + kVecThreads - 1) / kVecThreads);

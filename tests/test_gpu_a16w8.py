@@ -22,7 +22,7 @@ def mc2():
     return m
 
 
-def _run(mc2, r, bs, h, n, dtype="bf16", smooth=True, bias=True, seed=0, debug=True):
+def _run(mc2, r, bs, h, n, dtype="bf16", smooth=True, bias=True, seed=0, debug=True, permuted=True):
     import torch
     specs = mc2_inputs.configs.scaled("a16w8", r=r, bs=bs, h=h, n=n)
     for key in ("x1", "x1_smooth", "bias"):
@@ -34,10 +34,11 @@ def _run(mc2, r, bs, h, n, dtype="bf16", smooth=True, bias=True, seed=0, debug=T
     tdt = torch.bfloat16 if dtype == "bf16" else torch.float16
     dbg = {}
     if debug:
-        dbg = dict(permuted_out=torch.empty((rows, cols), dtype=tdt, device="cuda"),
-                   q_out=torch.empty((rows, cols), dtype=torch.int8, device="cuda"),
+        dbg = dict(q_out=torch.empty((rows, cols), dtype=torch.int8, device="cuda"),
                    x1_scale_out=torch.empty((rows,), dtype=torch.float32, device="cuda"),
                    acc_out=torch.empty((rows, n), dtype=torch.int32, device="cuda"))
+        if permuted:
+            dbg["permuted_out"] = torch.empty((rows, cols), dtype=tdt, device="cuda")
     sm = T(t["x1_smooth"], dtype) if smooth else None
     b = T(t["bias"], dtype) if bias else None
     out = mc2.mc2_alltoall_quant_matmul(T(t["x1"], dtype), r, T(t["x2"], "i8"), T(t["x2_scale"], "f32"), sm, b,
@@ -58,6 +59,24 @@ def test_a16w8_shapes(mc2, r, bs, h, n, dtype):
     print(f"a16w8 r={r} bs={bs} h={h} n={n} {dtype}", flush=True)
     got, ref = _run(mc2, r, bs, h, n, dtype, seed=r + bs + h + n)
     assert_bits_equal(got["permuted"], ref["permuted"], "permuted")
+    assert_bits_equal(got["s1"], ref["s1"], "x1_scale")
+    assert_bits_equal(got["q"], ref["q"], "q")
+    assert_bits_equal(got["acc"], ref["acc"], "acc")
+    assert_close16(got["out"], ref["out"], dtype, "out")
+
+
+# Without the permuted copy the quantisation runs on the pipelined path (a
+# persistent grid of at most 256 workgroups walking the tokens, C 16-byte
+# chunks per thread).  Cases: C = 1..5, every thread's chunks whole (r h a
+# multiple of 8192) or not, fewer tokens than workgroups, and tokens that do
+# not divide evenly over 256 workgroups (1 to 3 per workgroup).
+@pytest.mark.parametrize("r,bs,h,n,dtype", [
+    (2, 2, 256, 16, "bf16"), (2, 20, 8, 24, "f16"), (8, 8 * 300, 512, 64, "bf16"), (4, 4 * 700, 2048, 32, "bf16"),
+    (8, 8 * 40, 3072, 48, "f16"), (8, 8 * 600, 2560, 16, "bf16"), (4, 4 * 513, 4096, 16, "bf16"),
+    (8, 8 * 520, 4104, 16, "bf16"), (8, 8 * 9, 4104, 40, "f16")])
+def test_a16w8_pipelined_quant(mc2, r, bs, h, n, dtype):
+    print(f"a16w8 pipelined r={r} bs={bs} h={h} n={n} {dtype}", flush=True)
+    got, ref = _run(mc2, r, bs, h, n, dtype, seed=11 + r + bs + h, permuted=False)
     assert_bits_equal(got["s1"], ref["s1"], "x1_scale")
     assert_bits_equal(got["q"], ref["q"], "q")
     assert_bits_equal(got["acc"], ref["acc"], "acc")
