@@ -16,9 +16,14 @@ this order (names as in the JSON "rows"):
                then int8 (1024, 32768) @ (32768, 7168) with per-token x per-channel dequant + bias
   a8w8         AlltoAllQuantMatmul, full quantisation: int8 (8192, 4096) on 8 ranks with
                per-token scales, the permute folded into the int8 GEMM's loads, same GEMM
+  a16w4        AlltoAllQuantMatmul A16W4: the a16w8 chain with an int4 weight (32768, 7168), two codes per byte
+  a4w4         AlltoAllQuantMatmul A4W4 (full quantisation): int4 (8192, 4096) on 8 ranks with per-token
+               scales, int4 weight (32768, 7168)
   qar_int8     QuantAllReduce, 8 ranks x int8 (4, 2048, 7168) + fp32 group-128 scales -> fp32
   qar_mx       QuantAllReduce, 8 ranks x E4M3FN (4, 2048, 7168) + E8M0 mx scales -> bf16
   qrs_int8     QuantReduceScatter, rank 3's share of the qar_int8 workload: 1024 of 8192 rows -> fp32
+  ag_tiny      the AllGatherMatmul page's example: 8 x fp16 (16, 512) @ (512, 64) (launch-latency bound;
+               its microseconds per call are the figure)
 
 Inputs are generated on the host, copied to HBM before timing, and stay
 resident.  --copy-calib adds a plain 256 MiB device copy to every step (the
@@ -31,8 +36,10 @@ which libmc2 is handed); each row reports their mean (the roofline figure),
 minimum and median.  Every step runs all rows, so each call finds the caches
 holding the other rows' data (largely dirty outputs), not its own inputs.
 The headline value is the AllGatherMatmul's TFLOP/s; every row's figure and
-its roofline fraction are in "rows".  The oracle (CPU) is timed on a bounded
-sample of the AllGatherMatmul workload for the "cpu_baseline" entry.
+its roofline fraction are in "rows".  The oracle (CPU) is timed on bounded
+samples of the AllGatherMatmul, A16W8, backward and QuantAllReduce workloads
+and on the page's example for the "cpu_baseline" entry (with the CPU model,
+thread count and GPU / oracle ratios).
 """
 from __future__ import annotations
 
@@ -50,8 +57,8 @@ PEAK_BF16 = 2500.0     # TFLOP/s, dense MFMA, MI355X
 PEAK_INT8 = 5000.0     # TOP/s, dense MFMA, MI355X
 PEAK_HBM = 8000.0      # GB/s, MI355X HBM3E
 
-ALL_ROWS = ["ag_bf16_tp", "ag_arrival", "colpar_dx", "colpar_dw", "rs_fwd", "rs_dx", "a16w8", "a8w8", "qar_int8",
-            "qar_mx", "qrs_int8"]
+ALL_ROWS = ["ag_bf16_tp", "ag_arrival", "colpar_dx", "colpar_dw", "rs_fwd", "rs_dx", "a16w8", "a8w8", "a16w4",
+            "a4w4", "qar_int8", "qar_mx", "qrs_int8", "ag_tiny"]
 EXTRA_ROWS = ["copy_calib"]
 COPY_CALIB_BYTES = 256 << 20
 
@@ -192,6 +199,40 @@ def setup_rows(names, mc2, torch):
         row.bytes = bs * h + 4 * rows_ + cols * n + 4 * n + 2 * n + 2 * rows_ * n
         row.check = lambda t=t, d=d, out=out: check_a8w8(t, d, out)
         rows[row.name] = row
+    if "a16w4" in names:
+        seed, d, specs = mc2_inputs.CONFIGS["a16w4"]
+        t = mc2_inputs.make("a16w4")
+        r, bs, h, n = d["r"], d["bs"], d["h"], d["n"]
+        x1 = T(t["x1"], "bf16")
+        x2 = torch.from_numpy(mc2_inputs.pack_int4(t["x2"])).cuda()
+        s2, sm, bias = T(t["x2_scale"], "f32"), T(t["x1_smooth"], "bf16"), T(t["bias"], "bf16")
+        rows_, cols = bs // r, r * h
+        out = torch.empty((rows_, n), dtype=torch.bfloat16, device="cuda")
+        ws = torch.empty(mc2.mc2_alltoall_quant_matmul_a16w4_workspace_size(r, bs, h, n), dtype=torch.uint8,
+                         device="cuda")
+        row = Row("a16w4", "TOP/s", "mfma", PEAK_INT8, 2.0 * rows_ * cols * n,
+                  [("widen_int4+permute_quant+gemm_i8", lambda x1=x1, r=r, x2=x2, s2=s2, sm=sm, bias=bias, out=out,
+                    ws=ws: mc2.mc2_alltoall_quant_matmul_a16w4(x1, r, x2, s2, sm, bias, out=out, workspace=ws))])
+        row.bytes = 2 * bs * h + 2 * cols + cols * n // 2 + 4 * n + 2 * n + 2 * rows_ * n
+        row.check = lambda t=t, d=d, out=out: check_w4(t, d, out, "a16w4")
+        rows[row.name] = row
+    if "a4w4" in names:
+        seed, d, specs = mc2_inputs.CONFIGS["a4w4"]
+        t = mc2_inputs.make("a4w4")
+        r, bs, h, n = d["r"], d["bs"], d["h"], d["n"]
+        x1 = torch.from_numpy(mc2_inputs.pack_int4(t["x1"])).cuda()
+        x2 = torch.from_numpy(mc2_inputs.pack_int4(t["x2"])).cuda()
+        s1, s2, bias = T(t["x1_scale"], "f32"), T(t["x2_scale"], "f32"), T(t["bias"], "bf16")
+        rows_, cols = bs // r, r * h
+        out = torch.empty((rows_, n), dtype=torch.bfloat16, device="cuda")
+        ws = torch.empty(mc2.mc2_alltoall_quant_matmul_a4w4_workspace_size(r, bs, h, n), dtype=torch.uint8,
+                         device="cuda")
+        row = Row("a4w4", "TOP/s", "mfma", PEAK_INT8, 2.0 * rows_ * cols * n,
+                  [("widen_int4+gemm_i8", lambda x1=x1, r=r, s1=s1, x2=x2, s2=s2, bias=bias, out=out, ws=ws:
+                    mc2.mc2_alltoall_quant_matmul_a4w4(x1, r, s1, x2, s2, bias, out=out, workspace=ws))])
+        row.bytes = bs * h // 2 + 4 * rows_ + cols * n // 2 + 4 * n + 2 * n + 2 * rows_ * n
+        row.check = lambda t=t, d=d, out=out: check_w4(t, d, out, "a4w4")
+        rows[row.name] = row
     for name, xdt, sdt, odt in (("qar_int8", "i8", "f32", torch.float32), ("qar_mx", "e4m3fn", "e8m0", torch.bfloat16)):
         if name not in names:
             continue
@@ -226,6 +267,20 @@ def setup_rows(names, mc2, torch):
         row.bytes = nbytes
         row.check = lambda t=t, d=d, out=out, rank=rank: check_qrs(t, d, out, rank)
         rows[row.name] = row
+    if "ag_tiny" in names:
+        seed, d, specs = mc2_inputs.CONFIGS["ag_tiny"]
+        t = mc2_inputs.make("ag_tiny")
+        shards = [T(t[f"shard{i}"], "f16") for i in range(d["r"])]
+        x2 = T(t["x2"], "f16")
+        m, k, n = d["r"] * d["m_local"], d["k"], d["n"]
+        out = torch.empty((m, n), dtype=torch.float16, device="cuda")
+        g = torch.empty((m, k), dtype=torch.float16, device="cuda")
+        row = Row("ag_tiny", "TFLOP/s", "latency", PEAK_BF16, 2.0 * m * n * k,
+                  [("gemm_f16", lambda shards=shards, x2=x2, out=out, g=g:
+                    mc2.mc2_allgather_matmul(shards, x2, out=out, gather_out=g))])
+        row.bytes = 2 * (m * k + k * n + m * n + m * k)
+        row.check = lambda t=t, d=d, out=out, g=g: check_ag_tiny(t, d, out, g)
+        rows[row.name] = row
     if "copy_calib" in names:
         src = torch.empty(COPY_CALIB_BYTES, dtype=torch.uint8, device="cuda").fill_(1)
         dst = torch.empty_like(src)
@@ -259,6 +314,15 @@ def check_ag(t, d, out, g):
     got = mc2_inputs.from_torch(out)[rows]
     gat_ok = np.array_equal(mc2_inputs.from_torch(g), G)
     return bool(gat_ok and _tol16(got, want, "bf16"))
+
+
+def check_ag_tiny(t, d, out, g):
+    import mc2_inputs
+    import oracle
+    want, want_g = oracle.allgather_matmul([t[f"shard{i}"] for i in range(d["r"])], t["x2"], "f16")
+    import numpy as np
+    return bool(np.array_equal(mc2_inputs.from_torch(g).view(np.uint16), want_g.view(np.uint16)) and
+                _tol16(mc2_inputs.from_torch(out), want, "f16"))
 
 
 def check_bwd(t, res, which):
@@ -324,6 +388,25 @@ def check_a8w8(t, d, out):
     return _tol16(mc2_inputs.from_torch(out)[toks], want, "bf16")
 
 
+def check_w4(t, d, out, kind):
+    import numpy as np
+
+    import mc2_inputs
+    import oracle
+    r = d["r"]
+    rng = np.random.default_rng(5)
+    toks = np.sort(rng.choice(d["bs"] // r, 6, replace=False))
+    if kind == "a16w4":
+        q, s1 = oracle.smooth_quant(np.ascontiguousarray(oracle.permute(t["x1"], r)[toks]), t["x1_smooth"])
+    else:
+        q = np.ascontiguousarray(t["x1"].reshape(r, d["bs"] // r, d["h"]).transpose(1, 0, 2)
+                                 .reshape(d["bs"] // r, r * d["h"])[toks])
+        s1 = t["x1_scale"][toks]
+    acc = oracle.int8_matmul(q, oracle.unpack_int4(mc2_inputs.pack_int4(t["x2"])))
+    want = oracle.dequant(acc, s1, t["x2_scale"], t["bias"])
+    return _tol16(mc2_inputs.from_torch(out)[toks], want, "bf16")
+
+
 def check_qar(t, d, out, xdt, sdt):
     import numpy as np
 
@@ -362,42 +445,121 @@ def check_qrs(t, d, out, rank):
 
 
 # ---------------------------------------------------------------- CPU baseline (the oracle)
-def cpu_baseline(target_s):
-    """Oracle AllGatherMatmul on the same workload, scaled to TFLOP/s.
+def _cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
-    The sample is sized to about target_s seconds: a prefix of each shard's
-    rows if the whole workload would take longer, else the whole workload
-    repeated.
-    """
+
+def _timed(fn):
+    t0 = time.perf_counter()
+    fn()
+    return time.perf_counter() - t0
+
+
+def _scaled_run(run, full, target_s, probe):
+    """Times run(n) on a prefix of n of `full` units: a probe, then the size that takes
+    about target_s (the whole workload, repeated, if that is quicker).  Returns
+    (units per run, runs, seconds)."""
+    dt = run(probe)
+    n = int(min(full, max(probe, probe * target_s / max(dt, 1e-3))))
+    reps = 1
+    if n == full:
+        reps = max(1, int(target_s / max(run(n), 1e-3)))
+    total = sum(run(n) for _ in range(reps))
+    return n, reps, total
+
+
+def cpu_baseline(target_s, gpu_rows):
+    """The oracle, as it stands, on the host cores: the AllGatherMatmul workload (the
+    headline object), plus the A16W8, column-parallel backward and QuantAllReduce
+    workloads and the API page's example, each on a bounded sample scaled to the
+    metric's unit, with the GPU / oracle ratio."""
     import numpy as np
 
     import mc2_inputs
     import oracle
+
+    # AllGatherMatmul (8 x (512, 4096) @ (4096, 1792)): a prefix of each shard's rows
     seed, d, specs = mc2_inputs.CONFIGS["ag_bf16_tp"]
     t = mc2_inputs.make("ag_bf16_tp")
     r, k, n = d["r"], d["k"], d["n"]
+    x2 = t["x2"]
+    run = lambda rows: _timed(lambda: oracle.allgather_matmul(
+        [np.ascontiguousarray(t[f"shard{i}"][:rows]) for i in range(r)], x2, "bf16"))
+    per, reps, tot = _scaled_run(run, d["m_local"], target_s * 0.4, 64)
+    ag = 2.0 * r * per * k * n * reps / tot / 1e12
+    res = {"value": round(ag, 5), "unit": "TFLOP/s", "cores": oracle.num_threads(), "kind": "oracle",
+           "sample": f"AllGatherMatmul oracle (fp64 accumulation) on {per} of {d['m_local']} rows of each of the "
+                     f"{r} bf16 shards, k={k}, n={n}, run {reps} time(s): {tot:.1f} s wall",
+           "cpu_model": _cpu_model(), "omp_num_threads": os.environ.get("OMP_NUM_THREADS", "unset")}
+    configs = {}
 
-    def run(rows_per_shard):
-        shards = [np.ascontiguousarray(t[f"shard{i}"][:rows_per_shard]) for i in range(r)]
-        t0 = time.perf_counter()
-        oracle.allgather_matmul(shards, t["x2"], "bf16")
-        return time.perf_counter() - t0
+    # A16W8 (permute + quant + int8 GEMM + dequant): a prefix of the tokens
+    seed, d, specs = mc2_inputs.CONFIGS["a16w8"]
+    t = mc2_inputs.make("a16w8")
+    ra, bs, h, na = d["r"], d["bs"], d["h"], d["n"]
+    rows_all = bs // ra
+    p_all = oracle.permute(t["x1"], ra)
 
-    probe = 8
-    dt = run(probe)
-    per_shard = int(min(d["m_local"], max(probe, probe * target_s / max(dt, 1e-3))))
-    reps = 1
-    if per_shard == d["m_local"]:
-        once = run(per_shard)
-        reps = max(1, int(target_s / max(once, 1e-3)))
-    total = 0.0
-    for _ in range(reps):
-        total += run(per_shard)
-    flops = 2.0 * r * per_shard * k * n * reps
-    return {"value": round(flops / total / 1e12, 5), "unit": "TFLOP/s", "cores": oracle.num_threads(),
-            "kind": "oracle",
-            "sample": f"AllGatherMatmul oracle (fp64 accumulation) on {per_shard} of {d['m_local']} rows of each of "
-                      f"the {r} bf16 shards, k={k}, n={n}, run {reps} time(s): {total:.1f} s wall"}
+    def a16(tok):
+        q, s1 = oracle.smooth_quant(np.ascontiguousarray(p_all[:tok]), t["x1_smooth"])
+        oracle.dequant(oracle.int8_matmul(q, t["x2"]), s1, t["x2_scale"], t["bias"])
+    per, reps, tot = _scaled_run(lambda tok: _timed(lambda: a16(tok)), rows_all, target_s * 0.25, 16)
+    v = 2.0 * per * ra * h * na * reps / tot / 1e12
+    configs["a16w8"] = {"value": round(v, 5), "unit": "TOP/s", "sample": f"{per} of {rows_all} tokens, {reps} run(s), "
+                        f"{tot:.1f} s (quantisation, exact int8 GEMM, exact dequant)"}
+
+    # column-parallel backward dX = dY @ W and dW = dY^T @ AG(X): a prefix of the rows / columns
+    seed, d, specs = mc2_inputs.CONFIGS["colpar_bwd"]
+    t = mc2_inputs.make("colpar_bwd")
+    m, nl, kk = d["m"], d["n_local"], d["k"]
+    per, reps, tot = _scaled_run(lambda rows: _timed(lambda: oracle.matmul(
+        np.ascontiguousarray(t["dy"][:rows]), t["w"], "bf16")), m, target_s * 0.15, 256)
+    configs["colpar_dx"] = {"value": round(2.0 * per * nl * kk * reps / tot / 1e12, 5), "unit": "TFLOP/s",
+                            "sample": f"{per} of {m} rows of dY, {reps} run(s), {tot:.1f} s"}
+    per, reps, tot = _scaled_run(lambda cols: _timed(lambda: oracle.matmul(
+        np.ascontiguousarray(t["dy"][:, :cols]), t["ag_x"], "bf16", a_trans=True)), nl, target_s * 0.1, 64)
+    configs["colpar_dw"] = {"value": round(2.0 * per * m * kk * reps / tot / 1e12, 5), "unit": "TFLOP/s",
+                            "sample": f"{per} of {nl} rows of dW, {reps} run(s), {tot:.1f} s"}
+
+    # QuantAllReduce int8 + fp32 groups -> fp32: a prefix of the rows (bytes as the GPU row counts them)
+    for name, xdt, sdt, odt, ob in (("qar_int8", "i8", "f32", "f32", 4), ("qar_mx", "e4m3fn", "e8m0", "bf16", 2)):
+        seed, d, specs = mc2_inputs.CONFIGS[name]
+        t = mc2_inputs.make(name)
+        rq, hq = d["r"], d["shape"][-1]
+        nrows = int(np.prod(d["shape"][:-1]))
+        per_s = hq // 128 if sdt == "f32" else hq // 32
+        xs = [t[f"x{i}"].reshape(nrows, hq) for i in range(rq)]
+        sc = [t[f"scale{i}"].reshape(nrows, per_s) for i in range(rq)]
+        sb = 4 * per_s if sdt == "f32" else per_s
+        per, reps, tot = _scaled_run(lambda rows: _timed(lambda: oracle.quant_all_reduce(
+            [np.ascontiguousarray(x[:rows]) for x in xs], [np.ascontiguousarray(s[:rows]) for s in sc], xdt, sdt,
+            odt)), nrows, target_s * 0.05, 512)
+        nbytes = per * (rq * (hq + sb) + hq * ob) * reps
+        configs[name] = {"value": round(nbytes / tot / 1e9, 3), "unit": "GB/s",
+                         "sample": f"{per} of {nrows} rows, {reps} run(s), {tot:.2f} s"}
+
+    # the API page's example (8 x fp16 (16, 512) @ (512, 64)): median of 5, in us
+    seed, d, specs = mc2_inputs.CONFIGS["ag_tiny"]
+    t = mc2_inputs.make("ag_tiny")
+    times = sorted(_timed(lambda: oracle.allgather_matmul([t[f"shard{i}"] for i in range(d["r"])], t["x2"], "f16"))
+                   for _ in range(5))
+    configs["ag_tiny"] = {"value": round(times[2] * 1e6, 1), "unit": "us per call", "sample": "median of 5 runs"}
+
+    for key, c in configs.items():
+        g = gpu_rows.get(key)
+        if g is not None and c["value"] > 0:
+            gv = g["us_per_call"] if c["unit"] == "us per call" else g["achieved"]
+            c["gpu_over_oracle"] = round((c["value"] / gv) if c["unit"] == "us per call" else (gv / c["value"]), 1)
+    res["gpu_over_oracle"] = round(gpu_rows["ag_bf16_tp"]["achieved"] / res["value"], 1) \
+        if "ag_bf16_tp" in gpu_rows else None
+    res["configs"] = configs
+    return res
 
 
 # ---------------------------------------------------------------- profile summaries and stored traffic
@@ -591,7 +753,7 @@ def main():
     }
     if not args.no_cpu_baseline:
         t1 = time.time()
-        res["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
+        res["cpu_baseline"] = cpu_baseline(args.cpu_seconds, out_rows)
         log(f"cpu baseline {time.time() - t1:.1f} s")
     print(json.dumps(res))
 

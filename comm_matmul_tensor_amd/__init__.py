@@ -10,7 +10,8 @@ Functions carry the C names:
   mc2_allgather_matmul, mc2_allgather_matmul_bias, mc2_allgather_arrival_fallbacks, mc2_matmul_grad_input,
   mc2_matmul_grad_weight, mc2_matmul_reduce_scatter, mc2_matmul_reduce_scatter_bias, mc2_bias_grad,
   mc2_alltoall_quant_matmul_workspace_size, mc2_alltoall_quant_matmul, mc2_alltoall_quant_matmul_static,
-  mc2_alltoall_quant_matmul_noalloc, mc2_quant_all_reduce, mc2_quant_reduce_scatter, mc2_status_string, mc2_last_error;
+  mc2_alltoall_quant_matmul_noalloc, mc2_alltoall_quant_matmul_a16w4, mc2_alltoall_quant_matmul_a4w4,
+  mc2_quant_all_reduce, mc2_quant_reduce_scatter, mc2_status_string, mc2_last_error;
 and the test hook mc2_testing_arrival (csrc/testing.h, outside the public header).
 
 Every call checks each tensor's shape, dtype and device against the sizes it
@@ -72,6 +73,12 @@ _SIGS = {
     "mc2_allgather_matmul_bias": [_P, _INT, _I64, _I64, _P, _I64, _INT, _INT, _P, _P, _P, _INT, _INT, _P],
     "mc2_matmul_reduce_scatter_bias": [_P, _P, _INT, _INT, _I64, _I64, _I64, _INT, _INT, _P, _P, _P, _P, _P],
     "mc2_bias_grad": [_P, _I64, _I64, _INT, _P, _P],
+    "mc2_alltoall_quant_matmul_a16w4": [_P, _INT, _I64, _I64, _INT, _P, _I64, _P, _P, _P, _P, _P, _P, _P, _P,
+                                        _P, ctypes.c_size_t, _P],
+    "mc2_alltoall_quant_matmul_a4w4": [_P, _INT, _I64, _I64, _P, _P, _I64, _P, _P, _P, _INT, _P, _P,
+                                       ctypes.c_size_t, _P],
+    "mc2_alltoall_quant_matmul_a16w4_workspace_size": [_INT, _I64, _I64, _I64, ctypes.POINTER(ctypes.c_size_t)],
+    "mc2_alltoall_quant_matmul_a4w4_workspace_size": [_INT, _I64, _I64, _I64, ctypes.POINTER(ctypes.c_size_t)],
 }
 for _name, _args in _SIGS.items():
     _f = getattr(_lib, _name)
@@ -371,6 +378,18 @@ def mc2_alltoall_quant_matmul_workspace_size(rank_size: int, bs: int, h: int, n:
     return size.value
 
 
+def mc2_alltoall_quant_matmul_a16w4_workspace_size(rank_size: int, bs: int, h: int, n: int) -> int:
+    size = ctypes.c_size_t(0)
+    _check(_lib.mc2_alltoall_quant_matmul_a16w4_workspace_size(rank_size, bs, h, n, ctypes.byref(size)))
+    return size.value
+
+
+def mc2_alltoall_quant_matmul_a4w4_workspace_size(rank_size: int, bs: int, h: int, n: int) -> int:
+    size = ctypes.c_size_t(0)
+    _check(_lib.mc2_alltoall_quant_matmul_a4w4_workspace_size(rank_size, bs, h, n, ctypes.byref(size)))
+    return size.value
+
+
 def _a2a_sizes(x1, rank_size, x2):
     bs, h = _2d(x1, "x1")
     if rank_size < 1 or bs % rank_size != 0:
@@ -414,6 +433,93 @@ def mc2_alltoall_quant_matmul(x1: torch.Tensor, rank_size: int, x2: torch.Tensor
             _opt(x1_smooth, "x1_smooth"), _opt(bias, "bias"), _dev(out, "out"), _opt(permuted_out, "permuted_out"),
             _opt(q_out, "q_out"), _opt(x1_scale_out, "x1_scale_out"), _opt(acc_out, "acc_out"),
             _dev(workspace, "workspace"), workspace.numel() * workspace.element_size(), st.cuda_stream))
+    return out
+
+
+def mc2_alltoall_quant_matmul_a16w4(x1: torch.Tensor, rank_size: int, x2: torch.Tensor, x2_scale: torch.Tensor,
+                                    x1_smooth: Optional[torch.Tensor] = None, bias: Optional[torch.Tensor] = None,
+                                    *, out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+                                    permuted_out: Optional[torch.Tensor] = None, q_out: Optional[torch.Tensor] = None,
+                                    x1_scale_out: Optional[torch.Tensor] = None,
+                                    acc_out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """A16W4: mc2_alltoall_quant_matmul with x2 a uint8 (rank_size h, n / 2) tensor of int4 codes
+    (two per byte, low nibble first)."""
+    bs, h = _2d(x1, "x1")
+    if rank_size < 1 or bs % rank_size != 0:
+        raise ValueError(f"bs = {bs} must be a multiple of rank_size = {rank_size}")
+    n = 2 * _2d(x2, "x2")[1]
+    rows, cols = bs // rank_size, rank_size * h
+    _16bit(x1, "x1")
+    _want(x2, "x2", (cols, n // 2), torch.uint8)
+    _want(x2_scale, "x2_scale", (n,), torch.float32)
+    _want(x1_smooth, "x1_smooth", (cols,), x1.dtype, optional=True)
+    _want(bias, "bias", (n,), x1.dtype, optional=True)
+    _want(out, "out", (rows, n), x1.dtype, optional=True)
+    _want(permuted_out, "permuted_out", (rows, cols), x1.dtype, optional=True)
+    _want(q_out, "q_out", (rows, cols), torch.int8, optional=True)
+    _want(x1_scale_out, "x1_scale_out", (rows,), torch.float32, optional=True)
+    _want(acc_out, "acc_out", (rows, n), torch.int32, optional=True)
+    if workspace is not None and (not isinstance(workspace, torch.Tensor) or workspace.dim() != 1):
+        raise ValueError("workspace must be a 1-D tensor")
+    dev = _same_device([("x1", x1), ("x2", x2), ("x2_scale", x2_scale), ("x1_smooth", x1_smooth),
+                        ("bias", bias), ("out", out), ("permuted_out", permuted_out), ("q_out", q_out),
+                        ("x1_scale_out", x1_scale_out), ("acc_out", acc_out), ("workspace", workspace)])
+    need = mc2_alltoall_quant_matmul_a16w4_workspace_size(rank_size, bs, h, n)
+    st = _stream_obj(stream)
+    with torch.cuda.stream(st):
+        if out is None:
+            out = torch.empty((rows, n), dtype=x1.dtype, device=dev)
+        if workspace is None:
+            workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+        _check(_lib.mc2_alltoall_quant_matmul_a16w4(
+            _dev(x1, "x1"), rank_size, bs, h, _dt(x1), _dev(x2, "x2"), n, _dev(x2_scale, "x2_scale"),
+            _opt(x1_smooth, "x1_smooth"), _opt(bias, "bias"), _dev(out, "out"), _opt(permuted_out, "permuted_out"),
+            _opt(q_out, "q_out"), _opt(x1_scale_out, "x1_scale_out"), _opt(acc_out, "acc_out"),
+            _dev(workspace, "workspace"), workspace.numel() * workspace.element_size(), st.cuda_stream))
+    return out
+
+
+def mc2_alltoall_quant_matmul_a4w4(x1: torch.Tensor, rank_size: int, x1_scale: torch.Tensor, x2: torch.Tensor,
+                                   x2_scale: torch.Tensor, bias: Optional[torch.Tensor] = None, *,
+                                   out_dtype: torch.dtype = torch.bfloat16, out: Optional[torch.Tensor] = None,
+                                   acc_out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+                                   stream=None) -> torch.Tensor:
+    """A4W4 full quantisation: x1 uint8 (bs, h / 2) and x2 uint8 (rank_size h, n / 2) tensors of int4
+    codes (two per byte, low nibble first), x1_scale fp32 (bs / rank_size)."""
+    bs, hb = _2d(x1, "x1")
+    h = 2 * hb
+    if rank_size < 1 or bs % rank_size != 0:
+        raise ValueError(f"bs = {bs} must be a multiple of rank_size = {rank_size}")
+    n = 2 * _2d(x2, "x2")[1]
+    rows, cols = bs // rank_size, rank_size * h
+    if x1.dtype != torch.uint8:
+        raise TypeError("x1 must be uint8 (packed int4 codes)")
+    if out is not None:
+        out_dtype = out.dtype
+    if out_dtype not in (torch.float16, torch.bfloat16):
+        raise TypeError(f"out must be float16 or bfloat16, got {out_dtype}")
+    _want(x1_scale, "x1_scale", (rows,), torch.float32)
+    _want(x2, "x2", (cols, n // 2), torch.uint8)
+    _want(x2_scale, "x2_scale", (n,), torch.float32)
+    _want(bias, "bias", (n,), out_dtype, optional=True)
+    _want(out, "out", (rows, n), out_dtype, optional=True)
+    _want(acc_out, "acc_out", (rows, n), torch.int32, optional=True)
+    if workspace is not None and (not isinstance(workspace, torch.Tensor) or workspace.dim() != 1):
+        raise ValueError("workspace must be a 1-D tensor")
+    dev = _same_device([("x1", x1), ("x1_scale", x1_scale), ("x2", x2), ("x2_scale", x2_scale), ("bias", bias),
+                        ("out", out), ("acc_out", acc_out), ("workspace", workspace)])
+    need = mc2_alltoall_quant_matmul_a4w4_workspace_size(rank_size, bs, h, n)
+    st = _stream_obj(stream)
+    with torch.cuda.stream(st):
+        if out is None:
+            out = torch.empty((rows, n), dtype=out_dtype, device=dev)
+        if workspace is None:
+            workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+        _check(_lib.mc2_alltoall_quant_matmul_a4w4(_dev(x1, "x1"), rank_size, bs, h, _dev(x1_scale, "x1_scale"),
+                                                   _dev(x2, "x2"), n, _dev(x2_scale, "x2_scale"), _opt(bias, "bias"),
+                                                   _dev(out, "out"), _dt(out), _opt(acc_out, "acc_out"),
+                                                   _dev(workspace, "workspace"),
+                                                   workspace.numel() * workspace.element_size(), st.cuda_stream))
     return out
 
 
@@ -554,7 +660,9 @@ __all__ = [
     "mc2_matmul_grad_input", "mc2_matmul_grad_weight", "mc2_matmul_reduce_scatter", "mc2_matmul_reduce_scatter_bias",
     "mc2_bias_grad",
     "mc2_alltoall_quant_matmul_workspace_size", "mc2_alltoall_quant_matmul", "mc2_alltoall_quant_matmul_static",
-    "mc2_alltoall_quant_matmul_noalloc", "MC2_NOALLOC_SCRATCH_BYTES",
+    "mc2_alltoall_quant_matmul_noalloc", "MC2_NOALLOC_SCRATCH_BYTES", "mc2_alltoall_quant_matmul_a16w4",
+    "mc2_alltoall_quant_matmul_a4w4", "mc2_alltoall_quant_matmul_a16w4_workspace_size",
+    "mc2_alltoall_quant_matmul_a4w4_workspace_size",
     "mc2_quant_all_reduce", "mc2_quant_reduce_scatter",
     "mc2_status_string", "mc2_last_error", "Mc2Error", "LIB_PATH",
 ]

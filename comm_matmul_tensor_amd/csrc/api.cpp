@@ -112,7 +112,7 @@ mc2_status alltoall_quant_matmul_run(const void* x1, int rank_size, int64_t bs, 
                                      const int8_t* x2, int64_t n, const float* x2_scale, const void* x1_smooth,
                                      const void* bias, void* out, void* permuted_out, int8_t* q_out,
                                      float* x1_scale_out, int32_t* acc_out, void* workspace,
-                                     size_t workspace_bytes, void* stream, bool device_checked) {
+                                     size_t workspace_bytes, void* stream, bool device_checked, bool w4) {
   size_t need = 0;
   mc2_status s = mc2_alltoall_quant_matmul_workspace_size(rank_size, bs, h, n, &need);
   if (s != MC2_OK) {
@@ -120,15 +120,27 @@ mc2_status alltoall_quant_matmul_run(const void* x1, int rank_size, int64_t bs, 
       return fail(MC2_ERR_NULL, "alltoall_quant_matmul: x1, x2, x2_scale and out are required");
     return s;
   }
+  // A16W4: N even (two int4 codes per byte along N)
+  if (w4 && n % 2 != 0) return fail(MC2_ERR_SHAPE, "alltoall_quant_matmul_a16w4: n must be even");
+  const int64_t rows = bs / rank_size, cols = (int64_t)rank_size * h;
   s = check_alltoall_quant_matmul(x1, rank_size, bs, h, x1_dtype, x2, n, x2_scale, x1_smooth, bias, out,
                                   permuted_out, q_out, x1_scale_out, acc_out, workspace, workspace_bytes,
-                                  need);
+                                  w4 ? need + (size_t)(cols * n) : need);
   if (s != MC2_OK) return s;
   int dev;
   if (!device_checked && (s = current_device(&dev)) != MC2_OK) return s;
   hipStream_t st = static_cast<hipStream_t>(stream);
-  const int64_t rows = bs / rank_size, cols = (int64_t)rank_size * h;
   char* ws = static_cast<char*>(workspace);
+  if (w4) {  // the int4 weight widened to int8 at the end of the workspace
+    WidenArgs wa{};
+    int8_t* x2w = reinterpret_cast<int8_t*>(ws + need);
+    wa.src[0] = reinterpret_cast<const uint8_t*>(x2);
+    wa.dst[0] = x2w;
+    wa.bytes[0] = cols * n / 2;
+    hipError_t e = launch_widen_int4(wa, st);
+    if (e != hipSuccess) return hip_fail(e, "alltoall_quant_matmul_a16w4 widening launch");
+    x2 = x2w;
+  }
   int8_t* q = q_out ? q_out : reinterpret_cast<int8_t*>(ws);
   ws += align_up((size_t)(rows * cols), 256);
   float* s1 = x1_scale_out ? x1_scale_out : reinterpret_cast<float*>(ws);
@@ -521,6 +533,92 @@ mc2_status mc2_alltoall_quant_matmul(const void* x1, int rank_size, int64_t bs, 
   return alltoall_quant_matmul_run(x1, rank_size, bs, h, x1_dtype, x2, n, x2_scale, x1_smooth, bias, out,
                                    permuted_out, q_out, x1_scale_out, acc_out, workspace, workspace_bytes, stream,
                                    false);
+}
+
+mc2_status mc2_alltoall_quant_matmul_a16w4(const void* x1, int rank_size, int64_t bs, int64_t h,
+                                           mc2_dtype x1_dtype, const uint8_t* x2, int64_t n, const float* x2_scale,
+                                           const void* x1_smooth, const void* bias, void* out, void* permuted_out,
+                                           int8_t* q_out, float* x1_scale_out, int32_t* acc_out, void* workspace,
+                                           size_t workspace_bytes, void* stream) {
+  clear_error();
+  return alltoall_quant_matmul_run(x1, rank_size, bs, h, x1_dtype, reinterpret_cast<const int8_t*>(x2), n, x2_scale,
+                                   x1_smooth, bias, out, permuted_out, q_out, x1_scale_out, acc_out, workspace,
+                                   workspace_bytes, stream, false, true);
+}
+
+mc2_status mc2_alltoall_quant_matmul_a16w4_workspace_size(int rank_size, int64_t bs, int64_t h, int64_t n,
+                                                          size_t* bytes) {
+  clear_error();
+  if (!bytes) return fail(MC2_ERR_NULL, "a16w4_workspace_size: bytes is NULL");
+  size_t need = 0;
+  mc2_status s = mc2_alltoall_quant_matmul_workspace_size(rank_size, bs, h, n, &need);
+  if (s != MC2_OK) return s;
+  if (n % 2 != 0) return fail(MC2_ERR_SHAPE, "a16w4_workspace_size: n must be even");
+  *bytes = need + (size_t)rank_size * (size_t)h * (size_t)n;
+  return MC2_OK;
+}
+
+mc2_status mc2_alltoall_quant_matmul_a4w4_workspace_size(int rank_size, int64_t bs, int64_t h, int64_t n,
+                                                         size_t* bytes) {
+  clear_error();
+  if (!bytes) return fail(MC2_ERR_NULL, "a4w4_workspace_size: bytes is NULL");
+  mc2_status s = check_alltoall_a4w4_sizes(rank_size, bs, h, n);
+  if (s != MC2_OK) return s;
+  *bytes = align_up((size_t)(bs * h), 256) + (size_t)rank_size * (size_t)h * (size_t)n;
+  return MC2_OK;
+}
+
+mc2_status mc2_alltoall_quant_matmul_a4w4(const uint8_t* x1, int rank_size, int64_t bs, int64_t h,
+                                          const float* x1_scale, const uint8_t* x2, int64_t n,
+                                          const float* x2_scale, const void* bias, void* out, mc2_dtype out_dtype,
+                                          int32_t* acc_out, void* workspace, size_t workspace_bytes, void* stream) {
+  clear_error();
+  mc2_status s = check_alltoall_a4w4(x1, rank_size, bs, h, x1_scale, x2, n, x2_scale, bias, out, out_dtype, acc_out);
+  if (s != MC2_OK) return s;
+  const size_t x1w_bytes = align_up((size_t)(bs * h), 256);
+  const size_t need = x1w_bytes + (size_t)rank_size * (size_t)h * (size_t)n;
+  if (!workspace || workspace_bytes < need)
+    return fail(MC2_ERR_WORKSPACE, "alltoall_quant_matmul_a4w4: workspace needs " + std::to_string(need) + " bytes");
+  if (reinterpret_cast<uintptr_t>(workspace) % 16 != 0)
+    return fail(MC2_ERR_ALIGN, "alltoall_quant_matmul_a4w4: workspace not 16-byte aligned");
+  int dev;
+  if ((s = current_device(&dev)) != MC2_OK) return s;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  // both operands widened to int8 (x1 first, then x2, in the workspace),
+  // then the int8 chain of the static entry point
+  int8_t* x1w = static_cast<int8_t*>(workspace);
+  int8_t* x2w = x1w + x1w_bytes;
+  WidenArgs wa{};
+  wa.src[0] = x1;
+  wa.dst[0] = x1w;
+  wa.bytes[0] = bs * h / 2;
+  wa.src[1] = x2;
+  wa.dst[1] = x2w;
+  wa.bytes[1] = (int64_t)rank_size * h * n / 2;
+  hipError_t e = launch_widen_int4(wa, st);
+  if (e != hipSuccess) return hip_fail(e, "alltoall_quant_matmul_a4w4 widening launch");
+  // The AlltoAll permute is the GEMM's addressing of A (as in the static
+  // entry point): K split into rank_size segments of h codes, (bs / rank_size) h apart.
+  const int64_t rows = bs / rank_size, cols = (int64_t)rank_size * h;
+  GemmI8Args ga{};
+  ga.a = x1w;
+  ga.a_ld = h;
+  ga.kseg = h;
+  ga.kseg_stride = rows * h;
+  ga.a_bytes = bs * h;
+  ga.b = x2w;
+  ga.s1 = x1_scale;
+  ga.s2 = x2_scale;
+  ga.bias = bias;
+  ga.out = out;
+  ga.acc_out = acc_out;
+  ga.m = rows;
+  ga.n = n;
+  ga.k = cols;
+  ga.dtype = dt(out_dtype);
+  e = launch_gemm_i8(ga, st);
+  if (e != hipSuccess) return hip_fail(e, "alltoall_quant_matmul_a4w4 launch");
+  return MC2_OK;
 }
 
 mc2_status mc2_alltoall_quant_matmul_static(const int8_t* x1, int rank_size, int64_t bs, int64_t h,

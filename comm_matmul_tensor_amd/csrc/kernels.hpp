@@ -138,4 +138,13 @@ struct GemmI8Args {
 size_t gemm_i8_workspace_bytes(int64_t m, int64_t n, int64_t k);
 hipError_t launch_gemm_i8(const GemmI8Args& a, hipStream_t s);
 
+// ---- K7: int4 codes (two per byte, low nibble first) widened to int8
+struct WidenArgs {
+  const uint8_t* src[2];  // packed codes, 16-byte aligned (a range of 0 bytes: unused)
+  int8_t* dst[2];         // 2 bytes[i] int8 values, 16-byte aligned
+  int64_t bytes[2];       // packed bytes of each range
+  int64_t blocks0;        // set by the launcher
+};
+hipError_t launch_widen_int4(const WidenArgs& a, hipStream_t s);
+
 }  // namespace mc2

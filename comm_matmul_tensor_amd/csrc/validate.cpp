@@ -166,6 +166,37 @@ mc2_status check_alltoall_quant_matmul(const void* x1, int rank_size, int64_t bs
   return MC2_OK;
 }
 
+mc2_status check_alltoall_a4w4_sizes(int rank_size, int64_t bs, int64_t h, int64_t n) {
+  // aclnnAlltoAllQuantMatmul "constraints", A4W4: H and N even, rankSize * H
+  // in [1, 35000]; rankSize 2/4/8; BS divisible by rankSize; BS, N at most
+  // INT32_MAX; no empty tensors
+  if (!valid_world(rank_size))
+    return fail(MC2_ERR_SHAPE, "alltoall_quant_matmul_a4w4: rank_size must be 2, 4 or 8, got " + str(rank_size));
+  if (bs < 1 || h < 1 || n < 1) return fail(MC2_ERR_SHAPE, "alltoall_quant_matmul_a4w4: empty tensor");
+  if (bs % rank_size != 0) return fail(MC2_ERR_SHAPE, "alltoall_quant_matmul_a4w4: bs must be divisible by rank_size");
+  if (bs > INT32_MAX || n > INT32_MAX)
+    return fail(MC2_ERR_SHAPE, "alltoall_quant_matmul_a4w4: bs and n must not exceed INT32_MAX");
+  if (h % 2 != 0 || n % 2 != 0) return fail(MC2_ERR_SHAPE, "alltoall_quant_matmul_a4w4: h and n must be even");
+  if (h > 35000 || (int64_t)rank_size * h > 35000)
+    return fail(MC2_ERR_SHAPE, "alltoall_quant_matmul_a4w4: rank_size*h must lie in [1, 35000]");
+  return MC2_OK;
+}
+
+mc2_status check_alltoall_a4w4(const void* x1, int rank_size, int64_t bs, int64_t h, const void* x1_scale,
+                                const void* x2, int64_t n, const void* x2_scale, const void* bias, const void* out,
+                                mc2_dtype out_dtype, const void* acc_out) {
+  // per-token x1 scale (mode 3) and the per-channel x2 scale are required
+  if (!x1 || !x1_scale || !x2 || !x2_scale || !out)
+    return fail(MC2_ERR_NULL, "alltoall_quant_matmul_a4w4: x1, x1_scale, x2, x2_scale and out are required");
+  mc2_status s = check_alltoall_a4w4_sizes(rank_size, bs, h, n);
+  if (s != MC2_OK) return s;
+  if (!is_half(out_dtype)) return fail(MC2_ERR_DTYPE, "alltoall_quant_matmul_a4w4: out must be F16 or BF16");
+  const void* ptrs[] = {x1, x1_scale, x2, x2_scale, bias, out, acc_out};
+  for (const void* p : ptrs)
+    if (p && !aligned16(p)) return fail(MC2_ERR_ALIGN, "alltoall_quant_matmul_a4w4: tensor not 16-byte aligned");
+  return MC2_OK;
+}
+
 mc2_status check_alltoall_quant_matmul_static(const void* x1, int rank_size, int64_t bs, int64_t h,
                                               const void* x1_scale, const void* x2, int64_t n,
                                               const void* x2_scale, const void* bias, const void* out,

@@ -35,6 +35,10 @@ mc2_status check_alltoall_quant_matmul(const void* x1, int rank_size, int64_t bs
                                        const void* q_out, const void* x1_scale_out,
                                        const void* acc_out, const void* workspace,
                                        size_t workspace_bytes, size_t workspace_needed);
+mc2_status check_alltoall_a4w4_sizes(int rank_size, int64_t bs, int64_t h, int64_t n);
+mc2_status check_alltoall_a4w4(const void* x1, int rank_size, int64_t bs, int64_t h, const void* x1_scale,
+                                const void* x2, int64_t n, const void* x2_scale, const void* bias, const void* out,
+                                mc2_dtype out_dtype, const void* acc_out);
 mc2_status check_alltoall_quant_matmul_static(const void* x1, int rank_size, int64_t bs, int64_t h,
                                               const void* x1_scale, const void* x2, int64_t n,
                                               const void* x2_scale, const void* bias, const void* out,

@@ -312,6 +312,53 @@ mc2_status mc2_alltoall_quant_matmul_static(const int8_t* x1, int rank_size, int
                                             void* stream);
 
 /*
+ * Reading of the int4 formats of A16W4 / A4W4 (aclnnAlltoAllQuantMatmul page,
+ * "constraints": A16W4 needs N even, A4W4 needs H and N even; the quantised
+ * x1 dtype is INT8 only): two's-complement int4 codes (-8..7), two per byte
+ * along the last dimension, value 2i in the low nibble of byte i and value
+ * 2i + 1 in the high nibble.  The library widens int4 operands to int8 in the
+ * workspace (exactly) before the int8 GEMM.
+ *
+ * AlltoAllQuantMatmul A16W4: mc2_alltoall_quant_matmul's dynamic per-token
+ * chain (x1 quantised to int8 per token) with an int4 weight:
+ * x2 (rank_size h, n / 2) bytes of int4 codes; n must be even.  Every other
+ * argument and the results are those of mc2_alltoall_quant_matmul; acc is
+ * exact int32.  The workspace (16-byte aligned) holds
+ * mc2_alltoall_quant_matmul_a16w4_workspace_size bytes: the A16W8 workspace
+ * plus rank_size h n bytes for the widened weight.
+ */
+mc2_status mc2_alltoall_quant_matmul_a16w4_workspace_size(int rank_size, int64_t bs, int64_t h, int64_t n,
+                                                          size_t* bytes);
+mc2_status mc2_alltoall_quant_matmul_a16w4(const void* x1, int rank_size, int64_t bs, int64_t h,
+                                           mc2_dtype x1_dtype, const uint8_t* x2, int64_t n, const float* x2_scale,
+                                           const void* x1_smooth, const void* bias, void* out, void* permuted_out,
+                                           int8_t* q_out, float* x1_scale_out, int32_t* acc_out, void* workspace,
+                                           size_t workspace_bytes, void* stream);
+
+/*
+ * AlltoAllQuantMatmul A4W4 (full quantisation, x1 mode 3, x2 mode 2): the
+ * chain of mc2_alltoall_quant_matmul_static with int4 activations and weight.
+ *   P    = AlltoAll(x1.view(rank_size, bs / rank_size, h)).permute(1, 0, 2)
+ *          .view(bs / rank_size, rank_size h)        (int4 codes)
+ *   acc  = P @ x2                                     exact int32
+ *   out  = acc * x1_scale * x2_scale + bias           fp32, rounded once
+ * x1        (bs, h / 2) bytes of int4 codes; h even; rank_size h in [1, 35000]
+ * x1_scale  (bs / rank_size) fp32, one per token of P
+ * x2        (rank_size h, n / 2) bytes of int4 codes; n even
+ * x2_scale  (n) fp32; bias (n) of out_dtype or NULL; out (bs / rank_size, n)
+ * acc_out   optional (bs / rank_size, n) int32
+ * workspace 16-byte aligned, mc2_alltoall_quant_matmul_a4w4_workspace_size
+ *           bytes (bs h + rank_size h n, rounded up): both operands widened
+ *           to int8.  The permute is the GEMM's load addressing.
+ */
+mc2_status mc2_alltoall_quant_matmul_a4w4_workspace_size(int rank_size, int64_t bs, int64_t h, int64_t n,
+                                                         size_t* bytes);
+mc2_status mc2_alltoall_quant_matmul_a4w4(const uint8_t* x1, int rank_size, int64_t bs, int64_t h,
+                                          const float* x1_scale, const uint8_t* x2, int64_t n,
+                                          const float* x2_scale, const void* bias, void* out, mc2_dtype out_dtype,
+                                          int32_t* acc_out, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * QuantAllReduce -- QuantAllReduce README ("function" formula, parameter
  * table, constraints):
  *   out = sum over ranks i of dequant(x[i])   with dequant = x * its scale

@@ -31,7 +31,7 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     names = _declared()
-    assert len(names) == 16, names
+    assert len(names) == 20, names
     for n in names:
         assert hasattr(lib, n), n
 
@@ -141,6 +141,60 @@ def test_alltoall_static_validation(lib):
     assert f(*bad) == 3                                    # fp32 out
     bad = list(args); bad[11] = ctypes.c_void_p(0x10008)
     assert f(*bad) == 8                                    # permuted_out misaligned
+
+
+def test_int4_validation(lib):
+    """A16W4 / A4W4: int4 codes two per byte (n even; A4W4 also h even); the
+    workspace holds the widened int8 operands."""
+    P4 = [ctypes.c_int, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.POINTER(ctypes.c_size_t)]
+    w16 = lib.mc2_alltoall_quant_matmul_a16w4_workspace_size
+    w44 = lib.mc2_alltoall_quant_matmul_a4w4_workspace_size
+    w8 = lib.mc2_alltoall_quant_matmul_workspace_size
+    for f in (w16, w44, w8):
+        f.argtypes = P4
+    n, m = ctypes.c_size_t(0), ctypes.c_size_t(0)
+    assert w8(8, 8192, 4096, 7168, ctypes.byref(m)) == 0
+    assert w16(8, 8192, 4096, 7168, ctypes.byref(n)) == 0 and n.value == m.value + 32768 * 7168
+    assert w16(8, 8192, 4096, 7167, ctypes.byref(n)) == 2     # n odd
+    assert w16(4, 8192, 1002, 7168, ctypes.byref(n)) == 2     # rank_size*h not a multiple of 16
+    assert w44(8, 8192, 4096, 7168, ctypes.byref(n)) == 0 and n.value == 8192 * 4096 + 32768 * 7168
+    assert w44(4, 12, 6, 2, ctypes.byref(n)) == 0 and n.value == 256 + 24 * 2   # x1 part rounded up to 256
+    assert w44(8, 8192, 4095, 7168, ctypes.byref(n)) == 2     # h odd
+    assert w44(8, 8192, 4096, 7167, ctypes.byref(n)) == 2     # n odd
+    assert w44(8, 8192, 4376, 7168, ctypes.byref(n)) == 2     # rank_size*h above 35000
+    assert w44(8, 8192, 4096, 7168, None) == 1
+    f = lib.mc2_alltoall_quant_matmul_a4w4
+    f.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p,
+                  ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p,
+                  ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+    assert w44(8, 64, 256, 32, ctypes.byref(n)) == 0
+    args = [A, 8, 64, 256, B, C, 32, B, None, A, 2, None, C, n.value, None]
+    for i in (0, 4, 5, 7, 9):                                 # x1, x1_scale, x2, x2_scale, out
+        bad = list(args); bad[i] = None
+        assert f(*bad) == 1
+    bad = list(args); bad[13] = n.value - 1
+    assert f(*bad) == 5                                       # workspace too small
+    bad = list(args); bad[12] = None
+    assert f(*bad) == 5                                       # no workspace
+    bad = list(args); bad[12] = ctypes.c_void_p(0x30008)
+    assert f(*bad) == 8                                       # workspace misaligned
+    bad = list(args); bad[3] = 255
+    assert f(*bad) == 2                                       # h odd
+    bad = list(args); bad[10] = 0
+    assert f(*bad) == 3                                       # fp32 out
+    g = lib.mc2_alltoall_quant_matmul_a16w4
+    g.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_int64, ctypes.c_int, ctypes.c_void_p,
+                  ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                  ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                  ctypes.c_size_t, ctypes.c_void_p]
+    assert w16(8, 64, 256, 32, ctypes.byref(n)) == 0
+    args = [A, 8, 64, 256, 2, B, 32, C, None, None, C, None, None, None, None, A, n.value, None]
+    bad = list(args); bad[16] = n.value - 1
+    assert g(*bad) == 5                                       # workspace without room for the widened weight
+    bad = list(args); bad[6] = 31
+    assert g(*bad) == 2                                       # n odd
+    bad = list(args); bad[5] = None
+    assert g(*bad) == 1                                       # x2 NULL
 
 
 def test_matmul_reduce_scatter_validation(lib):
