@@ -329,8 +329,26 @@ __device__ __forceinline__ void copy_gather(const uint8_t* As, void* gout, int64
                                             int64_t k0) {
   using T = typename Elem<E>::T;
   constexpr int CH = 16 / E;
+  constexpr int NG = BM / 32;
+  if (m0 + BM <= m && k0 + CH * 8 <= k && k % CH == 0) {
+    // the tile's rows and this step's K range lie inside the matrix: all LDS
+    // reads first, one wait, then the stores (no per-lane branches, which
+    // made every chunk wait for its own read and for every earlier one)
+    u32x4 v[NG];
 #pragma unroll
-  for (int i = 0; i < BM / 32; i++) {
+    for (int i = 0; i < NG; i++) {
+      const int c = threadIdx.x + i * kThreads;
+      v[i] = *reinterpret_cast<const u32x4*>(As + swz(c / 8, c % 8));
+    }
+#pragma unroll
+    for (int i = 0; i < NG; i++) {
+      const int c = threadIdx.x + i * kThreads;
+      store_out16(static_cast<T*>(gout) + (m0 + c / 8) * k + k0 + CH * (c % 8), v[i]);
+    }
+    return;
+  }
+#pragma unroll
+  for (int i = 0; i < NG; i++) {
     const int c = threadIdx.x + i * kThreads, row = c / 8, chunk = c % 8;
     const int64_t grow = m0 + row, gk = k0 + CH * chunk;
     if (grow >= m || gk >= k) continue;
