@@ -131,16 +131,7 @@ mc2_status alltoall_quant_matmul_run(const void* x1, int rank_size, int64_t bs, 
   if (!device_checked && (s = current_device(&dev)) != MC2_OK) return s;
   hipStream_t st = static_cast<hipStream_t>(stream);
   char* ws = static_cast<char*>(workspace);
-  if (w4) {  // the int4 weight widened to int8 at the end of the workspace
-    WidenArgs wa{};
-    int8_t* x2w = reinterpret_cast<int8_t*>(ws + need);
-    wa.src[0] = reinterpret_cast<const uint8_t*>(x2);
-    wa.dst[0] = x2w;
-    wa.bytes[0] = cols * n / 2;
-    hipError_t e = launch_widen_int4(wa, st);
-    if (e != hipSuccess) return hip_fail(e, "alltoall_quant_matmul_a16w4 widening launch");
-    x2 = x2w;
-  }
+  int8_t* x2w = reinterpret_cast<int8_t*>(ws + need);  // A16W4: the widened weight, past the A16W8 part
   int8_t* q = q_out ? q_out : reinterpret_cast<int8_t*>(ws);
   ws += align_up((size_t)(rows * cols), 256);
   float* s1 = x1_scale_out ? x1_scale_out : reinterpret_cast<float*>(ws);
@@ -158,6 +149,20 @@ mc2_status alltoall_quant_matmul_run(const void* x1, int rank_size, int64_t bs, 
   qa.dtype = dt(x1_dtype);
   hipError_t e = launch_permute_quant(qa, st);
   if (e != hipSuccess) return hip_fail(e, "alltoall_quant_matmul quant launch");
+  // The weight passes through the caches right before the GEMM reads it: A16W4
+  // widens it there (int4 -> int8), A16W8 streams it once (K9).
+  if (w4) {
+    WidenArgs wa{};
+    wa.src[0] = reinterpret_cast<const uint8_t*>(x2);
+    wa.dst[0] = x2w;
+    wa.bytes[0] = cols * n / 2;
+    e = launch_widen_int4(wa, st);
+    if (e != hipSuccess) return hip_fail(e, "alltoall_quant_matmul_a16w4 widening launch");
+    x2 = x2w;
+  } else {
+    e = launch_prefetch(x2, cols * n, st);
+    if (e != hipSuccess) return hip_fail(e, "alltoall_quant_matmul prefetch launch");
+  }
 
   GemmI8Args ga{};
   ga.a = q;
@@ -653,7 +658,8 @@ mc2_status mc2_alltoall_quant_matmul_static(const int8_t* x1, int rank_size, int
   ga.n = n;
   ga.k = cols;
   ga.dtype = dt(out_dtype);
-  hipError_t e = launch_gemm_i8(ga, static_cast<hipStream_t>(stream));
+  hipError_t e = launch_prefetch(x2, cols * n, static_cast<hipStream_t>(stream));  // the weight into the caches (K9)
+  if (e == hipSuccess) e = launch_gemm_i8(ga, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "alltoall_quant_matmul_static launch");
   return MC2_OK;
 }
