@@ -28,6 +28,10 @@ struct DeviceState {
   hipEvent_t fork = nullptr, join = nullptr;
   unsigned* flags = nullptr;
   unsigned epoch = 0;
+  // held from recording `fork` on a caller's stream to waiting on `join`, so
+  // calls from several host threads do not re-record the shared events in
+  // between
+  std::mutex fork_mutex;
 };
 DeviceState g_dev[kMaxDevices];
 std::mutex g_dev_mutex;
@@ -150,7 +154,9 @@ mc2_status alltoall_quant_matmul_run(const void* x1, int rank_size, int64_t bs, 
   hipError_t e = launch_permute_quant(qa, st);
   if (e != hipSuccess) return hip_fail(e, "alltoall_quant_matmul quant launch");
   // The weight passes through the caches right before the GEMM reads it: A16W4
-  // widens it there (int4 -> int8), A16W8 streams it once (K9).
+  // widens it there (int4 -> int8), A16W8 streams it once (K9).  (K9 on a
+  // side stream beside K2 measured slower: both kernels slowed down, and the
+  // join before the GEMM cost about 11 us.)
   if (w4) {
     WidenArgs wa{};
     wa.src[0] = reinterpret_cast<const uint8_t*>(x2);
@@ -436,6 +442,7 @@ mc2_status allgather_matmul_impl(const void* const* shards, int world_size, int6
   c.r = world_size;
   c.first_chunk = (int)first_chunk;
   c.epoch = epoch;
+  std::lock_guard<std::mutex> fork_lock(ds->fork_mutex);
   hipError_t e = hipEventRecord(ds->fork, st);
   if (e == hipSuccess) e = hipStreamWaitEvent(ds->copy_stream, ds->fork, 0);
   if (e == hipSuccess) e = launch_arrival_copy(c, ds->copy_stream);
