@@ -287,8 +287,15 @@ __global__ __launch_bounds__(kPipeThreads, 1) void permute_quant_pipe(QuantArgs 
       if (valid[i]) *reinterpret_cast<u32x2*>(a.q + t * cols + ((int64_t)threadIdx.x + i * kPipeThreads) * 8) = qv;
     }
   };
+  // Token by token, as the loop issues them: interleaved (as the compiler
+  // scheduled them without the barrier) they set the waits at the top of the
+  // loop, shared with the steady state, to vmcnt(7), (5), (3), (1): pass 1 of
+  // a token then waited for most of the next token's loads.
 #pragma unroll
-  for (int d = 0; d < D; d++) issue(buf[d], d);
+  for (int d = 0; d < D; d++) {
+    issue(buf[d], d);
+    __builtin_amdgcn_sched_barrier(0);
+  }
   for (int k0 = 0;; k0 += D) {
 #pragma unroll
     for (int d = 0; d < D; d++) {
