@@ -220,6 +220,69 @@ __global__ __launch_bounds__(kThreads, 1) void gemm16_kernel(Problem p, void* c)
   else store_c16_tile<BM, BN, VEC>(h0, h1, static_cast<uint16_t*>(c), p.m, p.n, m0, n0, !GA);
 }
 
+// AllGatherMatmul with gather_out on the fast path (A K-contiguous, three
+// stages, no bias or arrival): 512 threads.  Wavefronts 0-3 run the
+// four-wavefront GEMM without the gather copy; wavefronts 4-7 copy A tiles
+// from the LDS stages to gather_out.  The A tile of step kt sits in stage
+// kt % 3 from the main loop's barrier kt (the prologue's counted as 0), after
+// which every wavefront has waited for its DMA, until barrier kt + 1, after
+// which the DMA of step kt + 3 may overwrite it; the copy wavefronts read it
+// in that window, so they go through the same barriers (the loop's nk + 1,
+// then the one that ends the staging of C).  Their stores count only in
+// their own wavefronts' vmcnt, so the GEMM's DMA waits never wait for them
+// (with the copy inside the GEMM's wavefronts every step that copies waited
+// for its stores).  The workgroup of tile column tn copies the steps kt with
+// kt % tiles_n == tn, so the tiles of a row share the copy of its A.  All 512
+// threads then store C.  AllGatherMatmul 8 x (512, 4096) @ (4096, 1792):
+// 62.1 -> 56.2 us with its inputs in the caches (53.5 us without gather_out),
+// 77.7 -> 77.1 us after a 512 MB write, 72.4 -> 70.9 us in the benchmark
+// step; the API page's 8 x (16, 512) @ (512, 64) example 19.8 -> 15.9 us.
+template <int BM, int BN, bool BKM, int DT>
+__global__ __launch_bounds__(2 * kThreads, 1) void gemm16_gather_kernel(Problem p, void* c) {
+  constexpr int FM = BM / 32, FN = BN / 32;
+  constexpr int BK = kRowBytes / 2;
+  static_assert(lds_stages<BM, BN>() == 3, "three stages");
+  __shared__ __attribute__((aligned(1024))) uint8_t s0[lds_stage_array_bytes<BM, BN>()];
+  __shared__ __attribute__((aligned(1024))) uint8_t s1[lds_stage_array_bytes<BM, BN>()];
+  __shared__ __attribute__((aligned(1024))) uint8_t s2[lds_stage_array_bytes<BM, BN>()];
+  int tm, tn;
+  tile_of_block(p.m, p.n, BM, BN, p.tile_order_cols, p.tile_group, tm, tn, p.first_row_tile);
+  const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
+  const int tiles_n = (int)((p.n + BN - 1) / BN);
+  uint16_t* h0 = reinterpret_cast<uint16_t*>(s0);
+  uint16_t* h1 = reinterpret_cast<uint16_t*>(s1);
+  if (threadIdx.x < kThreads) {
+    typename Ops16<DT>::Acc acc[FM][FN];
+#pragma unroll
+    for (int i = 0; i < FM; i++)
+#pragma unroll
+      for (int j = 0; j < FN; j++) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // the fast loop without the gather copy (the host launches this kernel
+    // only where it applies)
+    run_fast_loop<2, BM, BN, true, BKM, Ops16<DT>>(p, m0, n0, s0, s1, s2, acc);
+    stage_c16<BM, BN, DT>(h0, h1, [&](int i, int j, int r, int, int) { return acc[i][j][r]; });
+  } else {
+    const int tid = (int)threadIdx.x - kThreads;
+    const int nk = (int)(p.k / BK);
+    int next = tn;
+    for (int kt = 0; kt < nk; kt++) {
+      lds_barrier();  // barrier kt: stage kt % 3 holds step kt
+      if (kt == next) {
+        const uint8_t* st = kt % 3 == 0 ? s0 : kt % 3 == 1 ? s1 : s2;
+        copy_gather<2, BM>(st, p.gather_out, p.m, p.k, m0, (int64_t)kt * BK, tid);
+        next += tiles_n;
+      }
+    }
+    lds_barrier();   // barrier nk
+    __syncthreads();  // the one that ends the staging of C
+  }
+  store_c16_tile<BM, BN, true, 2 * kThreads>(h0, h1, static_cast<uint16_t*>(c), p.m, p.n, m0, n0);
+}
+
+#ifndef MC2_GATHER_WAVES
+#define MC2_GATHER_WAVES 1
+#endif
+
 template <int BM, int BN, bool AK, bool BKM, int DT>
 hipError_t launch_cfg(Problem p, void* c, hipStream_t s) {
   const int64_t tiles = ((p.m + BM - 1) / BM) * ((p.n + BN - 1) / BN);
@@ -246,6 +309,14 @@ hipError_t launch_cfg(Problem p, void* c, hipStream_t s) {
   }
   // the two-stage loop has neither the arrival wait nor the gather copy
   if (lds_stages<BM, BN>() == 2 && (p.ready || p.gather_out || p.bias)) return hipErrorInvalidValue;
+  // (tiles of at most 128 x 224: the larger ones spill registers with 512 threads)
+  if constexpr (MC2_GATHER_WAVES && AK && lds_stages<BM, BN>() == 3 && BM * BN <= 128 * 224) {
+    // whole steps (the copy wavefronts count them as the fast loop does)
+    if (p.gather_out && vec && !p.bias && !p.rs_out && p.k % 64 == 0 && p.kseg == p.k) {
+      gemm16_gather_kernel<BM, BN, BKM, DT><<<(unsigned)tiles, 2 * kThreads, 0, s>>>(p, c);
+      return hipGetLastError();
+    }
+  }
   if constexpr (AK && lds_stages<BM, BN>() == 3) {
     if (p.gather_out) {
       if (vec) gemm16_kernel<BM, BN, AK, BKM, true, DT, false, true><<<(unsigned)tiles, kThreads, 0, s>>>(p, c);

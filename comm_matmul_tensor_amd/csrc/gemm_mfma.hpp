@@ -326,7 +326,7 @@ __device__ __forceinline__ void compute_step(const uint8_t* As, const uint8_t* B
 // Copies the A tile of the step held in LDS to gather_out (K-contiguous A).
 template <int E, int BM>
 __device__ __forceinline__ void copy_gather(const uint8_t* As, void* gout, int64_t m, int64_t k, int64_t m0,
-                                            int64_t k0) {
+                                            int64_t k0, int tid) {
   using T = typename Elem<E>::T;
   constexpr int CH = 16 / E;
   constexpr int NG = BM / 32;
@@ -337,19 +337,19 @@ __device__ __forceinline__ void copy_gather(const uint8_t* As, void* gout, int64
     u32x4 v[NG];
 #pragma unroll
     for (int i = 0; i < NG; i++) {
-      const int c = threadIdx.x + i * kThreads;
+      const int c = tid + i * kThreads;
       v[i] = *reinterpret_cast<const u32x4*>(As + swz(c / 8, c % 8));
     }
 #pragma unroll
     for (int i = 0; i < NG; i++) {
-      const int c = threadIdx.x + i * kThreads;
+      const int c = tid + i * kThreads;
       store_out16(static_cast<T*>(gout) + (m0 + c / 8) * k + k0 + CH * (c % 8), v[i]);
     }
     return;
   }
 #pragma unroll
   for (int i = 0; i < NG; i++) {
-    const int c = threadIdx.x + i * kThreads, row = c / 8, chunk = c % 8;
+    const int c = tid + i * kThreads, row = c / 8, chunk = c % 8;
     const int64_t grow = m0 + row, gk = k0 + CH * chunk;
     if (grow >= m || gk >= k) continue;
     const u32x4 v = *reinterpret_cast<const u32x4*>(As + swz(row, chunk));
@@ -576,7 +576,10 @@ struct FragReader {
 //   read half 1 of step kt; MFMAs of half 0;
 //   wait for the DMA of step kt+1, barrier;
 //   issue the DMA of step kt+2; read half 0 of step kt+1; MFMAs of half 1.
-template <int E, int BM, int BN, bool AK, bool BKM, bool GATHER, bool ARR, int NS, typename Ops>
+// TAG: distinguishes the specialisation the gather-wavefront kernel uses from
+// the one run_mainloop uses (with one shared specialisation the compiler
+// rejected the second use as a substitution failure).
+template <int E, int BM, int BN, bool AK, bool BKM, bool GATHER, bool ARR, int NS, typename Ops, int TAG = 0>
 __device__ __forceinline__ void mainloop_fast(const Problem& p, int64_t m0, int64_t n0, int gather_phase,
                                               int gather_every, uint8_t* L0, uint8_t* L1, uint8_t* L2,
                                               typename Ops::Acc (&acc)[BM / 32][BN / 32]) {
@@ -698,7 +701,7 @@ __device__ __forceinline__ void mainloop_fast(const Problem& p, int64_t m0, int6
     // gather_out copy of this step's A tile (NG stores per thread, older than
     // every load issued below, so the wait below covers them)
     if (GATHER && kt == next_gather) {
-      copy_gather<E, BM>(cur, p.gather_out, p.m, p.k, m0, (int64_t)kt * BK);
+      copy_gather<E, BM>(cur, p.gather_out, p.m, p.k, m0, (int64_t)kt * BK, (int)threadIdx.x);
       next_gather += gather_every;
     }
     if constexpr (ARR) {
@@ -726,7 +729,7 @@ __device__ __forceinline__ void mainloop_fast(const Problem& p, int64_t m0, int6
     constexpr bool FULL = decltype(FULL_)::value;
     const bool dma2 = FULL || kt + 2 < nk;
     if (GATHER && kt == next_gather) {
-      copy_gather<E, BM>(cur, p.gather_out, p.m, p.k, m0, (int64_t)kt * BK);
+      copy_gather<E, BM>(cur, p.gather_out, p.m, p.k, m0, (int64_t)kt * BK, (int)threadIdx.x);
       next_gather += gather_every;
     }
     __builtin_amdgcn_sched_barrier(0);
@@ -830,7 +833,7 @@ __device__ __forceinline__ void mainloop_checked(const Problem& p, int64_t m0, i
       loadB((int64_t)(kt + 1) * BK, rb);
     }
     if (AK && gather_every > 0 && kt % gather_every == gather_phase)
-      copy_gather<E, BM>(cur, p.gather_out, p.m, p.k, m0, (int64_t)kt * BK);
+      copy_gather<E, BM>(cur, p.gather_out, p.m, p.k, m0, (int64_t)kt * BK, (int)threadIdx.x);
     compute_step<BM, BN, Ops>(cur, cur + kATile, acc);
     if (kt + 1 < nk) {
       la.store(nxt, ra);
@@ -881,6 +884,15 @@ __device__ __forceinline__ void run_mainloop(const Problem& p, int64_t m0, int64
   } else {
     mainloop_checked<E, BM, BN, AK, BKM, Ops>(p, m0, n0, tn, gather_every, L0, L1, acc);
   }
+}
+
+// The three-stage fast loop without the gather copy or arrival wait, for
+// callers that have checked its conditions (whole steps, one K segment per
+// step, 16-byte aligned rows, buffers within the DMA limits).
+template <int E, int BM, int BN, bool AK, bool BKM, typename Ops>
+__device__ __forceinline__ void run_fast_loop(const Problem& p, int64_t m0, int64_t n0, uint8_t* L0, uint8_t* L1,
+                                              uint8_t* L2, typename Ops::Acc (&acc)[BM / 32][BN / 32]) {
+  mainloop_fast<E, BM, BN, AK, BKM, false, false, 3, Ops, 1>(p, m0, n0, 0, 0, L0, L1, L2, acc);
 }
 
 // Choose the XCD-aware tile of workgroup blockIdx.x.  Workgroup b runs on XCD
@@ -953,24 +965,25 @@ __device__ __forceinline__ const uint16_t* staged_chunk(const uint16_t* h0, cons
 // tests, so its LDS reads are issued together instead of one wait per chunk
 // (16 chunks at a time: the 256 x 256 tile has 32; not after the gather
 // copy, where it measured slower); other tiles take the checked loop.
-template <int BM, int BN>
-constexpr bool unrolled_store() { return BM * (BN / 8) % kThreads == 0 && BM * (BN / 8) / kThreads <= 32; }
+template <int BM, int BN, int NTH = kThreads>
+constexpr bool unrolled_store() { return BM * (BN / 8) % NTH == 0 && BM * (BN / 8) / NTH <= 32; }
 
-template <int BM, int BN, bool VEC>
+// NTH: the threads of the workgroup that share the stores.
+template <int BM, int BN, bool VEC, int NTH = kThreads>
 __device__ __forceinline__ void store_c16_tile(const uint16_t* h0, const uint16_t* h1, uint16_t* C, int64_t m,
                                                int64_t n, int64_t m0, int64_t n0, bool unrolled = true) {
   constexpr int kRowChunks = BN / 8;
-  if constexpr (VEC && unrolled_store<BM, BN>()) {
+  if constexpr (VEC && unrolled_store<BM, BN, NTH>()) {
     if (unrolled && m0 + BM <= m && n0 + BN <= n) {
 #pragma unroll 16
-      for (int it = 0; it < BM * kRowChunks / kThreads; it++) {
-        const int c = threadIdx.x + it * kThreads, row = c / kRowChunks, col = (c % kRowChunks) * 8;
+      for (int it = 0; it < BM * kRowChunks / NTH; it++) {
+        const int c = threadIdx.x + it * NTH, row = c / kRowChunks, col = (c % kRowChunks) * 8;
         store_out16(C + (m0 + row) * n + n0 + col, *reinterpret_cast<const u32x4*>(staged_chunk<BM, BN>(h0, h1, row, col)));
       }
       return;
     }
   }
-  for (int c = threadIdx.x; c < BM * kRowChunks; c += kThreads) {
+  for (int c = threadIdx.x; c < BM * kRowChunks; c += NTH) {
     const int row = c / kRowChunks, col = (c % kRowChunks) * 8;
     const int64_t grow = m0 + row, gcol = n0 + col;
     if (grow >= m) continue;
