@@ -640,8 +640,9 @@ def summarize(d, write_traffic):
         lines.append("")
     print("\n".join(lines))
     if write_traffic:
-        # the fused AllGatherMatmul: bf16, 128 x 224 tiles, no arrival wait, gather copy on
-        ag = [k for k in counters if k.startswith("gemm16_kernel<128, 224, true, false, true, 2, false, true>")]
+        # the fused AllGatherMatmul: bf16, 128 x 224 tiles, B N-contiguous, gather_out written by
+        # the copy wavefronts
+        ag = [k for k in counters if k.startswith("gemm16_gather_kernel<128, 224, false, 2>")]
         if not ag or not all(c in counters[ag[0]] for c in ("FETCH_SIZE", "WRITE_SIZE")):
             raise SystemExit("no FETCH_SIZE / WRITE_SIZE for the AllGatherMatmul kernel in " + d)
         cs = counters[ag[0]]
