@@ -83,6 +83,35 @@ mc2_status arrival_setup(int dev, DeviceState** out, unsigned* epoch = nullptr) 
 
 size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
+#ifndef MC2_PREFETCH_SIDE
+#define MC2_PREFETCH_SIDE 1
+#endif
+
+// The int8 GEMM (K3) with its weight's pass through the last-level cache
+// (K9, prefetch.hip).  With the device's side stream (side != NULL), K9 runs
+// beside K3 instead of before it: it streams the weight ahead of the GEMM's
+// K loop from the CU slots K3 leaves free, and `st` waits for it only after
+// K3, so it is off the critical path.  Without (the no-allocation entry
+// point, which creates no stream), K9 runs first on `st`.
+mc2_status gemm_i8_prefetched(const GemmI8Args& ga, int64_t w_bytes, DeviceState* side, hipStream_t st,
+                              const char* where) {
+  hipError_t e;
+  if (side) {
+    std::lock_guard<std::mutex> fork_lock(side->fork_mutex);
+    e = hipEventRecord(side->fork, st);
+    if (e == hipSuccess) e = launch_gemm_i8(ga, st);
+    if (e == hipSuccess) e = hipStreamWaitEvent(side->copy_stream, side->fork, 0);
+    if (e == hipSuccess) e = launch_prefetch(ga.b, w_bytes, side->copy_stream);
+    if (e == hipSuccess) e = hipEventRecord(side->join, side->copy_stream);
+    if (e == hipSuccess) e = hipStreamWaitEvent(st, side->join, 0);
+  } else {
+    e = launch_prefetch(ga.b, w_bytes, st);
+    if (e == hipSuccess) e = launch_gemm_i8(ga, st);
+  }
+  if (e != hipSuccess) return hip_fail(e, where);
+  return MC2_OK;
+}
+
 }  // namespace
 
 // The current device must be a gfx950 (MI355X class) GPU.
@@ -153,10 +182,11 @@ mc2_status alltoall_quant_matmul_run(const void* x1, int rank_size, int64_t bs, 
   qa.dtype = dt(x1_dtype);
   hipError_t e = launch_permute_quant(qa, st);
   if (e != hipSuccess) return hip_fail(e, "alltoall_quant_matmul quant launch");
-  // The weight passes through the caches right before the GEMM reads it: A16W4
-  // widens it there (int4 -> int8), A16W8 streams it once (K9).  (K9 on a
-  // side stream beside K2 measured slower: both kernels slowed down, and the
-  // join before the GEMM cost about 11 us.)
+  // The weight passes through the caches just before or while the GEMM reads
+  // it: A16W4 widens it (int4 -> int8) after the quantisation, A16W8 streams it
+  // once (K9) beside the GEMM (gemm_i8_prefetched).  (K9 on the side stream
+  // beside K2, with the GEMM waiting for both, measured slower: both kernels
+  // slowed down and the join before the GEMM cost about 11 us.)
   if (w4) {
     WidenArgs wa{};
     wa.src[0] = reinterpret_cast<const uint8_t*>(x2);
@@ -165,9 +195,6 @@ mc2_status alltoall_quant_matmul_run(const void* x1, int rank_size, int64_t bs, 
     e = launch_widen_int4(wa, st);
     if (e != hipSuccess) return hip_fail(e, "alltoall_quant_matmul_a16w4 widening launch");
     x2 = x2w;
-  } else {
-    e = launch_prefetch(x2, cols * n, st);
-    if (e != hipSuccess) return hip_fail(e, "alltoall_quant_matmul prefetch launch");
   }
 
   GemmI8Args ga{};
@@ -183,9 +210,16 @@ mc2_status alltoall_quant_matmul_run(const void* x1, int rank_size, int64_t bs, 
   ga.k = cols;
   ga.dtype = dt(x1_dtype);
   ga.partials = reinterpret_cast<int32_t*>(ws);
-  e = launch_gemm_i8(ga, st);
-  if (e != hipSuccess) return hip_fail(e, "alltoall_quant_matmul gemm launch");
-  return MC2_OK;
+  if (w4) {
+    e = launch_gemm_i8(ga, st);
+    if (e != hipSuccess) return hip_fail(e, "alltoall_quant_matmul gemm launch");
+    return MC2_OK;
+  }
+  // the side stream is set up once per device; the no-allocation entry point
+  // (device_checked) creates none and runs K9 first
+  DeviceState* side = nullptr;
+  if (MC2_PREFETCH_SIDE && !device_checked && (s = arrival_setup(dev, &side)) != MC2_OK) return s;
+  return gemm_i8_prefetched(ga, cols * n, side, st, "alltoall_quant_matmul gemm launch");
 }
 
 }  // namespace mc2
@@ -665,10 +699,9 @@ mc2_status mc2_alltoall_quant_matmul_static(const int8_t* x1, int rank_size, int
   ga.n = n;
   ga.k = cols;
   ga.dtype = dt(out_dtype);
-  hipError_t e = launch_prefetch(x2, cols * n, static_cast<hipStream_t>(stream));  // the weight into the caches (K9)
-  if (e == hipSuccess) e = launch_gemm_i8(ga, static_cast<hipStream_t>(stream));
-  if (e != hipSuccess) return hip_fail(e, "alltoall_quant_matmul_static launch");
-  return MC2_OK;
+  DeviceState* side = nullptr;
+  if (MC2_PREFETCH_SIDE && (s = arrival_setup(dev, &side)) != MC2_OK) return s;
+  return gemm_i8_prefetched(ga, cols * n, side, static_cast<hipStream_t>(stream), "alltoall_quant_matmul_static launch");
 }
 
 }  // extern "C"
