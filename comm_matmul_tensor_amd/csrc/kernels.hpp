@@ -147,7 +147,7 @@ struct WidenArgs {
 };
 hipError_t launch_widen_int4(const WidenArgs& a, hipStream_t s);
 
-// ---- K9: one streaming read of `bytes` at p (16-byte aligned) into the caches
+// ---- K9: one streaming read of `bytes` at p (16-byte aligned) into the caches (no writes)
 hipError_t launch_prefetch(const void* p, int64_t bytes, hipStream_t s);
 
 }  // namespace mc2

@@ -1,6 +1,5 @@
 // K9: streaming read of the int8 GEMM's weight into the last-level cache
-// (MALL) right before the GEMM, in AlltoAllQuantMatmul (A16W8 and full
-// quantisation).
+// (MALL) for the GEMM, in AlltoAllQuantMatmul (A16W8 and full quantisation).
 //
 // The GEMM reads B = x2 (r h, n) int8 step by step, 128 rows of K at a time,
 // from 256 workgroups that drift apart over the K loop.  Fetched from HBM in
@@ -9,10 +8,12 @@
 // its loads then return at last-level-cache latency, and the workgroups of an
 // XCD stay close enough to share their L2 (fetched bytes: 890-990 MB against
 // the 504 MB floor).  One linear pass over x2 (235 MB at the A16W8 shape)
-// costs about 40 us.  The bytes are only loaded: each thread folds its loads
-// into one word and stores it (to a library-owned array nothing reads) only
-// if it equals a value passed at launch, so the loads cannot be dropped and
-// next to nothing is written.
+// takes about 40 us; run on a side stream beside the GEMM (which leaves CU
+// slots free: one 364-register wavefront per SIMD) it stays ahead of the
+// GEMM's K loop and costs the call little.  The bytes are only loaded: each
+// thread folds its loads into one word and stores it (to a library-owned
+// array nothing reads) only if it equals a value passed at launch, so the
+// loads cannot be dropped and next to nothing is written.
 #include "device.hpp"
 #include "kernels.hpp"
 
