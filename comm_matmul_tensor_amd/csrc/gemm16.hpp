@@ -221,22 +221,29 @@ __global__ __launch_bounds__(kThreads, 1) void gemm16_kernel(Problem p, void* c)
 }
 
 // AllGatherMatmul with gather_out on the fast path (A K-contiguous, three
-// stages, no bias or arrival): 512 threads.  Wavefronts 0-3 run the
-// four-wavefront GEMM without the gather copy; wavefronts 4-7 copy A tiles
-// from the LDS stages to gather_out.  The A tile of step kt sits in stage
-// kt % 3 from the main loop's barrier kt (the prologue's counted as 0), after
-// which every wavefront has waited for its DMA, until barrier kt + 1, after
-// which the DMA of step kt + 3 may overwrite it; the copy wavefronts read it
-// in that window, so they go through the same barriers (the loop's nk + 1,
-// then the one that ends the staging of C).  Their stores count only in
-// their own wavefronts' vmcnt, so the GEMM's DMA waits never wait for them
-// (with the copy inside the GEMM's wavefronts every step that copies waited
-// for its stores).  The workgroup of tile column tn copies the steps kt with
-// kt % tiles_n == tn, so the tiles of a row share the copy of its A.  All 512
-// threads then store C.  AllGatherMatmul 8 x (512, 4096) @ (4096, 1792):
-// 62.1 -> 56.2 us with its inputs in the caches (53.5 us without gather_out),
-// 77.7 -> 77.1 us after a 512 MB write, 72.4 -> 70.9 us in the benchmark
-// step; the API page's 8 x (16, 512) @ (512, 64) example 19.8 -> 15.9 us.
+// stages, no bias or arrival): 512 threads.  Wavefronts 0-3 run the GEMM's
+// reads of the LDS stages and its MFMAs (mainloop_fast without loads);
+// wavefronts 4-7 issue every load into the stages, wait for them before each
+// barrier, and copy A tiles from the stages to gather_out (dma_waves_loop).
+// The A tile of step kt sits in stage kt % 3 from the main loop's barrier kt
+// (the prologue's counted as 0) until barrier kt + 1, after which the loads
+// of step kt + 3 may overwrite it; the copy reads it in that window.  Both
+// groups go through the same barriers (the loop's nk + 1, then the one that
+// ends the staging of C).  The copy's stores count only in the loading
+// wavefronts' vmcnt, and the GEMM wavefronts issue no global access in the
+// loop at all (with the copy inside the GEMM's wavefronts every step that
+// copies waited for its stores).  The workgroup of tile column tn copies the
+// steps kt with kt % tiles_n == tn, so the tiles of a row share the copy of
+// its A.  All 512 threads then store C.  AllGatherMatmul 8 x (512, 4096) @
+// (4096, 1792), us: with its inputs in the caches 62.1 (copy in the GEMM's
+// wavefronts) -> 55.0 (copy in wavefronts 4-7, loads in 0-3) -> 52.0 (loads
+// also in 4-7; 51.9 without gather_out); after a 512 MB write 77.7 -> 77.1
+// -> 77.8; in the benchmark step 72.4 -> 70.0 -> 70.0.  MC2_DMA_WAVES=0
+// builds the variant with the loads in wavefronts 0-3.
+#ifndef MC2_DMA_WAVES
+#define MC2_DMA_WAVES 1
+#endif
+
 template <int BM, int BN, bool BKM, int DT>
 __global__ __launch_bounds__(2 * kThreads, 1) void gemm16_gather_kernel(Problem p, void* c) {
   constexpr int FM = BM / 32, FN = BN / 32;
@@ -259,10 +266,17 @@ __global__ __launch_bounds__(2 * kThreads, 1) void gemm16_gather_kernel(Problem 
       for (int j = 0; j < FN; j++) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
     // the fast loop without the gather copy (the host launches this kernel
     // only where it applies)
+#if MC2_DMA_WAVES
+    run_loop_nodma<2, BM, BN, true, BKM, Ops16<DT>>(p, m0, n0, s0, s1, s2, acc);
+#else
     run_fast_loop<2, BM, BN, true, BKM, Ops16<DT>>(p, m0, n0, s0, s1, s2, acc);
+#endif
     stage_c16<BM, BN, DT>(h0, h1, [&](int i, int j, int r, int, int) { return acc[i][j][r]; });
   } else {
     const int tid = (int)threadIdx.x - kThreads;
+#if MC2_DMA_WAVES
+    dma_waves_loop<2, BM, BN, BKM>(p, m0, n0, tn, tiles_n, s0, s1, s2, tid);
+#else
     const int nk = (int)(p.k / BK);
     int next = tn;
     for (int kt = 0; kt < nk; kt++) {
@@ -274,6 +288,7 @@ __global__ __launch_bounds__(2 * kThreads, 1) void gemm16_gather_kernel(Problem 
       }
     }
     lds_barrier();   // barrier nk
+#endif
     __syncthreads();  // the one that ends the staging of C
   }
   store_c16_tile<BM, BN, true, 2 * kThreads>(h0, h1, static_cast<uint16_t*>(c), p.m, p.n, m0, n0);

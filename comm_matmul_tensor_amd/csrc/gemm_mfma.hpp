@@ -323,8 +323,39 @@ __device__ __forceinline__ void compute_step(const uint8_t* As, const uint8_t* B
   }
 }
 
+// Up to four 16-byte LDS reads (LDS byte addresses a[0..N)) and the wait for
+// them, in one asm block.  For reads of a stage that an earlier barrier has
+// ordered after its loads: the compiler, which cannot tell the targets of
+// loads into LDS still in flight from these addresses, would otherwise wait
+// for those loads first.
+template <int N>
+__device__ __forceinline__ void lds_read_b128_waited(u32x4* v, const uint32_t* a) {
+  static_assert(N >= 1 && N <= 4, "one to four reads");
+  if constexpr (N == 4) {
+    asm volatile(
+        "ds_read_b128 %0, %4\n\tds_read_b128 %1, %5\n\tds_read_b128 %2, %6\n\tds_read_b128 %3, %7\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]), "=&v"(v[3])
+        : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3])
+        : "memory");
+  } else if constexpr (N == 3) {
+    asm volatile("ds_read_b128 %0, %3\n\tds_read_b128 %1, %4\n\tds_read_b128 %2, %5\n\ts_waitcnt lgkmcnt(0)"
+                 : "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2])
+                 : "v"(a[0]), "v"(a[1]), "v"(a[2])
+                 : "memory");
+  } else if constexpr (N == 2) {
+    asm volatile("ds_read_b128 %0, %2\n\tds_read_b128 %1, %3\n\ts_waitcnt lgkmcnt(0)"
+                 : "=&v"(v[0]), "=&v"(v[1])
+                 : "v"(a[0]), "v"(a[1])
+                 : "memory");
+  } else {
+    asm volatile("ds_read_b128 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=&v"(v[0]) : "v"(a[0]) : "memory");
+  }
+}
+
 // Copies the A tile of the step held in LDS to gather_out (K-contiguous A).
-template <int E, int BM>
+// ASMRD: the whole-tile path reads the stage with lds_read_b128_waited.
+template <int E, int BM, bool ASMRD = false>
 __device__ __forceinline__ void copy_gather(const uint8_t* As, void* gout, int64_t m, int64_t k, int64_t m0,
                                             int64_t k0, int tid) {
   using T = typename Elem<E>::T;
@@ -335,10 +366,26 @@ __device__ __forceinline__ void copy_gather(const uint8_t* As, void* gout, int64
     // reads first, one wait, then the stores (no per-lane branches, which
     // made every chunk wait for its own read and for every earlier one)
     u32x4 v[NG];
+    if constexpr (ASMRD) {
+      uint32_t a[NG];
 #pragma unroll
-    for (int i = 0; i < NG; i++) {
-      const int c = tid + i * kThreads;
-      v[i] = *reinterpret_cast<const u32x4*>(As + swz(c / 8, c % 8));
+      for (int i = 0; i < NG; i++) {
+        const int c = tid + i * kThreads;
+        a[i] = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint8_t*)(As + swz(c / 8, c % 8));
+      }
+#pragma unroll
+      for (int i = 0; i < NG; i += 4) {  // groups of four, then the rest
+        if (i + 4 <= NG) lds_read_b128_waited<4>(v + i, a + i);
+        else if (NG - i == 3) lds_read_b128_waited<3>(v + i, a + i);
+        else if (NG - i == 2) lds_read_b128_waited<2>(v + i, a + i);
+        else lds_read_b128_waited<1>(v + i, a + i);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < NG; i++) {
+        const int c = tid + i * kThreads;
+        v[i] = *reinterpret_cast<const u32x4*>(As + swz(c / 8, c % 8));
+      }
     }
 #pragma unroll
     for (int i = 0; i < NG; i++) {
@@ -433,13 +480,14 @@ struct DmaOperand {
   // K-contiguous operand: row r of the tile is matrix row mn0 + r, found in
   // the row blocks `parts` (rows_per_part rows each, ld_bytes per row).
   // part_bytes: bytes of each row block's buffer (the resource size).
+  // t: the thread's index among the kThreads threads that issue the loads.
   __device__ __forceinline__ void init_k(const void* const* parts, int64_t rows_per_part, int64_t ld_bytes,
-                                         int64_t mn0, int64_t mn_ext, int64_t part_bytes) {
-    const int w = __builtin_amdgcn_readfirstlane((int)(threadIdx.x / 64));
+                                         int64_t mn0, int64_t mn_ext, int64_t part_bytes, int t) {
+    const int w = __builtin_amdgcn_readfirstlane(t / 64);
     lds_wave = 1024 * w;
 #pragma unroll
     for (int i = 0; i < kN; i++) {
-      const int s = threadIdx.x + kThreads * i, row = s / 8, c = (s % 8) ^ (row & 7);
+      const int s = t + kThreads * i, row = s / 8, c = (s % 8) ^ (row & 7);
       const int64_t r = mn0 + row < mn_ext ? mn0 + row : mn_ext - 1;
       // the instruction's 8 rows (32 i + 8 w ...) lie in one row block
       int64_t g0 = mn0 + 32 * i + 8 * w;
@@ -455,12 +503,12 @@ struct DmaOperand {
   // MN-contiguous operand stored (k_ext, mn) with ld_bytes between k rows;
   // mn_ext is a multiple of the 16-byte chunk.
   __device__ __forceinline__ void init_mn(const void* base, int64_t ld_bytes, int64_t k_ext, int64_t mn0,
-                                          int64_t mn_ext) {
+                                          int64_t mn_ext, int t) {
     constexpr int CH = 16 / E, kChunks = R * E / 16;
-    lds_wave = 1024 * __builtin_amdgcn_readfirstlane((int)(threadIdx.x / 64));
+    lds_wave = 1024 * __builtin_amdgcn_readfirstlane(t / 64);
 #pragma unroll
     for (int i = 0; i < kN; i++) {
-      const int s = threadIdx.x + kThreads * i, k = s / kChunks, c = (s % kChunks) ^ mn_swz<E, R>(k);
+      const int s = t + kThreads * i, k = s / kChunks, c = (s % kChunks) ^ mn_swz<E, R>(k);
       int64_t col = mn0 + (int64_t)c * CH;
       if (col + CH > mn_ext) col = mn_ext - CH;
       rsrc[i] = make_rsrc(base, k_ext * ld_bytes);
@@ -579,12 +627,19 @@ struct FragReader {
 // TAG: distinguishes the specialisation the gather-wavefront kernel uses from
 // the one run_mainloop uses (with one shared specialisation the compiler
 // rejected the second use as a substitution failure).
-template <int E, int BM, int BN, bool AK, bool BKM, bool GATHER, bool ARR, int NS, typename Ops, int TAG = 0>
+//
+// NODMA: another group of four wavefronts issues every DMA and waits for it
+// before each barrier (dma_waves_loop); these wavefronts only read the
+// stages, multiply and meet the barriers.
+template <int E, int BM, int BN, bool AK, bool BKM, bool GATHER, bool ARR, int NS, typename Ops, int TAG = 0,
+          bool NODMA = false>
 __device__ __forceinline__ void mainloop_fast(const Problem& p, int64_t m0, int64_t n0, int gather_phase,
                                               int gather_every, uint8_t* L0, uint8_t* L1, uint8_t* L2,
                                               typename Ops::Acc (&acc)[BM / 32][BN / 32]) {
   static_assert(!ARR || (AK && !GATHER), "arrival needs a K-contiguous A and no gather copy");
   static_assert(NS == 3 || (NS == 2 && !ARR), "two stages: no arrival wait");
+  static_assert(!NODMA || (NS == 3 && !ARR && !GATHER), "loads from other wavefronts: three stages only");
+  const int tid = (int)threadIdx.x;
   constexpr int BK = kRowBytes / E;  // K elements per step
   constexpr int kATile = BM * kRowBytes;
   constexpr int WM = BM / 2, WN = BN / 2, FM = WM / 16, FN = WN / 16;
@@ -596,18 +651,20 @@ __device__ __forceinline__ void mainloop_fast(const Problem& p, int64_t m0, int6
   DA da_shards;  // arrival: A from the shards, for a wavefront whose wait timed out
   if constexpr (ARR) {
     const void* arrived[1] = {p.arrived};
-    da.init_k(arrived, p.m, p.k * E, m0, p.m, p.m * p.k * E);
-    da_shards.init_k(p.a_parts, p.rows_per_part, p.a_ld, m0, p.m, p.a_part_bytes);
+    da.init_k(arrived, p.m, p.k * E, m0, p.m, p.m * p.k * E, tid);
+    da_shards.init_k(p.a_parts, p.rows_per_part, p.a_ld, m0, p.m, p.a_part_bytes, tid);
+  } else if constexpr (NODMA) {
   } else if constexpr (AK) {
-    da.init_k(p.a_parts, p.rows_per_part, p.a_ld, m0, p.m, p.a_part_bytes);
+    da.init_k(p.a_parts, p.rows_per_part, p.a_ld, m0, p.m, p.a_part_bytes, tid);
   } else {
-    da.init_mn(p.a_parts[0], p.m * E, p.k, m0, p.m);
+    da.init_mn(p.a_parts[0], p.m * E, p.k, m0, p.m, tid);
   }
-  if constexpr (BKM) {
+  if constexpr (NODMA) {
+  } else if constexpr (BKM) {
     const void* bparts[1] = {p.b};
-    db.init_k(bparts, p.n, p.k * E, n0, p.n, p.n * p.k * E);
+    db.init_k(bparts, p.n, p.k * E, n0, p.n, p.n * p.k * E, tid);
   } else {
-    db.init_mn(p.b, p.n * E, p.k, n0, p.n);
+    db.init_mn(p.b, p.n * E, p.k, n0, p.n, tid);
   }
   const int wave = threadIdx.x / 64, wm = wave / 2, wn = wave % 2;
   FragReader<E, BM, AK, FM> ra;
@@ -650,9 +707,11 @@ __device__ __forceinline__ void mainloop_fast(const Problem& p, int64_t m0, int6
 
   u32x4 fa0[FM], fb0[FN], fa1[FM], fb1[FN];
   auto dma = [&](uint8_t* L, int kt) {
-    da.issue(L, a_next);
-    db.issue(L + kATile, kt * db.step_bytes);
-    advance_a();
+    if constexpr (!NODMA) {
+      da.issue(L, a_next);
+      db.issue(L + kATile, kt * db.step_bytes);
+      advance_a();
+    }
   };
   // One K half: the FM x FN MFMAs on (fa, fb), with DMA instructions
   // [d0, d1) of step kt_dma (when dma_on) and the FM + FN fragment reads of
@@ -712,12 +771,14 @@ __device__ __forceinline__ void mainloop_fast(const Problem& p, int64_t m0, int6
     __builtin_amdgcn_sched_barrier(0);
     // half 0 of step kt; the DMA of step kt+2 (its stage was last read
     // before the previous barrier); reads of half 1 of step kt
-    half(fa0, fb0, C0(), CD(), dma2, nn, kt + 2, true, cur, 1, fa1, fb1);
-    if (dma2) advance_a();
+    half(fa0, fb0, C0(), CD(), dma2 && !NODMA, nn, kt + 2, true, cur, 1, fa1, fb1);
+    if (dma2 && !NODMA) advance_a();
     // the DMA of step kt+1 (issued during step kt-1) has landed; only this
     // step's may still fly
-    if (dma2) wait_vmcnt<ND>();
-    else wait_vmcnt<0>();
+    if constexpr (!NODMA) {
+      if (dma2) wait_vmcnt<ND>();
+      else wait_vmcnt<0>();
+    }
     lds_barrier();
     __builtin_amdgcn_sched_barrier(0);
     // half 1 of step kt; reads of half 0 of step kt+1
@@ -752,12 +813,14 @@ __device__ __forceinline__ void mainloop_fast(const Problem& p, int64_t m0, int6
     if (nk > 1 && 1 % sps == 0) wait_step(1);
     if (!fell_back && nk > 2 && 2 % sps == 0) pv = poll(2);
   }
-  dma(L0, 0);
-  if (nk > 1) {
-    dma(L1, 1);
-    wait_vmcnt<ND>();
-  } else {
-    wait_vmcnt<0>();
+  if constexpr (!NODMA) {
+    dma(L0, 0);
+    if (nk > 1) {
+      dma(L1, 1);
+      wait_vmcnt<ND>();
+    } else {
+      wait_vmcnt<0>();
+    }
   }
   lds_barrier();
   ra.read(L0, 0, fa0);
@@ -893,6 +956,89 @@ template <int E, int BM, int BN, bool AK, bool BKM, typename Ops>
 __device__ __forceinline__ void run_fast_loop(const Problem& p, int64_t m0, int64_t n0, uint8_t* L0, uint8_t* L1,
                                               uint8_t* L2, typename Ops::Acc (&acc)[BM / 32][BN / 32]) {
   mainloop_fast<E, BM, BN, AK, BKM, false, false, 3, Ops, 1>(p, m0, n0, 0, 0, L0, L1, L2, acc);
+}
+
+// The same loop with its loads issued by another group of four wavefronts
+// (dma_waves_loop, run beside it in the same workgroup).
+template <int E, int BM, int BN, bool AK, bool BKM, typename Ops>
+__device__ __forceinline__ void run_loop_nodma(const Problem& p, int64_t m0, int64_t n0, uint8_t* L0, uint8_t* L1,
+                                               uint8_t* L2, typename Ops::Acc (&acc)[BM / 32][BN / 32]) {
+  mainloop_fast<E, BM, BN, AK, BKM, false, false, 3, Ops, 2, true>(p, m0, n0, 0, 0, L0, L1, L2, acc);
+}
+
+// The loads of the three-stage loop for a group of four wavefronts that run
+// mainloop_fast<..., NODMA> (tid: thread index within this group), plus the
+// gather_out copy (the steps kt with kt % tiles_n == tn).  It meets the same
+// barriers: the prologue's (after the loads of step 0 have landed), then one
+// per step kt, before which the loads of step kt + 1 have landed.  After the
+// barrier of step kt - 1 (the prologue's for kt = 0) no wavefront reads step
+// kt - 1's stage any more, so the loads of step kt + 2 go there; the copy
+// reads step kt's stage, which holds it until the barrier of step kt + 1.
+// Loads and stores leave vmcnt in the order issued, so the wait for step
+// kt + 1 lets this step's loads (ND per thread) and copy stores (NG, each
+// lane one per 16-byte chunk of a whole tile; a partial tile waits longer)
+// stay in flight.
+template <int E, int BM, int BN, bool BKM>
+__device__ __forceinline__ void dma_waves_loop(const Problem& p, int64_t m0, int64_t n0, int tn, int tiles_n,
+                                               uint8_t* L0, uint8_t* L1, uint8_t* L2, int tid) {
+  constexpr int BK = kRowBytes / E;
+  constexpr int kATile = BM * kRowBytes;
+  using DA = DmaOperand<E, BM, true>;
+  using DB = DmaOperand<E, BN, BKM>;
+  constexpr int ND = DA::kN + DB::kN, NG = BM / 32;
+  DA da;
+  DB db;
+  da.init_k(p.a_parts, p.rows_per_part, p.a_ld, m0, p.m, p.a_part_bytes, tid);
+  if constexpr (BKM) {
+    const void* bparts[1] = {p.b};
+    db.init_k(bparts, p.n, p.k * E, n0, p.n, p.n * p.k * E, tid);
+  } else {
+    db.init_mn(p.b, p.n * E, p.k, n0, p.n, tid);
+  }
+  const int nk = (int)(p.k / BK);
+  const bool whole = m0 + BM <= p.m;  // the copy's whole-tile path: NG stores per lane
+  const bool copy = p.gather_out != nullptr;
+  int next = tn;
+  auto dma = [&](uint8_t* L, int kt) {
+    da.issue(L, (int64_t)kt * da.step_bytes);
+    db.issue(L + kATile, (int64_t)kt * db.step_bytes);
+  };
+  // cur: stage of step kt; nn: stage of step kt + 2
+  auto step = [&](int kt, uint8_t* cur, uint8_t* nn) {
+    const bool dma2 = kt + 2 < nk;
+    if (dma2) dma(nn, kt + 2);
+    const bool cp = copy && kt == next;
+    if (cp) {
+      copy_gather<E, BM, true>(cur, p.gather_out, p.m, p.k, m0, (int64_t)kt * BK, tid);
+      next += tiles_n;
+    }
+    if (kt + 1 < nk) {
+      if (dma2) {
+        if (cp && whole) wait_vmcnt<ND + NG>();
+        else wait_vmcnt<ND>();
+      } else {
+        if (cp && whole) wait_vmcnt<NG>();
+        else wait_vmcnt<0>();
+      }
+    }
+    lds_barrier();
+  };
+  dma(L0, 0);
+  if (nk > 1) {
+    dma(L1, 1);
+    wait_vmcnt<ND>();
+  } else {
+    wait_vmcnt<0>();
+  }
+  lds_barrier();
+  int kt = 0;
+  for (; kt + 3 <= nk; kt += 3) {
+    step(kt, L0, L2);
+    step(kt + 1, L1, L0);
+    step(kt + 2, L2, L1);
+  }
+  if (kt < nk) step(kt, L0, L2);
+  if (kt + 1 < nk) step(kt + 1, L1, L0);
 }
 
 // Choose the XCD-aware tile of workgroup blockIdx.x.  Workgroup b runs on XCD
