@@ -16,9 +16,9 @@
 //           exact in any order)
 //   s       = absmax / 127 (IEEE division)
 //   pass 2  q = clamp(rint(y / s), -127, 127) with the result of the IEEE
-//           division and round-half-to-even (computed as y * (1/s) with an
-//           exact fallback near ties, see quant_fast); an all-zero row gives
-//           s = 0 and q = 0.
+//           division and round-half-to-even (computed as rint(y (1/s) + 128)
+//           - 128 with the division as the fallback near ties, see quant8); an
+//           all-zero row gives s = 0 and q = 0.
 // HBM traffic: 2 B read + 1 B written per element, plus the 4-byte scale.
 #include "device.hpp"
 #include "kernels.hpp"
@@ -36,9 +36,28 @@ __device__ __forceinline__ float dec16(uint32_t bits) {
   else return f16_bits_to_f32(bits & 0xFFFFu);
 }
 
+// Maximum over the wavefront's 64 lanes of a non-negative value, as a
+// wave-uniform result: DPP steps within each row of 16 lanes (quad swaps,
+// half-row and row mirrors), then row 0 / 2's lane 15 into rows 1 / 3 and
+// lane 31 into rows 2 and 3, so lane 63 holds the maximum.  Lanes a DPP step
+// does not write read 0, which leaves their maximum unchanged.  (The
+// shuffle loop it replaces took six LDS round trips per token.)
+template <int CTRL, int ROWS>
+__device__ __forceinline__ float dpp_max_step(float v) {
+  return fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, ROWS, 0xF, false)));
+}
+__device__ __forceinline__ float wave_max_nonneg(float v) {
+  v = dpp_max_step<0xB1, 0xF>(v);   // quad_perm 1,0,3,2
+  v = dpp_max_step<0x4E, 0xF>(v);   // quad_perm 2,3,0,1
+  v = dpp_max_step<0x141, 0xF>(v);  // row_half_mirror
+  v = dpp_max_step<0x140, 0xF>(v);  // row_mirror
+  v = dpp_max_step<0x142, 0xA>(v);  // row_bcast:15
+  v = dpp_max_step<0x143, 0xC>(v);  // row_bcast:31
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+}
+
 __device__ __forceinline__ float block_max(float v, float* red) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
+  v = wave_max_nonneg(v);
   const int wave = threadIdx.x / 64, lane = threadIdx.x % 64;
   if (lane == 0) red[wave] = v;
   __syncthreads();
@@ -54,12 +73,48 @@ __device__ __forceinline__ int quant1(float y, float s) {
   return (int)r;
 }
 
-// Why y * (1 / s) may replace the IEEE quotient y / s: with inv = RN(1 / s),
-// RN(y * inv) is within |y / s| (2^-23 + 2^-48) <= 1.6e-5 of y / s when
-// |y / s| <= 127 (1 + 2^-23), and RN(y / s) is within 3.9e-6 of y / s, so
-// both round to the same integer unless y * inv lies within 2e-5 of a
-// half-integer.  The kernel flags every element within 3e-5 and redoes it
-// with the division.
+// The codes of eight values y (|y| <= amax, s = amax / 127 > 0, inv = RN(1 / s))
+// packed low element first, without a division where that is exact.
+//
+// rb = RN(y inv + 128) (one fma) lies within 1.9e-5 of RN(y / s) + 128: its
+// own rounding is at most 2^-17 (rb < 256), inv's relative error 2^-24
+// contributes at most |y / s| 2^-24 <= 7.6e-6 (|y / s| <= 127 (1 + 2^-24)),
+// and RN(y / s) is within 3.8e-6 of y / s.  So where rb is more than 3e-5
+// from a half-integer, rint(rb) = rint(RN(y / s)) + 128, an integer in
+// [1, 255]: v_cvt_pk_u8_f32 converts it exactly into its byte of the packed
+// word, and flipping bit 7 of each byte gives the two's-complement byte of
+// rint(rb) - 128.  Elements within 3e-5 of a half-integer (ties included)
+// take the IEEE division, each behind its own branch, so a wavefront runs a
+// division only for an element that some lane needs (all eight where s is
+// subnormal, fast = false, and the bound above does not hold).
+__device__ __forceinline__ u32x2 quant8(const float (&y)[8], float inv, float s, bool fast) {
+  constexpr float kNear = 0.49997f;
+  uint32_t w[2] = {0u, 0u};
+  float dmax = 0.0f;
+#pragma unroll
+  for (int e = 0; e < 8; e++) {
+    const float rb = __builtin_fmaf(y[e], inv, 128.0f);
+    const float ri = __builtin_rintf(rb);
+    dmax = fmaxf(dmax, __builtin_fabsf(rb - ri));
+    w[e / 4] = __builtin_amdgcn_cvt_pk_u8_f32(ri, e % 4, w[e / 4]);
+  }
+  u32x2 q = {w[0] ^ 0x80808080u, w[1] ^ 0x80808080u};
+  if (!fast || dmax >= kNear) {  // rare: the flagged elements again, with the division
+    uint32_t mb[8];
+#pragma unroll
+    for (int e = 0; e < 8; e++) {
+      const float rb = __builtin_fmaf(y[e], inv, 128.0f);
+      const float ri = __builtin_rintf(rb);
+      if (!fast || __builtin_fabsf(rb - ri) >= kNear) mb[e] = (uint32_t)quant1(y[e], s);
+      else mb[e] = (uint32_t)((int)ri - 128);  // ri in [1, 255] here
+    }
+#pragma unroll
+    for (int k = 0; k < 2; k++)
+      q[k] = (__builtin_amdgcn_perm(mb[4 * k + 3], mb[4 * k + 2], 0x0c0c0400u) << 16) |
+             __builtin_amdgcn_perm(mb[4 * k + 1], mb[4 * k], 0x0c0c0400u);
+  }
+  return q;
+}
 
 // Vector path: h % 16 == 0, so every 16-element unit of P lies inside one
 // source row and is 32-byte aligned.  1024 threads per token, each owning
@@ -67,13 +122,7 @@ __device__ __forceinline__ int quant1(float y, float s) {
 // the token's loads are issued first and y = P * smooth stays in registers
 // between the two passes.
 //
-// Pass 2 per element, with inv = 1/s:  qa = y * inv;  c = med3(qa, -127, 127);
-// m = c + 1.5 * 2^23, which rounds c to an integer with ties to even and
-// leaves that integer's two's-complement low byte in the low byte of m's bit
-// pattern (|c| <= 127 < 2^22), so the int8 code is one byte of m.  If any
-// |qa - rint(c)| of a unit reaches 0.5 - 3e-5, that element is near a
-// half-integer and the unit is recomputed with the IEEE division (see the
-// bound above).
+// Pass 2: quant8 on each half of a unit.
 template <int DT, int U>
 __global__ __launch_bounds__(kVecThreads, 2) void permute_quant_vec(QuantArgs a) {
   __shared__ float red[kVecThreads / 64];
@@ -130,8 +179,7 @@ __global__ __launch_bounds__(kVecThreads, 2) void permute_quant_vec(QuantArgs a)
       }
     }
   }
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off, 64));
+  amax = wave_max_nonneg(amax);
   if (threadIdx.x % 64 == 0) red[threadIdx.x / 64] = amax;
   __syncthreads();
   amax = red[0];
@@ -142,9 +190,7 @@ __global__ __launch_bounds__(kVecThreads, 2) void permute_quant_vec(QuantArgs a)
   // The error bound of the fast path needs |y / s| <= 127 (1 + 2^-23), which
   // holds when s is a normal number; rows with a subnormal scale use the division.
   const float inv = 1.0f / s;
-  const bool fast = s >= 1.17549435e-38f;  // uniform over the workgroup
-  constexpr float kMagic = 12582912.0f;    // 1.5 * 2^23
-
+  const bool fast = s >= 1.17549435e-38f;  // uniform over the workgroup (see quant8)
 #pragma unroll
   for (int v = 0; v < U; v++) {
     const int u = threadIdx.x + v * kVecThreads;
@@ -152,24 +198,15 @@ __global__ __launch_bounds__(kVecThreads, 2) void permute_quant_vec(QuantArgs a)
       const int64_t e = (int64_t)u * 16;
       u32x4 qv = {0u, 0u, 0u, 0u};
       if (amax > 0.0f) {
-        float dmax = 0.0f;
-        uint32_t mb[16];
 #pragma unroll
-        for (int i = 0; i < 16; i++) {
-          const float qa = y[v][i] * inv;
-          const float m = __builtin_amdgcn_fmed3f(qa, -127.0f, 127.0f) + kMagic;
-          dmax = fmaxf(dmax, __builtin_fabsf(qa - (m - kMagic)));
-          mb[i] = __float_as_uint(m);
+        for (int hlf = 0; hlf < 2; hlf++) {
+          float y8[8];
+#pragma unroll
+          for (int i = 0; i < 8; i++) y8[i] = y[v][8 * hlf + i];
+          const u32x2 q2 = quant8(y8, inv, s, fast);
+          qv[2 * hlf] = q2[0];
+          qv[2 * hlf + 1] = q2[1];
         }
-        if (!fast || dmax >= 0.49997f) {  // rare: redo this unit with the IEEE division
-#pragma unroll
-          for (int i = 0; i < 16; i++) mb[i] = (uint32_t)quant1(y[v][i], s);
-        }
-        // low bytes of four codes -> one word
-#pragma unroll
-        for (int w = 0; w < 4; w++)
-          qv[w] = (__builtin_amdgcn_perm(mb[4 * w + 3], mb[4 * w + 2], 0x0c0c0400u) << 16) |
-                  __builtin_amdgcn_perm(mb[4 * w + 1], mb[4 * w], 0x0c0c0400u);
       }
       *reinterpret_cast<u32x4*>(a.q + t * cols + e) = qv;
     }
@@ -239,7 +276,6 @@ __global__ __launch_bounds__(kPipeThreads, 1) void permute_quant_pipe(QuantArgs 
     float y = dec16<DT>(raw[k / 2] >> (16 * (k & 1)));
     return y * dec16<DT>(s[k / 2] >> (16 * (k & 1)));
   };
-  constexpr float kMagic = 12582912.0f;  // 1.5 * 2^23
   auto process = [&](const u32x4 (&b)[C], int k) {
     const int64_t t = blockIdx.x + (int64_t)k * G;
     float amax = 0.0f;
@@ -250,8 +286,7 @@ __global__ __launch_bounds__(kPipeThreads, 1) void permute_quant_pipe(QuantArgs 
       for (int e = 0; e < 8; e++) cm = fmaxf(cm, __builtin_fabsf(yval(b[i], smr[i], e)));
       amax = fmaxf(amax, valid[i] ? cm : 0.0f);
     }
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 64));
+    amax = wave_max_nonneg(amax);
     float* slot = red[k & 1];
     if (threadIdx.x % 64 == 0) slot[threadIdx.x / 64] = amax;
     __syncthreads();
@@ -261,28 +296,14 @@ __global__ __launch_bounds__(kPipeThreads, 1) void permute_quant_pipe(QuantArgs 
     const float s = amax / 127.0f;
     if (threadIdx.x == 0) a.s1[t] = s;
     const float inv = 1.0f / s;
-    const bool fast = s >= 1.17549435e-38f;  // see the bound above permute_quant_vec
+    const bool fast = s >= 1.17549435e-38f;  // see quant8
     const bool nonzero = amax > 0.0f;
 #pragma unroll
     for (int i = 0; i < C; i++) {
-      float dmax = 0.0f;
-      uint32_t mb[8];
+      float y8[8];
 #pragma unroll
-      for (int e = 0; e < 8; e++) {
-        const float qa = yval(b[i], smr[i], e) * inv;
-        const float m = __builtin_amdgcn_fmed3f(qa, -127.0f, 127.0f) + kMagic;
-        dmax = fmaxf(dmax, __builtin_fabsf(qa - (m - kMagic)));
-        mb[e] = __float_as_uint(m);
-      }
-      if (nonzero && (!fast || dmax >= 0.49997f)) {  // rare: redo this chunk with the IEEE division
-#pragma unroll
-        for (int e = 0; e < 8; e++) mb[e] = (uint32_t)quant1(yval(b[i], smr[i], e), s);
-      }
-      u32x2 qv;
-#pragma unroll
-      for (int w = 0; w < 2; w++)
-        qv[w] = (__builtin_amdgcn_perm(mb[4 * w + 3], mb[4 * w + 2], 0x0c0c0400u) << 16) |
-                __builtin_amdgcn_perm(mb[4 * w + 1], mb[4 * w], 0x0c0c0400u);
+      for (int e = 0; e < 8; e++) y8[e] = yval(b[i], smr[i], e);
+      u32x2 qv = quant8(y8, inv, s, fast);
       if (!nonzero) qv = u32x2{0u, 0u};  // an all-zero token: s = 0, codes 0
       if (valid[i]) *reinterpret_cast<u32x2*>(a.q + t * cols + ((int64_t)threadIdx.x + i * kPipeThreads) * 8) = qv;
     }

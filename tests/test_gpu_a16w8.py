@@ -115,6 +115,40 @@ def test_a16w8_zero_rows_and_ties(mc2):
     assert_close16(mc2_inputs.from_torch(out), ref["out"], "bf16", "out")
 
 
+@pytest.mark.parametrize("permuted", [False, True])
+@pytest.mark.parametrize("h", [64, 4096])
+def test_a16w8_subnormal_scales(mc2, permuted, h):
+    """Tokens whose scale amax / 127 is subnormal (every code through the division),
+    tokens of subnormal inputs (y rounds in fp32), a token with one huge value and
+    an ordinary one; pipelined path (no permuted copy) and one token per workgroup."""
+    import torch
+    r, n = 2, 16
+    rng = np.random.default_rng(h + permuted)
+    rows = rng.uniform(-1.0, 1.0, (4, r * h))
+    rows[0] *= 1e-37          # normal bf16 values, s about 6e-40 (subnormal)
+    rows[1] *= 3e-39          # subnormal bf16 values
+    rows[2, 5] = 3e38         # one huge value, the rest of the row tiny relative to it
+    rows[3] = rng.standard_normal(r * h)
+    x1_p = oracle.encode("bf16", rows)
+    x1 = x1_p.reshape(4, r, h).transpose(1, 0, 2).reshape(4 * r, h).copy()
+    sm = oracle.encode("bf16", rng.uniform(0.5, 2.0, r * h))
+    x2 = rng.integers(-127, 128, (r * h, n)).astype(np.int8)
+    s2 = np.full(n, 0.01, np.float32)
+    T = mc2_inputs.to_torch
+    q = torch.empty((4, r * h), dtype=torch.int8, device="cuda")
+    s1 = torch.empty((4,), dtype=torch.float32, device="cuda")
+    extra = {"permuted_out": torch.empty((4, r * h), dtype=torch.bfloat16, device="cuda")} if permuted else {}
+    print(f"a16w8 subnormal scales h={h} permuted={permuted}", flush=True)
+    mc2.mc2_alltoall_quant_matmul(T(x1, "bf16"), r, T(x2, "i8"), T(s2, "f32"), T(sm, "bf16"),
+                                  q_out=q, x1_scale_out=s1, **extra)
+    torch.cuda.synchronize()
+    ref = oracle.alltoall_quant_matmul(x1, r, x2, s2, sm)
+    assert 0.0 < float(ref["s1"][0]) < 1.1754944e-38 and 0.0 < float(ref["s1"][1]) < 1.1754944e-38
+    assert np.abs(ref["q"][0]).max() == 127 and np.abs(ref["q"][1]).max() == 127
+    assert_bits_equal(mc2_inputs.from_torch(s1), ref["s1"], "s1")
+    assert_bits_equal(mc2_inputs.from_torch(q), ref["q"], "q")
+
+
 @pytest.mark.parametrize("h", [4374, 4368])
 def test_a16w8_largest_rank_h(mc2, h):
     """r*H at the top of the allowed range: 34992 (H not a multiple of 16, element path)
