@@ -47,10 +47,12 @@ def test_ag_tiny_example(mc2):
 # The shapes with k % 64 == 0 and 16-byte rows run the gather-wavefront kernel (loads and
 # gather copy in wavefronts 4-7): (4, 16, 512, 64) a single partial tile row; (8, 40, 512, 96)
 # two whole tile rows and a partial one, 8 steps; (4, 96, 1536, 448) whole rows, two tile
-# columns (each copies every other step), 24 steps; (2, 72, 640, 224) 10 steps.
+# columns (each copies every other step), 24 steps; (2, 72, 640, 224) 10 steps; (4, 32, 256, 64)
+# and (2, 64, 320, 128) the shortest loops the API allows, 4 and 5 steps.
 @pytest.mark.parametrize("r,m_l,k,n", [
     (2, 1, 256, 1), (2, 3, 300, 7), (4, 16, 512, 64), (8, 5, 1000, 130), (4, 100, 264, 200),
-    (8, 33, 768, 257), (2, 129, 256, 129), (8, 40, 512, 96), (4, 96, 1536, 448), (2, 72, 640, 224)])
+    (8, 33, 768, 257), (2, 129, 256, 129), (8, 40, 512, 96), (4, 96, 1536, 448), (2, 72, 640, 224),
+    (4, 32, 256, 64), (2, 64, 320, 128)])
 @pytest.mark.parametrize("dtype", ["bf16", "f16"])
 @pytest.mark.parametrize("x2_trans", [False, True])
 def test_ag_shapes(mc2, r, m_l, k, n, dtype, x2_trans):
