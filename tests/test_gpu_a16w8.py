@@ -149,6 +149,38 @@ def test_a16w8_subnormal_scales(mc2, permuted, h):
     assert_bits_equal(mc2_inputs.from_torch(q), ref["q"], "q")
 
 
+@pytest.mark.parametrize("permuted", [False, True])
+def test_a16w8_tiny_f16_values(mc2, permuted):
+    """fp16 tokens of small (1e-4) and subnormal (3e-6) values, one with a value near the
+    fp16 maximum and an ordinary one: the fp16 decode of subnormal codes and the scales
+    (normal in fp32 here) through both kernels."""
+    import torch
+    r, h, n = 2, 64, 16
+    rng = np.random.default_rng(5 + permuted)
+    rows = rng.uniform(-1.0, 1.0, (4, r * h))
+    rows[0] *= 1e-4
+    rows[1] *= 3e-6          # fp16 subnormal codes
+    rows[2, 5] = 6e4
+    rows[3] = rng.standard_normal(r * h)
+    x1_p = oracle.encode("f16", rows)
+    x1 = x1_p.reshape(4, r, h).transpose(1, 0, 2).reshape(4 * r, h).copy()
+    sm = oracle.encode("f16", rng.uniform(0.5, 2.0, r * h))
+    x2 = rng.integers(-127, 128, (r * h, n)).astype(np.int8)
+    s2 = np.full(n, 0.01, np.float32)
+    T = mc2_inputs.to_torch
+    q = torch.empty((4, r * h), dtype=torch.int8, device="cuda")
+    s1 = torch.empty((4,), dtype=torch.float32, device="cuda")
+    extra = {"permuted_out": torch.empty((4, r * h), dtype=torch.float16, device="cuda")} if permuted else {}
+    print(f"a16w8 tiny f16 values permuted={permuted}", flush=True)
+    mc2.mc2_alltoall_quant_matmul(T(x1, "f16"), r, T(x2, "i8"), T(s2, "f32"), T(sm, "f16"),
+                                  q_out=q, x1_scale_out=s1, **extra)
+    torch.cuda.synchronize()
+    ref = oracle.alltoall_quant_matmul(x1, r, x2, s2, sm, None, "f16")
+    assert np.abs(ref["q"][1]).max() == 127
+    assert_bits_equal(mc2_inputs.from_torch(s1), ref["s1"], "s1")
+    assert_bits_equal(mc2_inputs.from_torch(q), ref["q"], "q")
+
+
 @pytest.mark.parametrize("h", [4374, 4368])
 def test_a16w8_largest_rank_h(mc2, h):
     """r*H at the top of the allowed range: 34992 (H not a multiple of 16, element path)
