@@ -44,7 +44,9 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_i8_kernel(Problem p, GemmI8A
 #pragma unroll
     for (int j = 0; j < FN; j++) acc[i][j] = i32x4{0, 0, 0, 0};
 
-  run_mainloop<1, BM, BN, true, false, VEC, false, 3, OpsI8>(p, m0, n0, tn, tiles_n, s0, s1, s2, acc);
+  // K walked from a step set by the tile row (see mainloop_fast): the eight
+  // workgroups of a tile column read their shared band of B a step apart
+  run_mainloop<1, BM, BN, true, false, VEC, false, 3, OpsI8, 2, true>(p, m0, n0, tn, tiles_n, s0, s1, s2, acc);
 
   const int wave = threadIdx.x / 64, lane = threadIdx.x % 64;
   const int wm = wave / 2, wn = wave % 2;

@@ -632,13 +632,14 @@ struct FragReader {
 // before each barrier (dma_waves_loop); these wavefronts only read the
 // stages, multiply and meet the barriers.
 template <int E, int BM, int BN, bool AK, bool BKM, bool GATHER, bool ARR, int NS, typename Ops, int TAG = 0,
-          bool NODMA = false>
+          bool NODMA = false, bool ROTK = false>
 __device__ __forceinline__ void mainloop_fast(const Problem& p, int64_t m0, int64_t n0, int gather_phase,
                                               int gather_every, uint8_t* L0, uint8_t* L1, uint8_t* L2,
                                               typename Ops::Acc (&acc)[BM / 32][BN / 32]) {
   static_assert(!ARR || (AK && !GATHER), "arrival needs a K-contiguous A and no gather copy");
   static_assert(NS == 3 || (NS == 2 && !ARR), "two stages: no arrival wait");
   static_assert(!NODMA || (NS == 3 && !ARR && !GATHER), "loads from other wavefronts: three stages only");
+  static_assert(!ROTK || (E == 1 && !ARR && !GATHER && !NODMA), "rotated K walk: exact int8 products, plain loop");
   const int tid = (int)threadIdx.x;
   constexpr int BK = kRowBytes / E;  // K elements per step
   constexpr int kATile = BM * kRowBytes;
@@ -693,9 +694,33 @@ __device__ __forceinline__ void mainloop_fast(const Problem& p, int64_t m0, int6
   // A's offset of the next step to be loaded: steps go through K segment by
   // segment (one segment, kseg = k, for a plain or an M-contiguous A)
   const int seg_steps = (int)(p.kseg / BK);
+  // ROTK: the workgroup walks K from step rot = (tile row) mod nk and wraps
+  // around, so the workgroups that share a band of B (one per tile row) read
+  // it a step apart instead of all at once.  Step kt of the loop loads
+  // physical step phys(kt).
+  const int rot = ROTK ? (int)((m0 / BM) % nk) : 0;
+  auto phys = [&](int kt) {
+    if constexpr (ROTK) return kt + rot >= nk ? kt + rot - nk : kt + rot;
+    else return kt;
+  };
   int64_t a_next = 0, seg_base = 0;
   int seg_left = seg_steps;
+  int a_phys = rot;
+  if constexpr (ROTK) {
+    seg_base = (int64_t)(rot / seg_steps) * p.kseg_stride;
+    a_next = seg_base + (int64_t)(rot % seg_steps) * da.step_bytes;
+    seg_left = seg_steps - rot % seg_steps;
+  }
   auto advance_a = [&]() {
+    if constexpr (ROTK) {
+      if (++a_phys == nk) {  // past the last step: back to step 0
+        a_phys = 0;
+        seg_base = 0;
+        a_next = 0;
+        seg_left = seg_steps;
+        return;
+      }
+    }
     if (--seg_left == 0) {
       seg_base += p.kseg_stride;
       a_next = seg_base;
@@ -709,7 +734,7 @@ __device__ __forceinline__ void mainloop_fast(const Problem& p, int64_t m0, int6
   auto dma = [&](uint8_t* L, int kt) {
     if constexpr (!NODMA) {
       da.issue(L, a_next);
-      db.issue(L + kATile, kt * db.step_bytes);
+      db.issue(L + kATile, (int64_t)phys(kt) * db.step_bytes);
       advance_a();
     }
   };
@@ -725,7 +750,7 @@ __device__ __forceinline__ void mainloop_fast(const Problem& p, int64_t m0, int6
     constexpr int D0 = decltype(D0_)::value, D1 = decltype(D1_)::value;
     constexpr int NM = FM * FN, NF = FM + FN, NDH = D1 - D0;
     constexpr int kTail = NM >= 2 * NF ? NM - 2 * NF < 8 ? NM - 2 * NF : 8 : 0;
-    const int64_t offa = a_next, offb = (int64_t)kt_dma * db.step_bytes;
+    const int64_t offa = a_next, offb = (int64_t)phys(kt_dma) * db.step_bytes;
 #pragma unroll
     for (int q = 0; q < NM; q++) {
       acc[q / FN][q % FN] = Ops::mfma(fb[q % FN], fa[q / FN], acc[q / FN][q % FN]);
@@ -917,7 +942,10 @@ constexpr int stage_bytes() { return (BM + BN) * kRowBytes; }
 // whole row chunk first).
 // GMODE: 0 = no gather copy, 1 = gather copy (p.gather_out set), 2 = decided
 // from p.gather_out at run time (the first two compile one fast loop only).
-template <int E, int BM, int BN, bool AK, bool BKM, bool VEC, bool ARR, int NS, typename Ops, int GMODE = 2>
+// ROTK: the fast loop without the gather copy walks K from a step that
+// depends on the tile row (int8 only: exact sums do not depend on the order).
+template <int E, int BM, int BN, bool AK, bool BKM, bool VEC, bool ARR, int NS, typename Ops, int GMODE = 2,
+          bool ROTK = false>
 __device__ __forceinline__ void run_mainloop(const Problem& p, int64_t m0, int64_t n0, int tn, int tiles_n,
                                              uint8_t* L0, uint8_t* L1, uint8_t* L2,
                                              typename Ops::Acc (&acc)[BM / 32][BN / 32]) {
@@ -932,7 +960,8 @@ __device__ __forceinline__ void run_mainloop(const Problem& p, int64_t m0, int64
       } else if constexpr (AK && NS == 3 && GMODE == 2) {
         if (gather_every > 0)
           mainloop_fast<E, BM, BN, AK, BKM, true, false, NS, Ops>(p, m0, n0, tn, gather_every, L0, L1, L2, acc);
-        else mainloop_fast<E, BM, BN, AK, BKM, false, false, NS, Ops>(p, m0, n0, tn, gather_every, L0, L1, L2, acc);
+        else mainloop_fast<E, BM, BN, AK, BKM, false, false, NS, Ops, 0, false, ROTK>(p, m0, n0, tn, gather_every, L0,
+                                                                                  L1, L2, acc);
       } else {
         // no gather copy with two stages (the host picks no two-stage tile
         // when gather_out is set)
