@@ -639,7 +639,7 @@ __device__ __forceinline__ void mainloop_fast(const Problem& p, int64_t m0, int6
   static_assert(!ARR || (AK && !GATHER), "arrival needs a K-contiguous A and no gather copy");
   static_assert(NS == 3 || (NS == 2 && !ARR), "two stages: no arrival wait");
   static_assert(!NODMA || (NS == 3 && !ARR && !GATHER), "loads from other wavefronts: three stages only");
-  static_assert(!ROTK || (E == 1 && !ARR && !GATHER && !NODMA), "rotated K walk: exact int8 products, plain loop");
+  static_assert(!ROTK || !NODMA, "rotated K walk: the wavefronts that issue the loads rotate");
   const int tid = (int)threadIdx.x;
   constexpr int BK = kRowBytes / E;  // K elements per step
   constexpr int kATile = BM * kRowBytes;
@@ -674,17 +674,29 @@ __device__ __forceinline__ void mainloop_fast(const Problem& p, int64_t m0, int6
   rb.init(wn * WN);
   const int nk = (int)(p.k / BK);
   int next_gather = gather_phase;
+  // ROTK: the workgroup walks K from step rot = (tile row) mod nk and wraps
+  // around, so the workgroups that share a band of B (one per tile row) read
+  // it a step apart instead of all at once.  Step kt of the loop loads (and
+  // waits for, copies) physical step phys(kt); the accumulation order
+  // follows, the same in every loop that rotates.
+  const int rot = ROTK ? (int)((m0 / BM) % nk) : 0;
+  auto phys = [&](int kt) {
+    if constexpr (ROTK) return kt + rot >= nk ? kt + rot - nk : kt + rot;
+    else return kt;
+  };
 
   // arrival: the flags of this tile's row chunk, one per slab of K
   const unsigned* flags = ARR ? p.ready + (m0 / p.rows_chunk) * p.slabs : nullptr;
   const int sps = ARR ? (int)(p.slab_cols / BK) : 1;  // steps per slab
   bool fell_back = false;
   unsigned pv = 0;  // polled flag of the slab of the step after next
-  auto poll = [&](int kt) { return __hip_atomic_load(flags + kt / sps, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM); };
+  auto poll = [&](int kt) {
+    return __hip_atomic_load(flags + phys(kt) / sps, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+  };
   // Blocking wait for the slab of step kt; after a time-out A comes from the shards.
   auto wait_step = [&](int kt) {
     if (fell_back) return;
-    if (!wait_flag(flags + kt / sps, p.ready_value, p.wait_ticks)) {
+    if (!wait_flag(flags + phys(kt) / sps, p.ready_value, p.wait_ticks)) {
       fell_back = true;
       da = da_shards;
       if (threadIdx.x % 64 == 0) __hip_atomic_fetch_add(p.fallbacks, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -694,15 +706,6 @@ __device__ __forceinline__ void mainloop_fast(const Problem& p, int64_t m0, int6
   // A's offset of the next step to be loaded: steps go through K segment by
   // segment (one segment, kseg = k, for a plain or an M-contiguous A)
   const int seg_steps = (int)(p.kseg / BK);
-  // ROTK: the workgroup walks K from step rot = (tile row) mod nk and wraps
-  // around, so the workgroups that share a band of B (one per tile row) read
-  // it a step apart instead of all at once.  Step kt of the loop loads
-  // physical step phys(kt).
-  const int rot = ROTK ? (int)((m0 / BM) % nk) : 0;
-  auto phys = [&](int kt) {
-    if constexpr (ROTK) return kt + rot >= nk ? kt + rot - nk : kt + rot;
-    else return kt;
-  };
   int64_t a_next = 0, seg_base = 0;
   int seg_left = seg_steps;
   int a_phys = rot;
@@ -785,13 +788,13 @@ __device__ __forceinline__ void mainloop_fast(const Problem& p, int64_t m0, int6
     // gather_out copy of this step's A tile (NG stores per thread, older than
     // every load issued below, so the wait below covers them)
     if (GATHER && kt == next_gather) {
-      copy_gather<E, BM>(cur, p.gather_out, p.m, p.k, m0, (int64_t)kt * BK, (int)threadIdx.x);
+      copy_gather<E, BM>(cur, p.gather_out, p.m, p.k, m0, (int64_t)phys(kt) * BK, (int)threadIdx.x);
       next_gather += gather_every;
     }
     if constexpr (ARR) {
       // the slab of step kt+2 (polled during the previous step) must have arrived
-      if (dma2 && (kt + 2) % sps == 0 && pv != p.ready_value) wait_step(kt + 2);
-      if (!fell_back && kt + 3 < nk && (kt + 3) % sps == 0) pv = poll(kt + 3);
+      if (dma2 && phys(kt + 2) % sps == 0 && pv != p.ready_value) wait_step(kt + 2);
+      if (!fell_back && kt + 3 < nk && phys(kt + 3) % sps == 0) pv = poll(kt + 3);
     }
     __builtin_amdgcn_sched_barrier(0);
     // half 0 of step kt; the DMA of step kt+2 (its stage was last read
@@ -815,7 +818,7 @@ __device__ __forceinline__ void mainloop_fast(const Problem& p, int64_t m0, int6
     constexpr bool FULL = decltype(FULL_)::value;
     const bool dma2 = FULL || kt + 2 < nk;
     if (GATHER && kt == next_gather) {
-      copy_gather<E, BM>(cur, p.gather_out, p.m, p.k, m0, (int64_t)kt * BK, (int)threadIdx.x);
+      copy_gather<E, BM>(cur, p.gather_out, p.m, p.k, m0, (int64_t)phys(kt) * BK, (int)threadIdx.x);
       next_gather += gather_every;
     }
     __builtin_amdgcn_sched_barrier(0);
@@ -835,8 +838,8 @@ __device__ __forceinline__ void mainloop_fast(const Problem& p, int64_t m0, int6
   if constexpr (ARR) {
     wait_step(0);
     __atomic_thread_fence(__ATOMIC_ACQUIRE);  // no stale lines of A from earlier calls
-    if (nk > 1 && 1 % sps == 0) wait_step(1);
-    if (!fell_back && nk > 2 && 2 % sps == 0) pv = poll(2);
+    if (nk > 1 && phys(1) % sps == 0) wait_step(1);
+    if (!fell_back && nk > 2 && phys(2) % sps == 0) pv = poll(2);
   }
   if constexpr (!NODMA) {
     dma(L0, 0);
@@ -942,8 +945,8 @@ constexpr int stage_bytes() { return (BM + BN) * kRowBytes; }
 // whole row chunk first).
 // GMODE: 0 = no gather copy, 1 = gather copy (p.gather_out set), 2 = decided
 // from p.gather_out at run time (the first two compile one fast loop only).
-// ROTK: the fast loop without the gather copy walks K from a step that
-// depends on the tile row (int8 only: exact sums do not depend on the order).
+// ROTK: the fast loops walk K from a step that depends on the tile row (see
+// mainloop_fast); the checked loop does not.
 template <int E, int BM, int BN, bool AK, bool BKM, bool VEC, bool ARR, int NS, typename Ops, int GMODE = 2,
           bool ROTK = false>
 __device__ __forceinline__ void run_mainloop(const Problem& p, int64_t m0, int64_t n0, int tn, int tiles_n,
@@ -954,12 +957,14 @@ __device__ __forceinline__ void run_mainloop(const Problem& p, int64_t m0, int64
   if constexpr (VEC) {
     if (p.k % BK == 0 && p.kseg % BK == 0) {  // whole steps, each inside one K segment
       if constexpr (ARR) {
-        mainloop_fast<E, BM, BN, AK, BKM, false, true, NS, Ops>(p, m0, n0, tn, 0, L0, L1, L2, acc);
+        mainloop_fast<E, BM, BN, AK, BKM, false, true, NS, Ops, 0, false, ROTK>(p, m0, n0, tn, 0, L0, L1, L2, acc);
       } else if constexpr (AK && NS == 3 && GMODE == 1) {
-        mainloop_fast<E, BM, BN, AK, BKM, true, false, NS, Ops>(p, m0, n0, tn, gather_every, L0, L1, L2, acc);
+        mainloop_fast<E, BM, BN, AK, BKM, true, false, NS, Ops, 0, false, ROTK>(p, m0, n0, tn, gather_every, L0, L1,
+                                                                                 L2, acc);
       } else if constexpr (AK && NS == 3 && GMODE == 2) {
         if (gather_every > 0)
-          mainloop_fast<E, BM, BN, AK, BKM, true, false, NS, Ops>(p, m0, n0, tn, gather_every, L0, L1, L2, acc);
+          mainloop_fast<E, BM, BN, AK, BKM, true, false, NS, Ops, 0, false, ROTK>(p, m0, n0, tn, gather_every, L0,
+                                                                                   L1, L2, acc);
         else mainloop_fast<E, BM, BN, AK, BKM, false, false, NS, Ops, 0, false, ROTK>(p, m0, n0, tn, gather_every, L0,
                                                                                   L1, L2, acc);
       } else {
@@ -1028,9 +1033,12 @@ __device__ __forceinline__ void dma_waves_loop(const Problem& p, int64_t m0, int
   const bool whole = m0 + BM <= p.m;  // the copy's whole-tile path: NG stores per lane
   const bool copy = p.gather_out != nullptr;
   int next = tn;
+  // K walked from step (tile row) mod nk, as mainloop_fast does with ROTK
+  const int rot = (int)((m0 / BM) % nk);
+  auto phys = [&](int kt) { return kt + rot >= nk ? kt + rot - nk : kt + rot; };
   auto dma = [&](uint8_t* L, int kt) {
-    da.issue(L, (int64_t)kt * da.step_bytes);
-    db.issue(L + kATile, (int64_t)kt * db.step_bytes);
+    da.issue(L, (int64_t)phys(kt) * da.step_bytes);
+    db.issue(L + kATile, (int64_t)phys(kt) * db.step_bytes);
   };
   // cur: stage of step kt; nn: stage of step kt + 2
   auto step = [&](int kt, uint8_t* cur, uint8_t* nn) {
@@ -1038,7 +1046,7 @@ __device__ __forceinline__ void dma_waves_loop(const Problem& p, int64_t m0, int
     if (dma2) dma(nn, kt + 2);
     const bool cp = copy && kt == next;
     if (cp) {
-      copy_gather<E, BM, true>(cur, p.gather_out, p.m, p.k, m0, (int64_t)kt * BK, tid);
+      copy_gather<E, BM, true>(cur, p.gather_out, p.m, p.k, m0, (int64_t)phys(kt) * BK, tid);
       next += tiles_n;
     }
     if (kt + 1 < nk) {
