@@ -192,12 +192,12 @@ __global__ __launch_bounds__(kThreads, 1) void gemm16_kernel(Problem p, void* c)
 #pragma unroll
     for (int j = 0; j < FN; j++) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // the AllGatherMatmul loops (arrival wait, gather copy) walk K from a step
-  // set by the tile row, as the gather-wavefront kernel does, so the three
-  // give the same bits; the plain GEMMs (backward, MatmulReduceScatter) walk
-  // K in order
-  run_mainloop<2, BM, BN, AK, BKM, VEC, ARR, NS, Ops16<DT>, GA ? 1 : 0, ARR || GA>(p, m0, n0, tn, tiles_n, s0, s1,
-                                                                                   s2, acc);
+  // the fused AllGatherMatmul loop with the gather copy walks K from a step
+  // set by the tile (rot_start), as the gather-wavefront kernel does, so the
+  // two give the same bits; arrival mode walks K in order, the order its
+  // pieces arrive in, and so do the plain GEMMs (backward,
+  // MatmulReduceScatter), which ran slower rotated
+  run_mainloop<2, BM, BN, AK, BKM, VEC, ARR, NS, Ops16<DT>, GA ? 1 : 0, GA>(p, m0, n0, tn, tiles_n, s0, s1, s2, acc);
 
   uint16_t* h0 = reinterpret_cast<uint16_t*>(s0);
   uint16_t* h1 = reinterpret_cast<uint16_t*>(s1);

@@ -596,6 +596,18 @@ struct FragReader {
   }
 };
 
+// First K step of the rotated walk of tile (tm, tn) over nk steps (the fast
+// loops with ROTK, and dma_waves_loop).  int8 (the GEMM of AlltoAllQuantMatmul):
+// one step per tile row.  16-bit (the fused AllGatherMatmul loops): two steps
+// per tile row and six per tile column, the best of the patterns measured on
+// the 8 x (512, 4096) @ (4096, 1792) workload (one step per row: 66 us, 2 + 6:
+// 60-62 us; spreads of 4 per row or 10 per column ran slower than no rotation).
+// Arrival mode does not rotate: it takes K in the order its pieces arrive.
+template <int E>
+__device__ __forceinline__ int rot_start(int64_t tm, int64_t tn, int nk) {
+  return (int)((E == 1 ? tm : 2 * tm + 6 * tn) % nk);
+}
+
 // Fast path: k is a multiple of the step and every operand row is 16-byte
 // aligned; tiles may cross the M / N edges (clamped loads).  Three LDS stages
 // (separate arrays, so the compiler can tell a DMA target from the buffer
@@ -674,12 +686,12 @@ __device__ __forceinline__ void mainloop_fast(const Problem& p, int64_t m0, int6
   rb.init(wn * WN);
   const int nk = (int)(p.k / BK);
   int next_gather = gather_phase;
-  // ROTK: the workgroup walks K from step rot = (tile row) mod nk and wraps
-  // around, so the workgroups that share a band of B (one per tile row) read
-  // it a step apart instead of all at once.  Step kt of the loop loads (and
-  // waits for, copies) physical step phys(kt); the accumulation order
-  // follows, the same in every loop that rotates.
-  const int rot = ROTK ? (int)((m0 / BM) % nk) : 0;
+  // ROTK: the workgroup walks K from step rot (rot_start) and wraps around,
+  // so the workgroups that share a band of B (one per tile row) or of A (one
+  // per tile column) read it a few steps apart instead of all at once.  Step
+  // kt of the loop loads (and waits for, copies) physical step phys(kt); the
+  // accumulation order follows, the same in every loop that rotates.
+  const int rot = ROTK ? rot_start<E>(m0 / BM, n0 / BN, nk) : 0;
   auto phys = [&](int kt) {
     if constexpr (ROTK) return kt + rot >= nk ? kt + rot - nk : kt + rot;
     else return kt;
@@ -1033,8 +1045,8 @@ __device__ __forceinline__ void dma_waves_loop(const Problem& p, int64_t m0, int
   const bool whole = m0 + BM <= p.m;  // the copy's whole-tile path: NG stores per lane
   const bool copy = p.gather_out != nullptr;
   int next = tn;
-  // K walked from step (tile row) mod nk, as mainloop_fast does with ROTK
-  const int rot = (int)((m0 / BM) % nk);
+  // K walked from step rot_start, as mainloop_fast does with ROTK
+  const int rot = rot_start<E>(m0 / BM, n0 / BN, nk);
   auto phys = [&](int kt) { return kt + rot >= nk ? kt + rot - nk : kt + rot; };
   auto dma = [&](uint8_t* L, int kt) {
     da.issue(L, (int64_t)phys(kt) * da.step_bytes);

@@ -202,19 +202,30 @@ def _arrival_case(mc2, r, m_l, k, n, dtype, rank_id, seed, x2_trans=False):
     return shards_np, x2_np, mc2_inputs.from_torch(fused), mc2_inputs.from_torch(out), mc2_inputs.from_torch(g)
 
 
+def _arrival_out(mc2, shards_np, x2_np, dtype, rank_id, x2_trans=False):
+    """One more arrival-mode call on the same inputs (output only)."""
+    import torch
+    T = mc2_inputs.to_torch
+    out, _ = mc2.mc2_allgather_matmul([T(s, dtype) for s in shards_np], T(x2_np, dtype), x2_trans=x2_trans,
+                                      mode=mc2.MC2_AG_ARRIVAL, rank_id=rank_id)
+    torch.cuda.synchronize()
+    return mc2_inputs.from_torch(out)
+
+
 @pytest.mark.parametrize("r,m_l,k,n,rank_id", [
     (2, 1, 256, 1, 1), (4, 16, 512, 64, 2), (8, 5, 1000, 130, 7), (4, 100, 264, 200, 0),
     (8, 33, 768, 257, 3), (2, 129, 256, 129, 1), (8, 128, 512, 224, 5)])
 @pytest.mark.parametrize("dtype", ["bf16", "f16"])
 def test_ag_arrival_shapes(mc2, r, m_l, k, n, rank_id, dtype):
-    """Arrival mode reads the copied gather_out: same bits as the fused mode, gather_out exact."""
+    """Arrival mode reads the copied gather_out: out within the oracle's bound, gather_out exact.
+    (Its K walk is in order, the fused loops' is rotated, so the two differ in rounding.)"""
     print(f"arrival r={r} m_l={m_l} k={k} n={n} rank={rank_id} {dtype}", flush=True)
     mc2.mc2_allgather_arrival_fallbacks(reset=True)
     shards, x2, fused, out, g = _arrival_case(mc2, r, m_l, k, n, dtype, rank_id, seed=7000 + r * 100 + m_l)
     want, want_g = oracle.allgather_matmul(shards, x2, dtype)
     assert_bits_equal(g, want_g, "gather_out")
-    assert_bits_equal(out, fused, "arrival vs fused")
     assert_close16(out, want, dtype, "out")
+    assert_close16(fused, want, dtype, "fused out")
     assert mc2.mc2_allgather_arrival_fallbacks() == 0
 
 
@@ -227,12 +238,12 @@ def test_ag_arrival_repeated_calls(mc2):
                                                   x2_trans=bool(it % 2))
         want, want_g = oracle.allgather_matmul(shards, x2, "bf16", x2_trans=bool(it % 2))
         assert_bits_equal(g, want_g, f"gather_out call {it}")
-        assert_bits_equal(out, fused, f"arrival vs fused call {it}")
+        assert_close16(out, want, "bf16", f"arrival call {it}")
     assert mc2.mc2_allgather_arrival_fallbacks() == 0
 
 
 def test_ag_arrival_full_config(mc2):
-    """8 x bf16 (512, 4096) @ (4096, 1792) in arrival mode: bit-identical to the fused mode."""
+    """8 x bf16 (512, 4096) @ (4096, 1792) in arrival mode: every element within the oracle's bound."""
     import torch
     seed, d, specs = mc2_inputs.CONFIGS["ag_bf16_tp"]
     t = mc2_inputs.make("ag_bf16_tp")
@@ -245,7 +256,8 @@ def test_ag_arrival_full_config(mc2):
     torch.cuda.synchronize()
     G = np.concatenate([t[f"shard{i}"] for i in range(d["r"])])
     assert_bits_equal(mc2_inputs.from_torch(g), G, "gather_out")
-    assert_bits_equal(mc2_inputs.from_torch(out), mc2_inputs.from_torch(fused), "arrival vs fused")
+    want, _ = oracle.allgather_matmul([t[f"shard{i}"] for i in range(d["r"])], t["x2"], "bf16")
+    assert_close16(mc2_inputs.from_torch(out), want, "bf16", "arrival out")
     assert mc2.mc2_allgather_arrival_fallbacks() == 0
 
 
@@ -254,7 +266,9 @@ def test_ag_arrival_full_config(mc2):
 # withheld slab runs out and that wavefront (fast path) or workgroup (checked
 # path) reads the rest of A from the shards.  raised = 0: the first wait runs
 # out; raised = 1: the switch happens inside the main loop, after slab 0 came
-# through the arrived buffer.  The output must equal the fused mode bit for bit.
+# through the arrived buffer.  The output must equal a normal arrival-mode call on
+# the same inputs bit for bit (both walk K in order; the shards hold the same
+# values as the arrived buffer).
 @pytest.mark.parametrize("r,m_l,k,n,raised,path", [
     (8, 128, 512, 224, 1, "fast"), (8, 128, 512, 224, 0, "fast"), (4, 64, 1024, 128, 3, "fast"),
     (8, 33, 768, 257, 2, "checked"), (2, 129, 256, 129, 0, "checked")])
@@ -271,9 +285,13 @@ def test_ag_arrival_timeout_fallback(mc2, r, m_l, k, n, raised, path):
     want, want_g = oracle.allgather_matmul(shards, x2, "bf16")
     assert fallbacks > 0
     assert_bits_equal(g, want_g, "gather_out")
-    assert_bits_equal(out, fused, "fallback vs fused")
     assert_close16(out, want, "bf16", "out")
-    # and the default settings are back: no fallback on the next call
+    # the default settings are back: the same inputs without a time-out give the same bits
+    ref = _arrival_out(mc2, shards, x2, "bf16", rank_id=1)
+    assert mc2.mc2_allgather_arrival_fallbacks() == 0
+    assert_bits_equal(out, ref, "fallback vs arrival without time-outs")
+    # and new data: no fallback
     shards, x2, fused, out, g = _arrival_case(mc2, r, m_l, k, n, "bf16", rank_id=0, seed=7800 + k)
-    assert_bits_equal(out, fused, "arrival vs fused after the hook")
+    want, _ = oracle.allgather_matmul(shards, x2, "bf16")
+    assert_close16(out, want, "bf16", "arrival after the hook")
     assert mc2.mc2_allgather_arrival_fallbacks() == 0
