@@ -957,8 +957,8 @@ constexpr int stage_bytes() { return (BM + BN) * kRowBytes; }
 // whole row chunk first).
 // GMODE: 0 = no gather copy, 1 = gather copy (p.gather_out set), 2 = decided
 // from p.gather_out at run time (the first two compile one fast loop only).
-// ROTK: the fast loops walk K from a step that depends on the tile row (see
-// mainloop_fast); the checked loop does not.
+// ROTK: the fast loops walk K from a step set by the tile (rot_start, see
+// mainloop_fast); the checked loop walks K in order.
 template <int E, int BM, int BN, bool AK, bool BKM, bool VEC, bool ARR, int NS, typename Ops, int GMODE = 2,
           bool ROTK = false>
 __device__ __forceinline__ void run_mainloop(const Problem& p, int64_t m0, int64_t n0, int tn, int tiles_n,
